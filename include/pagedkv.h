@@ -1,0 +1,258 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: paged-KV decode on MI355X (gfx950).
+ *
+ * The library implements the hot path of paged KV-cache decoding as the
+ * reference pages describe it:
+ *   - a host-side block manager (refcounts, chained prefix hashes, an LRU
+ *     evictable pool, all-or-nothing allocate/append, reverse-order free,
+ *     fork and copy-on-write append);
+ *   - pa_write_kv: scatter new tokens' K/V into their slots;
+ *   - pa_copy_blocks: the copy-on-write block copy;
+ *   - pa_decode: attention of one query token per sequence over K/V that
+ *     live in fixed-size blocks scattered through HBM, found through the
+ *     sequence's block table, with split-KV partitions and a final reduce.
+ *
+ * Pages cited:
+ *   [A130]  "qaqbuyan.com article 130" (vLLM PagedAttention walk-through):
+ *           KV-cache and block-size formulas, BlockTable, paged_attention
+ *           pseudocode, BlockAllocator, paged_attention_kernel listing.
+ *   [D31]   "day31" (blog.ans20xx.com): toy block allocator, toy COW append
+ *           (fork_sequence / ensure_private_last_block / append_with_cow).
+ *   [P06]   "P06 · BlockManager: paged KV + prefix cache" (kuanzhou.online
+ *           nano-vllm-omni drills): spec overview, operations table,
+ *           invariants I1-I5, pitfalls, Examples 1-3, details, data-structure
+ *           table, algorithm notes, eviction trace.
+ *
+ * Conventions for every call:
+ *   - Every call returns a pa_status (0 = PA_OK) unless documented otherwise.
+ *     On any error nothing is modified and no kernel is launched; a
+ *     human-readable detail is available from pa_last_error() on the same
+ *     thread.
+ *   - The library never allocates device memory and never synchronizes a
+ *     stream.  Device buffers are owned by the caller.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the null stream); device calls are
+ *     asynchronous on it.
+ *   - The KV cache of one layer is two arrays (K and V), each laid out
+ *     [num_blocks][block_size][num_kv_heads][head_dim] in the element type
+ *     `dtype`, densely packed ([A130] paged_attention pseudocode and kernel
+ *     listing).  One physical block id names the same block in every layer
+ *     ([A130] block-size formula: a block's bytes span all layers).
+ *   - Token position `pos` of a sequence lives in flat slot
+ *     table[pos / block_size] * block_size + pos % block_size ([P06] spec
+ *     overview).
+ *   - Block-manager calls on one pa_bm are serialized by an internal mutex.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_OUT_OF_BLOCKS = 1, /* [P06] OutOfBlocks: nothing free or evictable */
+  PA_ERR_INVALID = 2,       /* bad argument, unknown/duplicate sequence id  */
+  PA_ERR_UNSUPPORTED = 3,   /* valid but not implemented (dtype, head_dim)  */
+  PA_ERR_DEVICE = 4         /* a HIP runtime call failed                    */
+};
+
+/* Element types of Q and of the KV cache. */
+enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 };
+
+/* Static name of a status code ("PA_OK", ...). */
+const char* pa_status_str(int status);
+/* Detail of the last error raised on the calling thread ("" if none). The
+ * pointer stays valid until the next library call on this thread. */
+const char* pa_last_error(void);
+
+/* ==== host block manager ================================================
+ * [P06] data-structure table, operations table and algorithm notes, with
+ * [D31] fork and copy-on-write append.  Semantics:
+ *   - free list: FIFO, initially 0..num_blocks-1 ([P06] Example 1);
+ *   - a full block is identified by h_i = H(h_{i-1}, tokens of block i),
+ *     h_{-1} a fixed sentinel; H is a 64-bit splitmix64-based chain and a
+ *     hit also verifies the stored parent hash and tokens, so a false hit
+ *     needs a 64-bit collision of whole prefixes;
+ *   - allocate matches at most (len-1)/block_size leading blocks,
+ *     contiguously from block 0, stopping at the first miss;
+ *   - free walks the table in reverse; a block reaching ref 0 goes to the
+ *     newest end of the evictable pool if it carries a hash, else to the
+ *     free list;
+ *   - taking a block: free list first, else evict the oldest evictable block
+ *     and drop its registration (the hash->block entry only if it points at
+ *     that block);
+ *   - num_free_blocks = free + evictable.
+ */
+typedef struct pa_bm pa_bm;
+
+/* Create a manager for `num_blocks` blocks of `block_size` tokens.  Prefix
+ * caching on iff enable_prefix_cache != 0 ([P06] details: off means nothing
+ * is hashed, every freed block returns to the free list, cached is 0).
+ * Returns NULL (with pa_last_error set) if num_blocks <= 0 or
+ * block_size <= 0.  Owned by the caller; release with pa_bm_destroy. */
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, int32_t enable_prefix_cache);
+void pa_bm_destroy(pa_bm* bm);
+
+/* [P06] operations table, allocate row.  Admit sequence `seq` with prompt
+ * tokens[0..n).  Matches cached prefix blocks, checks capacity exactly
+ * (new blocks needed <= num_free_blocks - hits that sit in the evictable
+ * pool) before any change, revives hits, takes new blocks in logical order,
+ * registers the full blocks and records the sequence.  On success writes
+ * the ceil(n/block_size) physical ids to table_out[0..] (if table_out is
+ * not NULL) and their count to *nblocks_out (if not NULL).
+ * Errors: PA_ERR_OUT_OF_BLOCKS (state unchanged); PA_ERR_INVALID if `seq`
+ * exists, n < 0, tokens is NULL with n > 0, or table_out is given with
+ * cap < ceil(n/block_size).  n == 0 is allowed (empty table). */
+int pa_bm_allocate(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n,
+                   int32_t* table_out, int32_t cap, int32_t* nblocks_out);
+
+/* [P06] operations table, append_slot row, with [D31] copy-on-write.
+ * pos = current length.  If pos/block_size == table length, a new block is
+ * taken; otherwise, if the last block is shared (ref > 1), a new block is
+ * taken, the old one decref'd and replaced in the table, and the pair
+ * (old, new) is reported in *cow_src_out and *cow_dst_out (both -1 when no copy
+ * is needed) -- the caller must copy that block (pa_copy_blocks) before
+ * writing the token.  Then the token is appended; if the block just became
+ * full and prefix caching is on it is hashed with the chain tail as parent
+ * and registered.  *slot_out receives the token's flat slot.
+ * Errors: PA_ERR_OUT_OF_BLOCKS at the take-block step (state unchanged);
+ * PA_ERR_INVALID for an unknown seq.  Output pointers may be NULL. */
+int pa_bm_append_slot(pa_bm* bm, int64_t seq, int32_t token, int64_t* slot_out,
+                      int32_t* cow_src_out, int32_t* cow_dst_out);
+
+/* pa_bm_append_slot for seqs[0..B) with tokens[0..B), in order.  slots_out
+ * [B] receives each slot; cow_pairs_out [B][2] receives the copy pairs
+ * packed from the front, their count in *n_cow_out.  Stops at the first
+ * failing append and returns its status; *n_done_out (if not NULL) is the
+ * number of appends completed, which stay done. */
+int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, const int32_t* tokens, int32_t B,
+                       int64_t* slots_out, int32_t* cow_pairs_out, int32_t* n_cow_out,
+                       int32_t* n_done_out);
+
+/* [D31] fork_sequence: `child` gets a copy of the parent's table, tokens,
+ * hash chain and cached count; every block's ref is incremented.  Never
+ * needs a block.  PA_ERR_INVALID if parent is unknown or child exists. */
+int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
+
+/* [P06] operations table, free row: reverse walk, ref-1, blocks at 0 to the
+ * evictable pool (hashed) or free list (not hashed); the sequence's records
+ * are dropped.  Never fails; an unknown seq is a no-op returning PA_OK. */
+int pa_bm_free(pa_bm* bm, int64_t seq);
+
+/* Flat slot of token `pos` (0 <= pos < len) of `seq` ([P06] spec overview).
+ * PA_ERR_INVALID for an unknown seq or pos out of range. */
+int pa_bm_slot(const pa_bm* bm, int64_t seq, int32_t pos, int64_t* slot_out);
+/* Free + evictable block count; -1 if bm is NULL. */
+int32_t pa_bm_num_free_blocks(const pa_bm* bm);
+/* [P06] details: coarse check ceil(n_tokens/block_size) <= num_free_blocks
+ * (ignores prefix hits).  Returns 1 or 0 (0 also for bad arguments). */
+int32_t pa_bm_can_allocate(const pa_bm* bm, int32_t n_tokens);
+/* Tokens of `seq` served from the prefix cache at allocate (hits * bs). */
+int pa_bm_num_cached_tokens(const pa_bm* bm, int64_t seq, int32_t* out);
+/* Current length (tokens) of `seq`. */
+int pa_bm_seq_len(const pa_bm* bm, int64_t seq, int32_t* out);
+/* Copy the block table of `seq` into out[0..cap); *n_out = its length.
+ * PA_ERR_INVALID if unknown or cap is too small (nothing written). */
+int pa_bm_get_table(const pa_bm* bm, int64_t seq, int32_t* out, int32_t cap, int32_t* n_out);
+/* Number of live sequences; -1 if bm is NULL. */
+int32_t pa_bm_num_seqs(const pa_bm* bm);
+/* Ids of the live sequences in ascending order into out[0..cap); *n_out =
+ * their count.  PA_ERR_INVALID if cap is too small (nothing written). */
+int pa_bm_seq_ids(const pa_bm* bm, int64_t* out, int32_t cap, int32_t* n_out);
+
+/* Export the decode inputs for seqs[0..B): tables_out is a row-major
+ * [B][max_blocks] int32 host array, each row the sequence's table padded
+ * with pad_block; context_lens_out [B] gets each length.  PA_ERR_INVALID if
+ * a seq is unknown or its table is longer than max_blocks (nothing
+ * written).  The caller uploads both arrays to the device. */
+int pa_bm_export_batch(const pa_bm* bm, const int64_t* seqs, int32_t B, int32_t* tables_out,
+                       int32_t max_blocks, int32_t pad_block, int32_t* context_lens_out);
+
+/* Check [P06] invariants I1-I5 (plus tight tables).  PA_OK, or
+ * PA_ERR_INVALID with the violated invariant in pa_last_error(). */
+int pa_bm_check_invariants(const pa_bm* bm);
+/* Observable state: ref[num_blocks], has_hash[num_blocks] (1 if a hash is
+ * registered on the block), the free list front to back in
+ * free_order[0..*n_free) and the evictable pool oldest to newest in
+ * evict_order[0..*n_evict).  Each array must hold num_blocks entries; any
+ * pointer may be NULL to skip that output. */
+int pa_bm_dump(const pa_bm* bm, int32_t* ref, int8_t* has_hash, int32_t* free_order,
+               int32_t* n_free, int32_t* evict_order, int32_t* n_evict);
+
+/* ==== device operations (gfx950) ========================================= */
+
+/* Paged KV write.  For t in [0, T): copy the row k_new[t] (num_kv_heads *
+ * head_dim elements) into K at flat slot s = slot_mapping[t], i.e.
+ * k_cache[s / block_size][s % block_size][:][:], and likewise v_new into V
+ * ([A130] KV-cache section: each step appends the new token's K and V;
+ * [D31]: it goes into the last, partly filled block).  Bitwise copy.
+ * k_new/v_new: device, [T][num_kv_heads][head_dim] in `dtype`.
+ * slot_mapping: device int64 [T].  A slot outside
+ * [0, num_blocks*block_size) is skipped (e.g. -1 for padding).
+ * Precondition: valid slots are unique (otherwise which row lands is
+ * unspecified).  T == 0 launches nothing. */
+int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                const int64_t* slot_mapping, int32_t T, int32_t num_blocks, int32_t block_size,
+                int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* stream);
+
+/* Copy-on-write block copy ([D31] toy COW append: the new private block
+ * receives the old block's KV bytes).  For every layer l < num_layers and
+ * every pair p < num_pairs: K_l[dst] = K_l[src] and V_l[dst] = V_l[src],
+ * whole blocks of `block_bytes` bytes (= block_size * num_kv_heads *
+ * head_dim * element size).  k_caches/v_caches: HOST arrays of num_layers
+ * device pointers.  pairs: device int32 [num_pairs][2] = (src, dst).
+ * A pair with an id outside [0, num_blocks) is skipped.  Preconditions:
+ * destinations are distinct and none is also a source.  block_bytes must be
+ * a positive multiple of 16 and every cache pointer 16-byte aligned. */
+int pa_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                   int64_t block_bytes, int32_t num_blocks, const int32_t* pairs,
+                   int32_t num_pairs, void* stream);
+
+/* Workspace bytes pa_decode needs for these sizes (0 when one partition
+ * covers max_context_len, i.e. partition_tokens == 0 or >= max_context_len). */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens);
+
+/* Paged decode attention ([A130] paged_attention pseudocode: gather the
+ * sequence's blocks through its block table, then scaled dot-product
+ * attention; kernel listing: layout, float output, scale).  For each
+ * sequence b and query head h, with g = h / (num_q_heads / num_kv_heads)
+ * and n = context_lens[b]:
+ *   s_t = scale * <q[b][h], K[slot(b,t)][g]>,  t < n
+ *   out[b][h] = sum_t softmax(s)_t * V[slot(b,t)][g]
+ * computed with float32 accumulation as an online softmax over split-KV
+ * partitions of `partition_tokens` tokens, combined by a reduce kernel.
+ *   out:  device float32 [B][num_q_heads][head_dim] (written, never read).
+ *   q:    device [B][num_q_heads][head_dim] in `dtype`.
+ *   k_cache, v_cache: device, one layer, layout above, in `dtype`.
+ *   block_tables: device int32 [B][max_blocks_per_seq]; entries past a
+ *     sequence's last block are never read.
+ *   context_lens: device int32 [B].
+ *   max_context_len: host-side upper bound of context_lens (sizes the grid;
+ *     no device-to-host read is made).
+ *   partition_tokens: multiple of block_size, or 0 for one partition.
+ *   workspace: device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
+ *     aligned (may be NULL when that is 0).
+ * Supported: dtype F32/F16/BF16, head_dim 64 or 128, block_size 16,
+ * num_q_heads a multiple of num_kv_heads with group size 1, 2, 4 or 8.
+ * Degenerate and invalid inputs: n == 0 gives a zero output row; a
+ * sequence with n < 0, n > max_context_len, more than max_blocks_per_seq
+ * blocks, or a table entry outside [0, num_blocks) gets NaN output rows
+ * (the kernel reads no out-of-range memory).  B == 0 launches nothing. */
+int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t max_context_len, int32_t B,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -8,20 +8,21 @@ Both are plain element copies on NumPy arrays in the pages' cache layout
 import numpy as np
 
 
-def ref_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping):
+def ref_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, inplace=False):
     """Scatter token t's K/V rows into flat slot ``slot_mapping[t]``.
 
     "qaqbuyan.com article 130", KV-cache section (each step computes the new
     token's K and V and appends them to the cache) and "day31" (a new token
     goes into the last, partly filled block).  Slots outside
     ``[0, num_blocks*block_size)`` are skipped; valid slots must be unique.
-    Returns new arrays; the inputs are not modified.
+    Returns new arrays (the inputs untouched), or with ``inplace`` writes
+    into ``k_cache``/``v_cache`` and returns them.
     """
     nb, bs = k_cache.shape[0], k_cache.shape[1]
     slots = np.asarray(slot_mapping, dtype=np.int64)
     valid = [(t, int(s)) for t, s in enumerate(slots) if 0 <= s < nb * bs]
     assert len({s for _, s in valid}) == len(valid), "duplicate slot"
-    k_out, v_out = k_cache.copy(), v_cache.copy()
+    k_out, v_out = (k_cache, v_cache) if inplace else (k_cache.copy(), v_cache.copy())
     k_flat = k_out.reshape(nb * bs, *k_cache.shape[2:])
     v_flat = v_out.reshape(nb * bs, *v_cache.shape[2:])
     for t, s in valid:
@@ -30,21 +31,22 @@ def ref_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping):
     return k_out, v_out
 
 
-def ref_copy_blocks(k_caches, v_caches, pairs):
+def ref_copy_blocks(k_caches, v_caches, pairs, inplace=False):
     """For every layer and every (src, dst): K[dst] = K[src], V[dst] = V[src].
 
     "day31", toy COW append: the new private block receives the old block's
     KV bytes.  The whole block (all slots) is copied.  Destinations must be
-    distinct and none may also be a source.  Returns new per-layer lists.
+    distinct and none may also be a source.  Returns new per-layer lists,
+    or with ``inplace`` copies within the given arrays and returns them.
     """
     pairs = [(int(s), int(d)) for s, d in pairs]
     dsts = [d for _, d in pairs]
     assert len(set(dsts)) == len(dsts), "duplicate destination"
     assert not (set(dsts) & {s for s, _ in pairs}), "destination is a source"
-    k_out = [k.copy() for k in k_caches]
-    v_out = [v.copy() for v in v_caches]
+    k_out = list(k_caches) if inplace else [k.copy() for k in k_caches]
+    v_out = list(v_caches) if inplace else [v.copy() for v in v_caches]
     for layer in range(len(k_out)):
         for s, d in pairs:
-            k_out[layer][d] = k_caches[layer][s]
-            v_out[layer][d] = v_caches[layer][s]
+            k_out[layer][d] = k_out[layer][s]
+            v_out[layer][d] = v_out[layer][s]
     return k_out, v_out

@@ -1,0 +1,19 @@
+"""MI355X-native paged-KV decode: Python binding of libpagedkv.so.
+
+* :class:`BlockManager` -- host block manager (``pa_bm_*``);
+* :func:`pa_write_kv`, :func:`pa_copy_blocks`, :func:`pa_decode`,
+  :func:`pa_decode_workspace_bytes` -- the device calls, on torch tensors.
+
+The C ABI is declared in ``include/pagedkv.h``.  Importing this package
+loads the library and fails if it has not been built
+(``python paged_kv_cache_136_amd/build.py``).
+"""
+
+from ._lib import LIB_PATH, OutOfBlocks, PagedKVError, lib
+from .block_manager import BlockManager
+from .ops import pa_copy_blocks, pa_decode, pa_decode_workspace_bytes, pa_write_kv
+
+lib()  # load now: a missing library is an import error, never a fallback
+
+__all__ = ["BlockManager", "OutOfBlocks", "PagedKVError", "pa_write_kv", "pa_copy_blocks",
+           "pa_decode", "pa_decode_workspace_bytes", "LIB_PATH"]

@@ -1,0 +1,444 @@
+// Paged decode attention for gfx950.
+//
+// What is computed: "qaqbuyan.com article 130", paged_attention pseudocode
+// (gather a sequence's K/V through its block table, then scaled dot-product
+// attention of the one query token) and kernel listing (cache layout
+// [num_blocks][block_size][heads][head_dim], float output, scale
+// 1/sqrt(head_dim)); slot of token pos = table[pos/bs]*bs + pos%bs ("P06 ·
+// BlockManager" spec overview).  Unlike that listing, only context_len
+// tokens are attended (the last block may be partly filled), the softmax is
+// an online (running max / running sum) softmax so scores never need to be
+// stored, and long sequences are split into partitions whose partial
+// results a second kernel combines.
+//
+// Phase 1 -- one workgroup of 4 waves per (partition, KV head, sequence):
+//   * the partition's block-table slice is staged in LDS once (and every
+//     entry range-checked);
+//   * wave w takes the partition's blocks w, w+4, w+8, ...;
+//   * a token row of one KV head (head_dim elements) is read by
+//     LPR = head_dim*elem/16 lanes with one 16-byte load each, so one load
+//     instruction covers 64/LPR rows and a 16-token block takes 16*LPR/64
+//     loads for K and as many for V; the next block's loads are issued
+//     before the current block is consumed;
+//   * QK partial dots are summed over the LPR lanes of a row with DPP;
+//     every query head of the GQA group reuses the same K/V registers;
+//   * running max m, sum l and output o are kept per query head in float32,
+//     in the exp2 domain (q.k is scaled by scale*log2(e));
+//   * the four waves' (m, l, o) are merged through LDS; a sequence with one
+//     partition writes out[] directly, otherwise (m, l, o/l) go to the
+//     workspace.
+// Phase 2 -- one wave per (query head, sequence) merges the partitions.
+//
+// Memory traffic is dominated by K and V: 2*len*Hkv*head_dim*elem bytes per
+// sequence and layer; every byte is read once.  Q, tables and partials are
+// under 1% of that at the supported shapes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "device_common.hpp"
+#include "pagedkv.h"
+#include "status.hpp"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;          // waves per phase-1 workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBlock = 16;         // tokens per KV block
+constexpr int kTableChunk = 256;   // table entries staged in LDS at a time
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeArgs {
+  float* out;            // [B][Hq][D]
+  float* ws_o;           // [B][Hq][P][D]  partition output, normalized
+  float* ws_m;           // [B][Hq][P]     partition max (exp2 domain)
+  float* ws_l;           // [B][Hq][P]     partition sum
+  const char* q;         // [B][Hq][D]
+  const char* k;         // [num_blocks][16][Hkv][D]
+  const char* v;
+  const int32_t* tables; // [B][max_blocks]
+  const int32_t* lens;   // [B]
+  int32_t max_blocks;
+  int32_t max_len;
+  int32_t hq, hkv;
+  int32_t num_blocks;
+  int32_t part_blocks;   // blocks per partition
+  int32_t num_parts;     // P = partitions of max_len
+  float scale_log2;      // scale * log2(e)
+};
+
+__device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
+  return n >= 0 && n <= a.max_len && (n + kBlock - 1) / kBlock <= a.max_blocks;
+}
+
+__device__ __forceinline__ int num_parts_of(int n, int part_blocks) {
+  int nb = (n + kBlock - 1) / kBlock;
+  return nb == 0 ? 1 : (nb + part_blocks - 1) / part_blocks;
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
+  constexpr int ELEM = ElemTraits<DT>::bytes;
+  constexpr int EPL = 16 / ELEM;          // elements per lane per load
+  constexpr int LPR = D * ELEM / 16;      // lanes per token row
+  constexpr int RPI = 64 / LPR;           // rows per load instruction
+  constexpr int LPB = kBlock / RPI;       // loads per block (K or V)
+  static_assert(LPR >= 1 && LPR <= 64 && RPI * LPR == 64 && LPB * RPI == kBlock, "shape");
+
+  __shared__ int32_t s_tab[kTableChunk];
+  __shared__ int32_t s_bad;
+  __shared__ float s_m[kWaves][G], s_l[kWaves][G];
+  __shared__ float s_o[kWaves][G][D];
+
+  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane / LPR, c = lane % LPR;
+  const int n = a.lens[b];
+  const bool valid = len_valid(n, a);
+  const int nblk = valid ? (n + kBlock - 1) / kBlock : 0;
+  const int nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
+  if (part >= nparts) return;
+  const int h0 = g * G;
+
+  // Degenerate rows: empty sequence -> 0, invalid length -> NaN.
+  if (!valid || n == 0) {
+    const float fill = valid ? 0.f : __builtin_nanf("");
+    for (int i = tid; i < G * D; i += kThreads)
+      a.out[(static_cast<size_t>(b) * a.hq + h0 + i / D) * D + i % D] = fill;
+    return;
+  }
+
+  // Query chunk of every head of the group, as float.
+  float qf[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint4 w4 = *reinterpret_cast<const uint4*>(
+        a.q + ((static_cast<size_t>(b) * a.hq + h0 + hh) * D + c * EPL) * ELEM);
+    unpack16<DT>(w4, qf[hh]);
+  }
+
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
+  }
+
+  // Byte offset of this lane's chunk in load i of a block.
+  const size_t row_bytes = static_cast<size_t>(a.hkv) * D * ELEM;
+  const size_t block_bytes = row_bytes * kBlock;
+  uint32_t lane_off[LPB];
+#pragma unroll
+  for (int i = 0; i < LPB; ++i)
+    lane_off[i] = static_cast<uint32_t>((i * RPI + r) * row_bytes + (static_cast<size_t>(g) * D + c * EPL) * ELEM);
+
+  const int first = part * a.part_blocks;
+  const int last = min(nblk, first + a.part_blocks);   // exclusive
+  const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
+  if (tid == 0) s_bad = 0;
+
+  // Consume one block: scores, online-softmax update, PV accumulation.
+  auto consume = [&](const uint4 (&kw)[LPB], const uint4 (&vw)[LPB], int valid_rows) {
+    float s[G][LPB];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      float kf[EPL];
+      unpack16<DT>(kw[i], kf);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[hh][e], kf[e], acc);
+        acc = group_sum<1, LPR>(acc);
+        s[hh][i] = (i * RPI + r < valid_rows) ? acc * a.scale_log2 : -INFINITY;
+      }
+    }
+    float vf[LPB][EPL];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      unpack16<DT>(vw[i], vf[i]);
+      if (i * RPI + r >= valid_rows) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[i][e] = 0.f;   // select, never 0*NaN
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float bm = s[hh][0];
+#pragma unroll
+      for (int i = 1; i < LPB; ++i) bm = fmaxf(bm, s[hh][i]);
+      bm = group_max<LPR, 64>(bm);
+      const float mn = fmaxf(m[hh], bm);
+      const float alpha = fast_exp2(m[hh] - mn);
+      m[hh] = mn;
+      float ps = 0.f;
+      float acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = o[hh][e] * alpha;
+#pragma unroll
+      for (int i = 0; i < LPB; ++i) {
+        const float p = fast_exp2(s[hh][i] - mn);
+        ps += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[i][e], acc[e]);
+      }
+      l[hh] = l[hh] * alpha + ps;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[hh][e] = acc[e];
+    }
+  };
+
+  auto load_block = [&](int blk, uint4 (&kw)[LPB], uint4 (&vw)[LPB]) {
+    const char* kb = a.k + static_cast<size_t>(blk) * block_bytes;
+    const char* vb = a.v + static_cast<size_t>(blk) * block_bytes;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) kw[i] = *reinterpret_cast<const uint4*>(kb + lane_off[i]);
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) vw[i] = *reinterpret_cast<const uint4*>(vb + lane_off[i]);
+  };
+
+  for (int base = first; base < last; base += kTableChunk) {
+    const int cnt = min(kTableChunk, last - base);
+    __syncthreads();                       // previous chunk fully consumed
+    for (int i = tid; i < cnt; i += kThreads) {
+      const int32_t e = trow[base + i];
+      const bool ok = e >= 0 && e < a.num_blocks;
+      s_tab[i] = ok ? e : 0;
+      if (!ok) s_bad = 1;
+    }
+    __syncthreads();
+    if (s_bad) break;
+    // This wave's blocks in the chunk: w, w+4, ...; one block of lookahead.
+    uint4 ka[LPB], va[LPB], kb[LPB], vb[LPB];
+    int j = w;
+    if (j < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[j]), ka, va);
+    for (; j < cnt; j += 2 * kWaves) {
+      const int j1 = j + kWaves, j2 = j + 2 * kWaves;
+      if (j1 < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[j1]), kb, vb);
+      consume(ka, va, min(kBlock, n - (base + j) * kBlock));
+      if (j1 < cnt) {
+        if (j2 < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[j2]), ka, va);
+        consume(kb, vb, min(kBlock, n - (base + j1) * kBlock));
+      }
+    }
+  }
+
+  // Wave result: combine the RPI row groups of each lane's chunk.
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    l[hh] = group_sum<LPR, 64>(l[hh]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[hh][e] = group_sum<LPR, 64>(o[hh][e]);
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_o[w][hh][c * EPL + e] = o[hh][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      s_m[w][hh] = m[hh];
+      s_l[w][hh] = l[hh];
+    }
+  }
+  __syncthreads();
+
+  const bool bad = s_bad != 0;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int hh = i / D, d = i % D;
+    float M = s_m[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][hh]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = fast_exp2(s_m[ww][hh] - M);   // 0 for a wave with no block
+      L = fmaf(s_l[ww][hh], f, L);
+      O = fmaf(s_o[ww][hh][d], f, O);
+    }
+    const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
+    const float res = bad ? __builtin_nanf("") : O / L;
+    if (nparts == 1) {
+      a.out[bh * D + d] = res;
+    } else {
+      const size_t bhp = bh * a.num_parts + part;
+      a.ws_o[bhp * D + d] = res;
+      if (d == 0) {
+        a.ws_m[bhp] = bad ? 0.f : M;
+        a.ws_l[bhp] = bad ? __builtin_nanf("") : L;
+      }
+    }
+  }
+}
+
+// Phase 2: out = sum_p w_p * o_p with w_p = l_p 2^(m_p - M) / sum_q l_q 2^(m_q - M).
+template <int D>
+__global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int n = a.lens[b];
+  if (!len_valid(n, a)) return;
+  const int nparts = num_parts_of(n, a.part_blocks);
+  if (nparts <= 1) return;                 // phase 1 wrote the output
+  const size_t bh = static_cast<size_t>(b) * a.hq + h;
+  const float* pm = a.ws_m + bh * a.num_parts;
+  const float* pl = a.ws_l + bh * a.num_parts;
+  float M = -INFINITY;
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, pm[p]);
+  M = group_max<1, 64>(M);
+  float L = 0.f;
+  for (int p = lane; p < nparts; p += 64) L += pl[p] * fast_exp2(pm[p] - M);
+  L = group_sum<1, 64>(L);
+  const float inv = 1.f / L;
+  constexpr int PER = D / 64;
+  float acc[PER] = {};
+  for (int p = 0; p < nparts; ++p) {
+    const float wgt = pl[p] * fast_exp2(pm[p] - M) * inv;
+    const float* po = a.ws_o + (bh * a.num_parts + p) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, po[lane + 64 * e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) a.out[bh * D + lane + 64 * e] = acc[e];
+}
+
+template <int DT, int D>
+hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
+  dim3 grid(a.num_parts, a.hkv, B);
+  switch (group) {
+    case 1: decode_phase1<DT, D, 1><<<grid, kThreads, 0, st>>>(a); break;
+    case 2: decode_phase1<DT, D, 2><<<grid, kThreads, 0, st>>>(a); break;
+    case 4: decode_phase1<DT, D, 4><<<grid, kThreads, 0, st>>>(a); break;
+    case 8: decode_phase1<DT, D, 8><<<grid, kThreads, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (a.num_parts > 1) decode_reduce<D><<<dim3(a.hq, B), 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const DecodeArgs& a, int B, int D, int group, hipStream_t st) {
+  if (D == 64) return launch_dt_d<DT, 64>(a, B, group, st);
+  return launch_dt_d<DT, 128>(a, B, group, st);
+}
+
+int32_t part_blocks_for(int32_t max_len, int32_t partition_tokens) {
+  if (partition_tokens > 0) return partition_tokens / kBlock;
+  const int32_t nb = (max_len + kBlock - 1) / kBlock;
+  return nb > 0 ? nb : 1;
+}
+
+struct WsLayout {
+  size_t o_off, m_off, l_off, total;
+};
+
+WsLayout ws_layout(int32_t B, int32_t hq, int32_t D, int32_t P) {
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  WsLayout w{};
+  if (P <= 1) return w;
+  const size_t bhp = static_cast<size_t>(B) * hq * P;
+  w.o_off = 0;
+  w.m_off = al(bhp * D * sizeof(float));
+  w.l_off = w.m_off + al(bhp * sizeof(float));
+  w.total = w.l_off + al(bhp * sizeof(float));
+  return w;
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                            int32_t max_context_len, int32_t partition_tokens) {
+  if (B <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_tokens < 0)
+    return 0;
+  const int32_t pb = part_blocks_for(max_context_len, partition_tokens);
+  if (pb <= 0) return 0;
+  const int32_t nb = (max_context_len + kBlock - 1) / kBlock;
+  const int32_t P = nb == 0 ? 1 : (nb + pb - 1) / pb;
+  return ws_layout(B, num_q_heads, head_dim, P).total;
+}
+
+extern "C" int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, float scale,
+                         int32_t partition_tokens, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (B < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID, "pa_decode: negative size or empty pool");
+  if (B == 0) { clear_error(); return PA_OK; }
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID, "pa_decode: null pointer");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "pa_decode: num_q_heads must be a positive multiple of num_kv_heads");
+  const int group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: query group size must be 1, 2, 4 or 8");
+  if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size must be 16");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim must be 64 or 128");
+  if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: unknown dtype");
+  if (partition_tokens < 0 || partition_tokens % kBlock != 0)
+    return fail(PA_ERR_INVALID, "pa_decode: partition_tokens must be 0 or a multiple of 16");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_decode: scale must be finite");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) & 15)
+    return fail(PA_ERR_INVALID, "pa_decode: q and caches must be 16-byte aligned");
+  const size_t block_bytes = static_cast<size_t>(num_kv_heads) * head_dim * kBlock *
+                             (dtype == PA_DTYPE_F32 ? 4 : 2);
+  if (block_bytes >= (static_cast<size_t>(1) << 31))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: one block of one layer must be under 2 GiB");
+  // Grid limits: partitions on x, KV heads on y (<= 65535), sequences on z.
+  if (num_kv_heads > 65535 || B > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: too many heads or sequences for one launch");
+
+  DecodeArgs a{};
+  a.part_blocks = part_blocks_for(max_context_len, partition_tokens);
+  const int32_t nb = (max_context_len + kBlock - 1) / kBlock;
+  a.num_parts = nb == 0 ? 1 : (nb + a.part_blocks - 1) / a.part_blocks;
+  const WsLayout wl = ws_layout(B, num_q_heads, head_dim, a.num_parts);
+  if (wl.total > 0) {
+    if (!workspace || workspace_bytes < wl.total)
+      return fail(PA_ERR_INVALID, "pa_decode: workspace too small (need " +
+                                      std::to_string(wl.total) + " bytes)");
+    if (reinterpret_cast<uintptr_t>(workspace) & 15)
+      return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
+    a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
+    a.ws_l = reinterpret_cast<float*>(ws + wl.l_off);
+  }
+  a.out = out;
+  a.q = static_cast<const char*>(q);
+  a.k = static_cast<const char*>(k_cache);
+  a.v = static_cast<const char*>(v_cache);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_len = max_context_len;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * kLog2e;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  switch (dtype) {
+    case PA_DTYPE_F32: err = launch_dt<PA_DTYPE_F32>(a, B, head_dim, group, st); break;
+    case PA_DTYPE_F16: err = launch_dt<PA_DTYPE_F16>(a, B, head_dim, group, st); break;
+    default: err = launch_dt<PA_DTYPE_BF16>(a, B, head_dim, group, st); break;
+  }
+  if (err != hipSuccess)
+    return fail(PA_ERR_DEVICE, std::string("pa_decode: launch failed: ") + hipGetErrorString(err));
+  clear_error();
+  return PA_OK;
+}

@@ -1,0 +1,118 @@
+"""torch-tensor front end of the device calls (argument marshalling only).
+
+Each function checks shapes, dtypes and devices, then calls the C entry
+point of the same name on the current HIP stream.  Every step of the path
+runs in the library's kernels; nothing here computes.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import (PA_DTYPE_BF16, PA_DTYPE_F16, PA_DTYPE_F32, c_vp, check, lib)
+
+_DTYPES = {torch.float32: PA_DTYPE_F32, torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensor must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
+    """Scatter k_new/v_new [T, Hkv, D] into caches [num_blocks, bs, Hkv, D]
+    at int64 slot_mapping [T] (out-of-range slots are skipped)."""
+    _dev(k_cache, v_cache, k_new, v_new, slot_mapping)
+    nb, bs, hkv, d = k_cache.shape
+    T = k_new.shape[0]
+    if v_cache.shape != k_cache.shape or k_new.shape != (T, hkv, d) or v_new.shape != (T, hkv, d):
+        raise ValueError("shape mismatch")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if not (k_cache.dtype == v_cache.dtype == k_new.dtype == v_new.dtype):
+        raise ValueError("dtype mismatch")
+    check(lib().pa_write_kv(k_cache.data_ptr(), v_cache.data_ptr(), k_new.data_ptr(),
+                            v_new.data_ptr(), slot_mapping.data_ptr(), T, nb, bs, hkv, d,
+                            _dtype_code(k_cache), _stream(stream)))
+
+
+def pa_copy_blocks(k_caches, v_caches, pairs, stream=None):
+    """For each layer's caches and each (src, dst) row of int32 ``pairs``
+    [P, 2] on the GPU: K[dst] = K[src], V[dst] = V[src] (whole blocks)."""
+    k_caches, v_caches = list(k_caches), list(v_caches)
+    if len(k_caches) != len(v_caches):
+        raise ValueError("K and V layer counts differ")
+    _dev(pairs, *k_caches, *v_caches)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [P, 2]")
+    if not k_caches:
+        return
+    shape = k_caches[0].shape
+    for t in k_caches + v_caches:
+        if t.shape != shape or t.dtype != k_caches[0].dtype:
+            raise ValueError("all caches must share shape and dtype")
+    nb = shape[0]
+    block_bytes = k_caches[0][0].numel() * k_caches[0].element_size()
+    L = len(k_caches)
+    kp = (c_vp * L)(*[t.data_ptr() for t in k_caches])
+    vp = (c_vp * L)(*[t.data_ptr() for t in v_caches])
+    check(lib().pa_copy_blocks(kp, vp, L, block_bytes, nb, pairs.data_ptr(), pairs.shape[0],
+                               _stream(stream)))
+
+
+def pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partition_tokens):
+    return lib().pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len,
+                                           partition_tokens)
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
+              partition_tokens=512, out=None, workspace=None, stream=None):
+    """Paged decode attention; returns float32 out [B, Hq, D].
+
+    q [B, Hq, D] and caches [num_blocks, 16, Hkv, D] share a dtype;
+    block_tables int32 [B, max_blocks]; context_lens int32 [B];
+    max_context_len is a host int bounding context_lens."""
+    _dev(q, k_cache, v_cache, block_tables, context_lens)
+    B, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and caches must share a dtype")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (B, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [B, Hq, D]")
+    need = pa_decode_workspace_bytes(B, hq, d, int(max_context_len), int(partition_tokens))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                          block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                          int(max_context_len), B, hq, hkv, d, bs, nb, float(scale),
+                          int(partition_tokens), _dtype_code(q), ws_ptr, ws_bytes,
+                          _stream(stream)))
+    return out

@@ -1,0 +1,364 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: KV writes, COW copies, slots and tables bit-exact; attention within
+max |err| 2e-3 for fp16/bf16 inputs (1e-4 for fp32 inputs) against the
+float64 oracle.  Inputs are seeded (host NumPy for small cases, torch's
+device generator for full-size ones, whose bytes the oracle reads back);
+no oracle input comes from a HIP kernel's output.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import (TOL, TORCH_DTYPES, host_f32, make_cache, poison_mask,
+                            random_tables, say)
+
+pytestmark = pytest.mark.gpu
+
+pkv = pytest.importorskip("paged_kv_cache_136_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(t):
+    """Raw bit pattern of a device tensor as a host integer array."""
+    it = {4: torch.int32, 2: torch.int16}[t.element_size()]
+    return t.detach().contiguous().view(it).cpu().numpy()
+
+
+# ---------------------------------------------------------------- write / copy
+
+@pytest.mark.parametrize("dtype,hkv,d", [("f32", 4, 64), ("f16", 8, 128), ("bf16", 2, 128)])
+def test_write_kv_bitexact(dtype, hkv, d):
+    nb, bs, T = 64, 16, 40
+    say("write_kv", dtype, hkv, d)
+    k, v = make_cache(nb, bs, hkv, d, dtype, seed=10)
+    kn = workloads.normal_torch((T, hkv, d), 11, TORCH_DTYPES[dtype], "cuda")
+    vn = workloads.normal_torch((T, hkv, d), 12, TORCH_DTYPES[dtype], "cuda")
+    rng = np.random.default_rng(0)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    slots[[3, 17, 39]] = [-1, nb * bs, -5]          # skipped (out of range)
+    kb, vb = _bits(k), _bits(v)
+    want_k, want_v = oracle.ref_write_kv(kb, vb, _bits(kn), _bits(vn), slots)
+    pkv.pa_write_kv(k, v, kn, vn, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(k), want_k)
+    assert np.array_equal(_bits(v), want_v)
+
+
+def test_copy_blocks_bitexact():
+    nb, bs, hkv, d, L = 48, 16, 4, 128, 3
+    say("copy_blocks")
+    ks, vs = zip(*[make_cache(nb, bs, hkv, d, "f16", seed=20 + 2 * i) for i in range(L)])
+    pairs = np.array([[1, 5], [7, 2], [30, 31], [47, 0]], dtype=np.int32)
+    want_k, want_v = oracle.ref_copy_blocks([_bits(k) for k in ks], [_bits(v) for v in vs], pairs)
+    pkv.pa_copy_blocks(ks, vs, torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    for i in range(L):
+        assert np.array_equal(_bits(ks[i]), want_k[i])
+        assert np.array_equal(_bits(vs[i]), want_v[i])
+    # Ids outside the pool are skipped; the rest of the pool is untouched.
+    before = [_bits(k) for k in ks]
+    bad = torch.tensor([[-1, 3], [4, nb], [nb + 7, 9]], dtype=torch.int32, device="cuda")
+    pkv.pa_copy_blocks(ks, vs, bad)
+    torch.cuda.synchronize()
+    for i in range(L):
+        assert np.array_equal(_bits(ks[i]), before[i])
+
+
+# ---------------------------------------------------------------- decode
+
+def _run_decode(lens, hq, hkv, d, dtype, partition, seed, poison=True, num_blocks=None):
+    bs = 16
+    need = sum(-(-int(n) // bs) for n in lens)
+    num_blocks = num_blocks or need + 5
+    tables = random_tables(lens, bs, num_blocks, seed, pad=0)
+    mask = poison_mask(tables, lens, num_blocks, bs) if poison else None
+    k, v = make_cache(num_blocks, bs, hkv, d, dtype, seed, poison=mask)
+    q = workloads.normal_torch((len(lens), hq, d), seed + 7, TORCH_DTYPES[dtype], "cuda")
+    max_len = int(max(lens)) if len(lens) else 0
+    out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(),
+                        torch.tensor(lens, dtype=torch.int32, device="cuda"), max_len,
+                        partition_tokens=partition)
+    torch.cuda.synchronize()
+    want = oracle.ref_decode(host_f32(q), host_f32(k), host_f32(v), tables, lens)
+    return out.cpu().numpy().astype(np.float64), want
+
+
+RAGGED = [1, 15, 16, 17, 31, 33, 64, 100, 511, 512, 513, 700]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_ragged(dtype, d, group):
+    hkv = 2
+    say("decode_ragged", dtype, d, group)
+    got, want = _run_decode(RAGGED, hkv * group, hkv, d, dtype, 128, seed=100 + d + group)
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max()
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("partition", [0, 16, 64, 256, 512, 4096])
+def test_decode_partition_sizes(partition):
+    say("decode_partition", partition)
+    got, want = _run_decode([1, 300, 1000, 2049], 8, 4, 128, "f16", partition, seed=7)
+    assert np.abs(got - want).max() <= TOL["f16"]
+
+
+def test_decode_tiny_workload():
+    """Lengths [7,16,31,48,63], 4 heads x 64, fp32, scale 1/8, 64-block pool;
+    tables built by the library's block manager with the prefix cache on
+    (the five prompts are prefixes of one stream, so blocks are shared) and
+    checked against the oracle's manager."""
+    cfg = workloads.CONFIGS["tiny"]
+    lens = cfg["lens"]
+    stream = workloads.token_ids(max(lens), seed=0)
+    bm = pkv.BlockManager(cfg["num_blocks"], 16, True)
+    rbm = oracle.RefBlockManager(cfg["num_blocks"], 16, True)
+    for i, n in enumerate(lens):
+        assert bm.allocate(i, stream[:n - 1]) == rbm.allocate(i, stream[:n - 1])
+    slots, pairs = bm.append_slots(list(range(5)), [stream[n - 1] for n in lens])
+    want_slots = [rbm.append_slot(i, stream[n - 1])[0] for i, n in enumerate(lens)]
+    assert slots.tolist() == want_slots and len(pairs) == 0
+    tables, clens = bm.export_batch(list(range(5)), max_blocks=4, pad_block=63)
+    assert clens.tolist() == lens
+    for i in range(5):
+        assert tables[i, :len(rbm.get_table(i))].tolist() == rbm.get_table(i)
+    say("decode tiny workload")
+    mask = poison_mask(tables, lens, 64, 16)
+    k, v = make_cache(64, 16, 4, 64, "f32", seed=0, poison=mask)
+    q = workloads.normal_torch((5, 4, 64), 3, torch.float32, "cuda")
+    out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(),
+                        torch.from_numpy(clens).cuda(), max(lens), scale=1 / 8)
+    torch.cuda.synchronize()
+    want = oracle.ref_decode(host_f32(q), host_f32(k), host_f32(v), tables, clens, scale=1 / 8)
+    assert np.abs(out.cpu().numpy() - want).max() <= TOL["f32"]
+
+
+def test_decode_edge_cases():
+    """Length 0 -> zero row; a length over max_context_len or a table entry
+    outside the pool -> NaN rows for that sequence only; B == 0 is a no-op."""
+    bs, nb, hq, d = 16, 40, 4, 64
+    lens = np.array([0, 20, 50, 33], dtype=np.int32)
+    tables = random_tables(lens, bs, nb, 3, pad=0)
+    tables[3, 1] = nb + 100                      # bad entry inside seq 3's range
+    k, v = make_cache(nb, bs, 2, d, "f16", seed=4)
+    q = workloads.normal_torch((4, hq, d), 5, torch.float16, "cuda")
+    lens_dev = torch.from_numpy(lens).cuda()
+    lens_dev[2] = 60                             # > max_context_len below
+    say("decode edge cases")
+    out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(), lens_dev, 50,
+                        partition_tokens=16).cpu().numpy()
+    assert (out[0] == 0).all()
+    assert np.isnan(out[2]).all() and np.isnan(out[3]).all()
+    want = oracle.ref_decode(host_f32(q)[1:2], host_f32(k), host_f32(v), tables[1:2], lens[1:2])
+    assert np.abs(out[1] - want[0]).max() <= TOL["f16"]
+    empty = torch.empty((0, hq, d), dtype=torch.float16, device="cuda")
+    r = pkv.pa_decode(empty, k, v, torch.empty((0, 4), dtype=torch.int32, device="cuda"),
+                      torch.empty(0, dtype=torch.int32, device="cuda"), 0)
+    assert r.shape == (0, hq, d)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(), lens_dev, 50, partition_tokens=24)
+
+
+def test_placement_invariance():
+    """The same logical K/V under two different tables gives bitwise-equal
+    outputs (the kernel's arithmetic depends only on logical positions)."""
+    lens = [37, 600, 1025]
+    bs, hkv, d = 16, 4, 128
+    need = sum(-(-n // bs) for n in lens)
+    nb = need + 10
+    t1 = random_tables(lens, bs, nb, 1, pad=0)
+    t2 = random_tables(lens, bs, nb, 2, pad=0)
+    k1, v1 = make_cache(nb, bs, hkv, d, "bf16", seed=9)
+    k2, v2 = torch.empty_like(k1), torch.empty_like(v1)
+    m1, m2 = torch.from_numpy(t1).long().cuda(), torch.from_numpy(t2).long().cuda()
+    for b, n in enumerate(lens):
+        nblk = -(-n // bs)
+        k2[m2[b, :nblk]] = k1[m1[b, :nblk]]
+        v2[m2[b, :nblk]] = v1[m1[b, :nblk]]
+    q = workloads.normal_torch((3, 8, d), 10, torch.bfloat16, "cuda")
+    L = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    say("placement invariance")
+    o1 = pkv.pa_decode(q, k1, v1, m1.int(), L, max(lens))
+    o2 = pkv.pa_decode(q, k2, v2, m2.int(), L, max(lens))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_decode_13b_layer_full():
+    """Llama-2-13B layer: 10 x 4096 tokens, 40 heads x 128, fp16, tables =
+    seeded shuffle of a 4096-block pool; every output element checked."""
+    cfg = workloads.CONFIGS["13b_layer"]
+    lens = workloads.lengths("13b_layer")
+    say("13b layer full size")
+    got, want = _run_decode(lens, cfg["hq"], cfg["hkv"], cfg["d"], "f16",
+                            cfg["partition_tokens"], seed=13, poison=False,
+                            num_blocks=cfg["num_blocks"])
+    err = np.abs(got - want).max()
+    assert err <= TOL["f16"], err
+
+
+def _sub_pool(k, v, tables, lens, rows, bs, seed):
+    """Host copies of just the blocks that the sampled rows read, renumbered
+    by a seeded permutation (the oracle still gathers through a table)."""
+    blocks = sorted({int(b) for r in rows for b in tables[r, :-(-int(lens[r]) // bs)]})
+    perm = np.random.default_rng(seed).permutation(len(blocks))
+    new_id = {b: int(perm[i]) for i, b in enumerate(blocks)}
+    order = torch.tensor([blocks[j] for j in np.argsort(perm)], device=k.device)
+    ks = host_f32(k.index_select(0, order))
+    vs = host_f32(v.index_select(0, order))
+    sub_tables = np.zeros((len(rows), tables.shape[1]), dtype=np.int64)
+    for i, r in enumerate(rows):
+        nblk = -(-int(lens[r]) // bs)
+        sub_tables[i, :nblk] = [new_id[int(b)] for b in tables[r, :nblk]]
+    return ks, vs, sub_tables
+
+
+def test_decode_gqa_long_full():
+    """GQA 32/8 x 128, bf16, 32 x 32768 tokens, 131072-block pool, 512-token
+    partitions (the launch configuration timed); 4 sampled sequences checked
+    on all 32 query heads."""
+    cfg = workloads.CONFIGS["gqa_long"]
+    lens = workloads.lengths("gqa_long")
+    bs, nb = 16, cfg["num_blocks"]
+    tables = random_tables(lens, bs, nb, seed=55, pad=0)
+    say("gqa long: allocating 8 GiB cache")
+    k, v = make_cache(nb, bs, cfg["hkv"], cfg["d"], "bf16", seed=56)
+    q = workloads.normal_torch((32, cfg["hq"], cfg["d"]), 57, torch.bfloat16, "cuda")
+    say("gqa long: decode")
+    out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(),
+                        torch.from_numpy(lens.astype(np.int32)).cuda(), int(lens.max()),
+                        partition_tokens=cfg["partition_tokens"])
+    torch.cuda.synchronize()
+    rows = [0, 7, 19, 31]
+    ks, vs, st = _sub_pool(k, v, tables, lens, rows, bs, 58)
+    qh = host_f32(q)
+    want = oracle.ref_decode(qh[rows], ks, vs, st, lens[rows])
+    got = out.cpu().numpy()[rows]
+    err = np.abs(got - want).max()
+    assert err <= TOL["bf16"], err
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_decode_mixed_7b_layer_full():
+    """Mixed-length batch, 7B shape: one full-size layer (128 sequences,
+    lengths log-uniform in [50, 4096] seed 0, 16384-block pool, 32 heads x
+    128 fp16), tables from the library's block manager on a scrambled free
+    list (checked against the oracle's manager); all outputs checked, for
+    two layers' worth of data."""
+    cfg = workloads.CONFIGS["mixed_7b"]
+    lens = workloads.lengths("mixed_7b")
+    bs, nb = 16, cfg["num_blocks"]
+    order = workloads.block_order(nb, seed=1)
+    bm = pkv.BlockManager(nb, bs, False)
+    rbm = oracle.RefBlockManager(nb, bs, False)
+    workloads.scramble_free_list(bm, order)
+    workloads.scramble_free_list(rbm, order)
+    toks = workloads.token_ids(int(lens.max()), seed=2)
+    for i, n in enumerate(lens):
+        assert bm.allocate(i, toks[:n - 1]) == rbm.allocate(i, toks[:n - 1])
+    slots, _ = bm.append_slots(list(range(len(lens))), [5] * len(lens))
+    assert slots.tolist() == [rbm.append_slot(i, 5)[0] for i in range(len(lens))]
+    max_blocks = -(-int(lens.max()) // bs)
+    tables, clens = bm.export_batch(list(range(len(lens))), max_blocks, pad_block=0)
+    assert clens.tolist() == lens.tolist()
+    for layer_seed in (300, 331):
+        say("mixed 7b layer", layer_seed)
+        k, v = make_cache(nb, bs, cfg["hkv"], cfg["d"], "f16", seed=layer_seed)
+        q = workloads.normal_torch((len(lens), cfg["hq"], cfg["d"]), layer_seed + 5,
+                                   torch.float16, "cuda")
+        out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(),
+                            torch.from_numpy(clens).cuda(), int(lens.max()),
+                            partition_tokens=cfg["partition_tokens"])
+        torch.cuda.synchronize()
+        rows = list(range(len(lens)))
+        ks, vs, st = _sub_pool(k, v, tables, lens, rows, bs, layer_seed)
+        want = oracle.ref_decode(host_f32(q), ks, vs, st, lens)
+        err = np.abs(out.cpu().numpy() - want).max()
+        assert err <= TOL["f16"], err
+        del k, v, ks, vs
+        torch.cuda.empty_cache()
+
+
+def test_fork_cow_full_flow():
+    """Parallel sampling: 64 prompts x 2048 tokens (prefix cache on), each
+    parent appends one sampled token, then forks 7 children; all 512
+    sequences append 256 tokens.  Every step's slots and COW pairs must equal
+    the oracle manager's; the caches after all COW copies and writes must be
+    bit-identical to the oracle's; decode over all 512 forks is checked on
+    16 sampled forks (all heads)."""
+    cfg = workloads.CONFIGS["fork_cow"]
+    bs, nb, H, d = 16, cfg["num_blocks"], cfg["hkv"], cfg["d"]
+    P, F, L0, X = cfg["prompts"], cfg["forks"], cfg["prompt_len"], cfg["extra"]
+    bm = pkv.BlockManager(nb, bs, True)
+    rbm = oracle.RefBlockManager(nb, bs, True)
+    say("fork_cow: cache")
+    k, v = make_cache(nb, bs, H, d, "f16", seed=40)
+    kh, vh = _bits(k), _bits(v)                       # oracle's cache (bits)
+    for p in range(P):
+        prompt = workloads.token_ids(L0, seed=1000 + p)
+        assert bm.allocate(p * F, prompt) == rbm.allocate(p * F, prompt)
+
+    def step(seqs, toks, rnd):
+        slots, pairs = bm.append_slots(seqs, toks)
+        want = [rbm.append_slot(s, t) for s, t in zip(seqs, toks)]
+        assert slots.tolist() == [w[0] for w in want]
+        wp = [w[1] for w in want if w[1] is not None]
+        assert [tuple(x) for x in pairs.tolist()] == wp
+        kn = workloads.normal_torch((len(seqs), H, d), 5000 + rnd, torch.float16, "cuda")
+        vn = workloads.normal_torch((len(seqs), H, d), 9000 + rnd, torch.float16, "cuda")
+        if len(pairs):
+            pkv.pa_copy_blocks([k], [v], torch.from_numpy(pairs).cuda())
+            oracle.ref_copy_blocks([kh], [vh], wp, inplace=True)
+        pkv.pa_write_kv(k, v, kn, vn, torch.from_numpy(slots).cuda())
+        oracle.ref_write_kv(kh, vh, _bits(kn), _bits(vn), slots, inplace=True)
+        return len(wp)
+
+    parents = [p * F for p in range(P)]
+    say("fork_cow: parent tokens")
+    step(parents, [7] * P, 0)
+    for p in parents:
+        for c in range(1, F):
+            bm.fork(p, p + c)
+            rbm.fork(p, p + c)
+    seqs = [p + c for p in parents for c in range(F)]
+    ncow = 0
+    say("fork_cow: 256 append rounds")
+    for r in range(X):
+        ncow += step(seqs, workloads.token_ids(len(seqs), seed=20000 + r), r + 1)
+    assert ncow == P * (F - 1) == 448
+    assert bm.dump()["ref"] == rbm.dump()["ref"]
+    assert nb - bm.num_free_blocks == P * 264
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(k), kh) and np.array_equal(_bits(v), vh)
+    max_blocks = -(-(L0 + 1 + X) // bs)
+    tables, clens = bm.export_batch(seqs, max_blocks, pad_block=0)
+    assert (clens == L0 + 1 + X).all()
+    q = workloads.normal_torch((len(seqs), H, d), 77, torch.float16, "cuda")
+    say("fork_cow: decode 512 forks")
+    out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(clens).cuda(),
+                        L0 + 1 + X, partition_tokens=cfg["partition_tokens"])
+    torch.cuda.synchronize()
+    rows = list(range(0, 8)) + list(range(8 * 37, 8 * 37 + 8))
+    kf = kh.view(np.float16)
+    vf = vh.view(np.float16)
+    ref_tables = np.array([rbm.get_table(seqs[r]) for r in rows])
+    want = oracle.ref_decode(host_f32(q)[rows], kf, vf, ref_tables, clens[rows])
+    err = np.abs(out.cpu().numpy()[rows] - want).max()
+    assert err <= TOL["f16"], err
