@@ -45,7 +45,30 @@ def parse_args():
     p.add_argument("--partition-tokens", type=int, default=512)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    p.add_argument("--calibrate", action="store_true",
+                   help="instead of the step: run pa_copy_blocks over a known number of "
+                        "bytes (3 launches of 8192 x 128 KiB blocks, K and V), for scaling "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return p.parse_args()
+
+
+def calibrate():
+    """pa_copy_blocks over 8192 disjoint block pairs of 128 KiB in one layer's
+    K and V: each launch reads and writes exactly 2 * 8192 * 128 KiB = 2 GiB."""
+    import torch
+
+    import paged_kv_cache_136_amd as pkv
+
+    nb, block = 16384, (16, 32, 128)
+    k = torch.zeros((nb, *block), dtype=torch.float16, device="cuda")
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(0, 8192), torch.arange(8192, 16384)], 1).int().cuda()
+    for _ in range(3):
+        pkv.pa_copy_blocks([k], [v], pairs)
+    torch.cuda.synchronize()
+    nbytes = 2 * 8192 * k[0].numel() * k.element_size()
+    print(json.dumps({"calibration": "pa_copy_blocks", "launches": 3,
+                      "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}))
 
 
 def source_sha(path):
@@ -106,6 +129,9 @@ def cpu_baseline(lens, H, D, bs, seconds):
 
 def main():
     args = parse_args()
+    if args.calibrate:
+        calibrate()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

@@ -11,7 +11,7 @@
 // stored, and long sequences are split into partitions whose partial
 // results a second kernel combines.
 //
-// Phase 1 -- one workgroup of 4 waves per (partition, KV head, sequence):
+// Phase 1 -- one workgroup of 4 waves per (KV head, sequence, partition):
 //   * the partition's block-table slice is staged in LDS once (and every
 //     entry range-checked);
 //   * wave w takes the partition's blocks w, w+4, w+8, ...;
@@ -49,6 +49,15 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 16;         // tokens per KV block
 constexpr int kTableChunk = 256;   // table entries staged in LDS at a time
 constexpr float kLog2e = 1.4426950408889634f;
+// Buffer-descriptor word 3 for raw (untyped) dword access on CDNA:
+// DATA_FORMAT = 32-bit, everything else 0.
+constexpr int kRsrcWord3 = 0x00020000;
+#ifndef PKV_LOAD_AUX
+#define PKV_LOAD_AUX 2             // K/V loads are nontemporal (read once: nt)
+#endif
+#ifndef PKV_NBUF
+#define PKV_NBUF 3                 // K/V blocks in flight per wave (1, 2 groups)
+#endif
 
 struct DecodeArgs {
   float* out;            // [B][Hq][D]
@@ -78,7 +87,68 @@ __device__ __forceinline__ int num_parts_of(int n, int part_blocks) {
   return nb == 0 ? 1 : (nb + part_blocks - 1) / part_blocks;
 }
 
+// Running softmax state of one lane: every lane of a row group (the LPR
+// lanes that share token rows) holds the same m and l and its own chunk of o.
+// Row groups are independent until the end of the wave's work, so no lane
+// exchange happens per block.  m starts at a large finite negative value so
+// that a row group that has seen only masked rows stays NaN-free
+// (alpha = 2^0 = 1, p = 2^-inf = 0).
+constexpr float kMinusBig = -1.0e30f;
+
 template <int DT, int D, int G>
+struct RowState {
+  static constexpr int EPL = 16 / ElemTraits<DT>::bytes;
+  float m[G], l[G], o[G][EPL];
+};
+
+// One block: scores for the lane's LPB rows, online-softmax update, PV.
+// MASKED: rows at or past valid_rows get score -inf and a zero V chunk
+// (a select, so poisoned slots never reach the arithmetic).
+template <int DT, int D, int G, int LPB, int RPI, bool MASKED>
+__device__ __forceinline__ void consume_block(RowState<DT, D, G>& st, const uint4 (&q)[G],
+                                              const uint4 (&kw)[LPB], const uint4 (&vw)[LPB],
+                                              float scale_log2, int r, int valid_rows) {
+  constexpr int LPR = 64 / RPI;
+  float s[G][LPB];
+#pragma unroll
+  for (int i = 0; i < LPB; ++i) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float acc = group_sum<1, LPR>(chunk_dot<DT>(q[hh], kw[i])) * scale_log2;
+      if constexpr (MASKED) acc = (i * RPI + r < valid_rows) ? acc : -INFINITY;
+      s[hh][i] = acc;
+    }
+  }
+  uint4 v[LPB];
+#pragma unroll
+  for (int i = 0; i < LPB; ++i) {
+    v[i] = vw[i];
+    if constexpr (MASKED) {
+      if (i * RPI + r >= valid_rows) v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    float bm = s[hh][0];
+#pragma unroll
+    for (int i = 1; i < LPB; ++i) bm = fmaxf(bm, s[hh][i]);
+    const float mn = fmaxf(st.m[hh], bm);
+    const float alpha = fast_exp2(st.m[hh] - mn);
+    st.m[hh] = mn;
+    float ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < RowState<DT, D, G>::EPL; ++e) st.o[hh][e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      const float p = fast_exp2(s[hh][i] - mn);
+      ps += p;
+      chunk_axpy<DT>(st.o[hh], p, v[i]);
+    }
+    st.l[hh] = fmaf(st.l[hh], alpha, ps);
+  }
+}
+
+template <int DT, int D, int G, int NBUF>
 __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   constexpr int ELEM = ElemTraits<DT>::bytes;
   constexpr int EPL = 16 / ELEM;          // elements per lane per load
@@ -92,7 +162,12 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   __shared__ float s_m[kWaves][G], s_l[kWaves][G];
   __shared__ float s_o[kWaves][G][D];
 
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Grid: x = KV head, y = sequence, z = partition.  Workgroups are dealt to
+  // the 8 XCDs round-robin by linear id, so the fastest index must not
+  // correlate with work size: heads of one (sequence, partition) cost the
+  // same, and partitions that a sequence does not have (the cheap exits)
+  // collect at the end of the grid.
+  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
   const int n = a.lens[b];
@@ -110,95 +185,56 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     return;
   }
 
-  // Query chunk of every head of the group, as float.
-  float qf[G][EPL];
+  // Query chunk of every head of the group, raw (same element type as K).
+  uint4 q[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const uint4 w4 = *reinterpret_cast<const uint4*>(
+  for (int hh = 0; hh < G; ++hh)
+    q[hh] = *reinterpret_cast<const uint4*>(
         a.q + ((static_cast<size_t>(b) * a.hq + h0 + hh) * D + c * EPL) * ELEM);
-    unpack16<DT>(w4, qf[hh]);
-  }
 
-  float m[G], l[G], o[G][EPL];
+  RowState<DT, D, G> st;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
+    st.m[hh] = kMinusBig;
+    st.l[hh] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[hh][e] = 0.f;
+    for (int e = 0; e < EPL; ++e) st.o[hh][e] = 0.f;
   }
 
-  // Byte offset of this lane's chunk in load i of a block.
-  const size_t row_bytes = static_cast<size_t>(a.hkv) * D * ELEM;
-  const size_t block_bytes = row_bytes * kBlock;
-  uint32_t lane_off[LPB];
-#pragma unroll
-  for (int i = 0; i < LPB; ++i)
-    lane_off[i] = static_cast<uint32_t>((i * RPI + r) * row_bytes + (static_cast<size_t>(g) * D + c * EPL) * ELEM);
+  // K/V rows are read with buffer loads: a scalar descriptor per block
+  // (base = block start, range = one block, so the hardware bounds-checks
+  // every access), one VGPR lane offset, and the row stride of load i in the
+  // scalar offset.
+  const uint32_t row_bytes = static_cast<uint32_t>(a.hkv) * D * ELEM;
+  const uint32_t block_bytes = row_bytes * kBlock;
+  const uint32_t lane_off = r * row_bytes + static_cast<uint32_t>(g * D + c * EPL) * ELEM;
 
   const int first = part * a.part_blocks;
   const int last = min(nblk, first + a.part_blocks);   // exclusive
   const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
   if (tid == 0) s_bad = 0;
 
-  // Consume one block: scores, online-softmax update, PV accumulation.
-  auto consume = [&](const uint4 (&kw)[LPB], const uint4 (&vw)[LPB], int valid_rows) {
-    float s[G][LPB];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      float kf[EPL];
-      unpack16<DT>(kw[i], kf);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[hh][e], kf[e], acc);
-        acc = group_sum<1, LPR>(acc);
-        s[hh][i] = (i * RPI + r < valid_rows) ? acc * a.scale_log2 : -INFINITY;
-      }
-    }
-    float vf[LPB][EPL];
-#pragma unroll
-    for (int i = 0; i < LPB; ++i) {
-      unpack16<DT>(vw[i], vf[i]);
-      if (i * RPI + r >= valid_rows) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[i][e] = 0.f;   // select, never 0*NaN
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      float bm = s[hh][0];
-#pragma unroll
-      for (int i = 1; i < LPB; ++i) bm = fmaxf(bm, s[hh][i]);
-      bm = group_max<LPR, 64>(bm);
-      const float mn = fmaxf(m[hh], bm);
-      const float alpha = fast_exp2(m[hh] - mn);
-      m[hh] = mn;
-      float ps = 0.f;
-      float acc[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = o[hh][e] * alpha;
-#pragma unroll
-      for (int i = 0; i < LPB; ++i) {
-        const float p = fast_exp2(s[hh][i] - mn);
-        ps += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[i][e], acc[e]);
-      }
-      l[hh] = l[hh] * alpha + ps;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[hh][e] = acc[e];
-    }
-  };
-
   auto load_block = [&](int blk, uint4 (&kw)[LPB], uint4 (&vw)[LPB]) {
-    const char* kb = a.k + static_cast<size_t>(blk) * block_bytes;
-    const char* vb = a.v + static_cast<size_t>(blk) * block_bytes;
+    const size_t boff = static_cast<size_t>(blk) * block_bytes;
+    const auto kd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.k + boff), 0,
+                                                      static_cast<int>(block_bytes), kRsrcWord3);
+    const auto vd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.v + boff), 0,
+                                                      static_cast<int>(block_bytes), kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) kw[i] = *reinterpret_cast<const uint4*>(kb + lane_off[i]);
+    for (int i = 0; i < LPB; ++i)
+      kw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            kd, lane_off, i * RPI * row_bytes, PKV_LOAD_AUX));
 #pragma unroll
-    for (int i = 0; i < LPB; ++i) vw[i] = *reinterpret_cast<const uint4*>(vb + lane_off[i]);
+    for (int i = 0; i < LPB; ++i)
+      vw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            vd, lane_off, i * RPI * row_bytes, PKV_LOAD_AUX));
+  };
+  auto consume = [&](const uint4 (&kw)[LPB], const uint4 (&vw)[LPB], int gblk) {
+    const int vr = n - gblk * kBlock;
+    if (vr >= kBlock)
+      consume_block<DT, D, G, LPB, RPI, false>(st, q, kw, vw, a.scale_log2, r, kBlock);
+    else
+      consume_block<DT, D, G, LPB, RPI, true>(st, q, kw, vw, a.scale_log2, r, vr);
   };
 
   for (int base = first; base < last; base += kTableChunk) {
@@ -212,39 +248,49 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     }
     __syncthreads();
     if (s_bad) break;
-    // This wave's blocks in the chunk: w, w+4, ...; one block of lookahead.
-    uint4 ka[LPB], va[LPB], kb[LPB], vb[LPB];
-    int j = w;
-    if (j < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[j]), ka, va);
-    for (; j < cnt; j += 2 * kWaves) {
-      const int j1 = j + kWaves, j2 = j + 2 * kWaves;
-      if (j1 < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[j1]), kb, vb);
-      consume(ka, va, min(kBlock, n - (base + j) * kBlock));
-      if (j1 < cnt) {
-        if (j2 < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[j2]), ka, va);
-        consume(kb, vb, min(kBlock, n - (base + j1) * kBlock));
+    // This wave's blocks in the chunk are w, w+4, ...; NBUF of them are in
+    // flight in a register ring (the loop is unrolled by NBUF so each ring
+    // slot is a fixed set of registers).
+    uint4 kr[NBUF][LPB], vr[NBUF][LPB];
+#pragma unroll
+    for (int sl = 0; sl < NBUF; ++sl) {
+      const int jj = w + sl * kWaves;
+      if (jj < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[jj]), kr[sl], vr[sl]);
+    }
+    for (int j = w; j < cnt; j += NBUF * kWaves) {
+#pragma unroll
+      for (int sl = 0; sl < NBUF; ++sl) {
+        const int jj = j + sl * kWaves;
+        if (jj < cnt) {
+          consume(kr[sl], vr[sl], base + jj);
+          const int jn = jj + NBUF * kWaves;
+          if (jn < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[jn]), kr[sl], vr[sl]);
+        }
       }
     }
   }
 
-  // Wave result: combine the RPI row groups of each lane's chunk.
+  // Wave result: merge the RPI row groups (each with its own running max).
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    l[hh] = group_sum<LPR, 64>(l[hh]);
+    const float M = group_max<LPR, 64>(st.m[hh]);
+    const float f = fast_exp2(st.m[hh] - M);
+    st.l[hh] = group_sum<LPR, 64>(st.l[hh] * f);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[hh][e] = group_sum<LPR, 64>(o[hh][e]);
+    for (int e = 0; e < EPL; ++e) st.o[hh][e] = group_sum<LPR, 64>(st.o[hh][e] * f);
+    st.m[hh] = M;
   }
   if (r == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_o[w][hh][c * EPL + e] = o[hh][e];
+      for (int e = 0; e < EPL; ++e) s_o[w][hh][c * EPL + e] = st.o[hh][e];
   }
   if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      s_m[w][hh] = m[hh];
-      s_l[w][hh] = l[hh];
+      s_m[w][hh] = st.m[hh];
+      s_l[w][hh] = st.l[hh];
     }
   }
   __syncthreads();
@@ -309,12 +355,12 @@ __global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
 
 template <int DT, int D>
 hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
-  dim3 grid(a.num_parts, a.hkv, B);
+  dim3 grid(a.hkv, B, a.num_parts);
   switch (group) {
-    case 1: decode_phase1<DT, D, 1><<<grid, kThreads, 0, st>>>(a); break;
-    case 2: decode_phase1<DT, D, 2><<<grid, kThreads, 0, st>>>(a); break;
-    case 4: decode_phase1<DT, D, 4><<<grid, kThreads, 0, st>>>(a); break;
-    case 8: decode_phase1<DT, D, 8><<<grid, kThreads, 0, st>>>(a); break;
+    case 1: decode_phase1<DT, D, 1, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
+    case 2: decode_phase1<DT, D, 2, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
+    case 4: decode_phase1<DT, D, 4, 2><<<grid, kThreads, 0, st>>>(a); break;
+    case 8: decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   if (a.num_parts > 1) decode_reduce<D><<<dim3(a.hq, B), 64, 0, st>>>(a);
@@ -397,14 +443,15 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_cache, const v
                              (dtype == PA_DTYPE_F32 ? 4 : 2);
   if (block_bytes >= (static_cast<size_t>(1) << 31))
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: one block of one layer must be under 2 GiB");
-  // Grid limits: partitions on x, KV heads on y (<= 65535), sequences on z.
-  if (num_kv_heads > 65535 || B > 65535)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: too many heads or sequences for one launch");
+  // Grid limits: KV heads on x, sequences on y (<= 65535), partitions on z.
+  if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 sequences");
 
   DecodeArgs a{};
   a.part_blocks = part_blocks_for(max_context_len, partition_tokens);
   const int32_t nb = (max_context_len + kBlock - 1) / kBlock;
   a.num_parts = nb == 0 ? 1 : (nb + a.part_blocks - 1) / a.part_blocks;
+  if (a.num_parts > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 partitions; use larger partitions");
   const WsLayout wl = ws_layout(B, num_q_heads, head_dim, a.num_parts);
   if (wl.total > 0) {
     if (!workspace || workspace_bytes < wl.total)

@@ -107,4 +107,53 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- 16-byte chunk arithmetic ------------------------------------------
+// A lane holds one 16-byte chunk of a K/V row (4 floats or 8 halves) and the
+// matching chunk of q in the same raw form.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// <q chunk, k chunk> in float32 (dot2 instructions for 16-bit types).
+template <int DT>
+__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k) {
+  if constexpr (DT == PA_DTYPE_F32) {
+    float acc = __uint_as_float(q.x) * __uint_as_float(k.x);
+    acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+    acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+    return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  } else if constexpr (DT == PA_DTYPE_F16) {
+    float acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.x), __builtin_bit_cast(half2_t, k.x), 0.f, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.y), __builtin_bit_cast(half2_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.z), __builtin_bit_cast(half2_t, k.z), acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q.w), __builtin_bit_cast(half2_t, k.w), acc, false);
+  } else {
+    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.x), __builtin_bit_cast(bf162_t, k.x), 0.f, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.y), __builtin_bit_cast(bf162_t, k.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.z), __builtin_bit_cast(bf162_t, k.z), acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q.w), __builtin_bit_cast(bf162_t, k.w), acc, false);
+  }
+}
+
+// o[e] += p * v[e] over the chunk, float32 accumulation.
+template <int DT>
+__device__ __forceinline__ void chunk_axpy(float* o, float p, const uint4& v) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (DT == PA_DTYPE_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = fmaf(p, __uint_as_float(d[i]), o[i]);
+  } else if constexpr (DT == PA_DTYPE_F16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = fmaf(p, half_lo(d[i]), o[2 * i]);
+      o[2 * i + 1] = fmaf(p, half_hi(d[i]), o[2 * i + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = fmaf(p, __uint_as_float(d[i] << 16), o[2 * i]);
+      o[2 * i + 1] = fmaf(p, __uint_as_float(d[i] & 0xffff0000u), o[2 * i + 1]);
+    }
+  }
+}
+
 }  // namespace pkv
