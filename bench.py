@@ -42,7 +42,11 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--partition-tokens", type=int, default=512)
+    p.add_argument("--workload", default="mixed_7b",
+                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow"],
+                   help="mixed_7b is the headline workload; the others are reported lines")
+    p.add_argument("--partition-tokens", type=int, default=-1,
+                   help="split-KV partition size (default: the workload's, 512)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
     p.add_argument("--calibrate", action="store_true",
@@ -89,16 +93,24 @@ def load_traffic():
     return pmc.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(lens, H, D, bs, seconds):
+TORCH_DTYPE_NAMES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
+
+
+def cpu_baseline(lens, hq, hkv, D, bs, dtype, seconds, layers, workload):
     """The oracle timed on the host over one layer of the same workload
-    shape (all sequences, all heads), with fresh seeded inputs, repeated
-    until about ``seconds`` of CPU time; BLAS limited to one thread."""
+    shape (a prefix of the sequences, all heads), with fresh seeded inputs,
+    repeated until about ``seconds``; BLAS limited to one thread."""
     import torch
     from threadpoolctl import threadpool_limits
 
     import oracle
     import workloads
 
+    tdt = getattr(torch, TORCH_DTYPE_NAMES[dtype])
+    # Bounded sample: the first sequences of the batch, up to ~150k tokens.
+    cum = np.cumsum(lens)
+    nseq = int(max(1, np.searchsorted(cum, 150_000, side="right")))
+    lens = np.asarray(lens[:nseq])
     need = [-(-int(n) // bs) for n in lens]
     nblk = sum(need)
     order = workloads.block_order(nblk, seed=11)
@@ -107,10 +119,11 @@ def cpu_baseline(lens, H, D, bs, seconds):
     for i, k in enumerate(need):
         tables[i, :k] = order[o:o + k]
         o += k
-    k = workloads.normal_torch((nblk, bs, H, D), 12, torch.float16, "cuda").cpu().numpy()
-    v = workloads.normal_torch((nblk, bs, H, D), 13, torch.float16, "cuda").cpu().numpy()
-    q = workloads.normal_torch((len(lens), H, D), 14, torch.float16, "cuda").cpu().numpy()
-    layer_bytes = int(np.sum(lens)) * 2 * H * D * 2
+    k = workloads.normal_torch((nblk, bs, hkv, D), 12, tdt, "cuda").float().cpu().numpy()
+    v = workloads.normal_torch((nblk, bs, hkv, D), 13, tdt, "cuda").float().cpu().numpy()
+    q = workloads.normal_torch((len(lens), hq, D), 14, tdt, "cuda").float().cpu().numpy()
+    elem = workloads.ELEM_BYTES[dtype]
+    sample_bytes = int(np.sum(lens)) * 2 * hkv * D * elem
     reps, t0 = 0, time.perf_counter()
     with threadpool_limits(limits=1):
         while True:
@@ -119,12 +132,317 @@ def cpu_baseline(lens, H, D, bs, seconds):
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-    return {"value": round(layer_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+    return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"one layer of the mixed_7b step ({len(lens)} sequences x {H} heads, "
-                      f"{int(np.sum(lens))} tokens, fresh seeded fp16 inputs), "
+            "sample": f"one layer of the {workload} step restricted to its first {nseq} sequences "
+                      f"({int(np.sum(lens))} tokens x {hq} query heads, fresh seeded {dtype} inputs), "
                       f"{reps} repetitions in {el:.1f} s, float64 NumPy, BLAS 1 thread",
-            "seqs_per_s": round(len(lens) * reps / el / 32, 4)}
+            "seqs_per_s": round(nseq * reps / el / layers, 4)}
+
+
+class DecodeBench:
+    """Device state and step of a decode workload (see the module doc)."""
+
+    def __init__(self, name, args, torch, pkv, workloads):
+        self.name, self.args, self.torch, self.pkv = name, args, torch, pkv
+        cfg = workloads.CONFIGS[name]
+        self.cfg = cfg
+        dev = torch.device("cuda:0")
+        self.L, self.hq, self.H, self.D = cfg["layers"], cfg["hq"], cfg["hkv"], cfg["d"]
+        self.bs, self.NB, self.dtype = cfg["bs"], cfg["num_blocks"], cfg["dtype"]
+        self.tdt = getattr(torch, TORCH_DTYPE_NAMES[self.dtype])
+        self.elem = workloads.ELEM_BYTES[self.dtype]
+        self.lens0 = workloads.lengths(name)                # include the step's new token
+        B = self.B = len(self.lens0)
+        S = args.warmup + args.steps
+        self.max_len_final = int(self.lens0.max()) + S - 1
+        self.max_blocks = -(-self.max_len_final // self.bs)
+        self.partition = args.partition_tokens if args.partition_tokens >= 0 else cfg["partition_tokens"]
+
+        # Host block manager: free list scrambled by a seeded permutation,
+        # then each sequence admitted with its prompt (length - 1 tokens).
+        self.bm = pkv.BlockManager(self.NB, self.bs, enable_prefix_cache=False)
+        workloads.scramble_free_list(self.bm, workloads.block_order(self.NB, seed=1))
+        toks = workloads.token_ids(int(self.lens0.max()), seed=2)
+        for i in range(B):
+            self.bm.allocate(i, toks[:int(self.lens0[i]) - 1])
+        self.seqs = np.arange(B, dtype=np.int64)
+
+        # Device inputs, resident in HBM: every layer's KV pool, and each
+        # layer's query and new K/V rows.
+        L, H, D, bs, NB = self.L, self.H, self.D, self.bs, self.NB
+        self.pool = torch.empty((L, 2, NB, bs, H, D), dtype=self.tdt, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(3)
+        for layer in range(L):
+            self.pool[layer].normal_(generator=g)
+        self.q = workloads.normal_torch((L, B, self.hq, D), 4, self.tdt, dev)
+        self.k_new = workloads.normal_torch((L, B, H, D), 5, self.tdt, dev)
+        self.v_new = workloads.normal_torch((L, B, H, D), 6, self.tdt, dev)
+        self.out = torch.empty((L, B, self.hq, D), dtype=torch.float32, device=dev)
+        ws_bytes = pkv.pa_decode_workspace_bytes(B, self.hq, D, self.max_len_final, self.partition)
+        self.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        self.d_tab = torch.empty((B, self.max_blocks), dtype=torch.int32, device=dev)
+        self.d_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.d_slot = torch.empty(B, dtype=torch.int64, device=dev)
+        self.d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
+        # Two pinned host buffer sets: the host fills one while the other's
+        # upload may still be queued.
+        self.pin = [dict(tab=torch.empty((B, self.max_blocks), dtype=torch.int32).pin_memory(),
+                         len=torch.empty(B, dtype=torch.int32).pin_memory(),
+                         slot=torch.empty(B, dtype=torch.int64).pin_memory(),
+                         pairs=torch.empty((B, 2), dtype=torch.int32).pin_memory(),
+                         ev=torch.cuda.Event()) for _ in range(2)]
+        for p in self.pin:
+            p["ev"].record()
+        self.new_tok = np.full(B, 7, dtype=np.int32)
+        self.k_layers = [self.pool[layer, 0] for layer in range(L)]
+        self.v_layers = [self.pool[layer, 1] for layer in range(L)]
+        self.host_s = []
+        torch.cuda.synchronize()
+
+    def step(self, s, ev_pairs=None):
+        pkv, p = self.pkv, self.pin[s % 2]
+        p["ev"].synchronize()                 # its previous upload has run
+        h0 = time.perf_counter()
+        slots, pairs = self.bm.append_slots(self.seqs, self.new_tok)
+        p["slot"].numpy()[:] = slots
+        self.bm.export_batch(self.seqs, self.max_blocks, 0, tables_out=p["tab"].numpy(),
+                             lens_out=p["len"].numpy())
+        self.host_s.append(time.perf_counter() - h0)
+        self.d_tab.copy_(p["tab"], non_blocking=True)
+        self.d_len.copy_(p["len"], non_blocking=True)
+        self.d_slot.copy_(p["slot"], non_blocking=True)
+        if len(pairs):
+            p["pairs"].numpy()[:len(pairs)] = pairs
+            self.d_pairs[:len(pairs)].copy_(p["pairs"][:len(pairs)], non_blocking=True)
+        p["ev"].record()
+        if len(pairs):
+            pkv.pa_copy_blocks(self.k_layers, self.v_layers, self.d_pairs[:len(pairs)])
+        max_len = int(self.lens0.max()) + s
+        for layer in range(self.L):
+            pkv.pa_write_kv(self.k_layers[layer], self.v_layers[layer], self.k_new[layer],
+                            self.v_new[layer], self.d_slot)
+            if ev_pairs is not None:
+                ev_pairs[layer][0].record()
+            pkv.pa_decode(self.q[layer], self.k_layers[layer], self.v_layers[layer], self.d_tab,
+                          self.d_len, max_len, partition_tokens=self.partition,
+                          out=self.out[layer], workspace=self.ws)
+            if ev_pairs is not None:
+                ev_pairs[layer][1].record()
+
+    def run(self):
+        """Time the steps.  Working sets under 4 GiB per step could be served
+        partly from the 256 MB Infinity Cache across steps, so those steps
+        are separated by a 1 GiB scratch write and timed with HIP events
+        from the step's first to last GPU operation; larger ones are timed
+        by the wall clock over all steps."""
+        torch, args = self.torch, self.args
+        per_token_layer = 2 * self.H * self.D * self.elem
+        small = int(self.lens0.sum()) * per_token_layer * self.L < 4 * 2**30
+        scratch = torch.empty(2**30, dtype=torch.uint8, device="cuda") if small else None
+        for s in range(args.warmup):
+            self.step(s)
+        torch.cuda.synchronize()
+        T = torch.cuda.Event
+        events = [[(T(enable_timing=True), T(enable_timing=True)) for _ in range(self.L)]
+                  for _ in range(args.steps)]
+        step_ev = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
+        self.host_s.clear()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if small:
+                scratch.fill_(i & 0xff)
+            step_ev[i][0].record()
+            self.step(args.warmup + i, events[i])
+            step_ev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_gpu_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
+        gpu_s = step_gpu_ms.sum() * 1e-3
+        timed_s = gpu_s if small else wall
+        step_tokens = [int(self.lens0.sum()) + self.B * (args.warmup + i) for i in range(args.steps)]
+        kv_bytes = sum(step_tokens) * per_token_layer * self.L
+        value = kv_bytes / timed_s / 1e9
+        dec_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in events])
+        launch_bytes = np.array(step_tokens, dtype=np.float64) * per_token_layer
+        achieved = float(launch_bytes.mean() / (dec_ms.mean() * 1e-3) / 1e9)
+        cfg = self.cfg
+        return {
+            "metric": "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s",
+            "value": round(value, 2),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(timed_s / args.steps * 1e3, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": self.dtype,
+            "data": "synthetic",
+            "config": {"workload": self.name, "layers": self.L, "batch": self.B,
+                       "q_heads": self.hq, "kv_heads": self.H, "head_dim": self.D,
+                       "block_size": self.bs, "num_blocks": self.NB,
+                       "lengths": LENGTH_NOTES[self.name],
+                       "mean_context": round(float(np.mean(step_tokens)) / self.B, 1),
+                       "partition_tokens": self.partition,
+                       "timing": "GPU events per step, 1 GiB cache flush between steps"
+                                 if small else "wall clock over all steps"},
+            "seqs_per_s": round(self.B * args.steps / timed_s, 1),
+            "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+            "kv_bytes_per_step": int(kv_bytes // args.steps),
+            "host_bm_ms_per_step": round(1e3 * float(np.mean(self.host_s)), 4),
+            "gpu_step_ms_p10_p50_p90": [round(float(x), 4) for x in
+                                        np.percentile(step_gpu_ms, [10, 50, 90])],
+            "roofline": {"kernel": "pa_decode (split-KV phase 1 + reduce), one layer",
+                         "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic() if self.name == "mixed_7b" else None,
+                         "avg_launch_ms": round(float(dec_ms.mean()), 5),
+                         "algorithmic_bytes_per_launch": int(launch_bytes.mean())},
+        }
+
+
+def run_fork_cow(args, torch, pkv, workloads):
+    """Parallel sampling with copy-on-write: 64 prompts of 2048 tokens
+    (prefix cache on), each parent appends one sampled token and forks 7
+    children; every round all 512 sequences append one token.  The first
+    round after the fork copies 7 shared, partly filled blocks per prompt
+    (448 pa_copy_blocks pairs); rounds 2..255 are run untimed; the timed
+    steps are then rounds of append + write + decode over 512 sequences of
+    2305+ tokens.  Reported: logical KV GB/s (every sequence's tokens) and
+    GB/s over the unique blocks read, plus the COW round's copy kernel."""
+    cfg = workloads.CONFIGS["fork_cow"]
+    bs, NB, H, D = cfg["bs"], cfg["num_blocks"], cfg["hkv"], cfg["d"]
+    P, F, L0, X = cfg["prompts"], cfg["forks"], cfg["prompt_len"], cfg["extra"]
+    dev = torch.device("cuda:0")
+    bm = pkv.BlockManager(NB, bs, True)
+    k = workloads.normal_torch((NB, bs, H, D), 40, torch.float16, dev)
+    v = workloads.normal_torch((NB, bs, H, D), 41, torch.float16, dev)
+    for p in range(P):
+        bm.allocate(p * F, workloads.token_ids(L0, seed=1000 + p))
+    parents = np.arange(P, dtype=np.int64) * F
+    seqs = np.array([p + c for p in parents for c in range(F)], dtype=np.int64)
+    B = len(seqs)
+    S = X + args.warmup + args.steps
+    max_blocks = -(-(L0 + 1 + S) // bs)
+    kn = workloads.normal_torch((B, H, D), 42, torch.float16, dev)
+    vn = workloads.normal_torch((B, H, D), 43, torch.float16, dev)
+    q = workloads.normal_torch((B, cfg["hq"], D), 44, torch.float16, dev)
+    out = torch.empty((B, cfg["hq"], D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(pkv.pa_decode_workspace_bytes(B, cfg["hq"], D, L0 + 1 + S, 512), 1),
+                     dtype=torch.uint8, device=dev)
+    tab_h = torch.empty((B, max_blocks), dtype=torch.int32).pin_memory()
+    len_h = torch.empty(B, dtype=torch.int32).pin_memory()
+    d_tab = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    d_len = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def append(ids, toks):
+        slots, pairs = bm.append_slots(ids, toks)
+        d_slot = torch.from_numpy(slots).to(dev, non_blocking=False)
+        d_pairs = torch.from_numpy(pairs).to(dev) if len(pairs) else None
+        return d_slot, d_pairs, len(pairs)
+
+    def decode(max_len, ev=None):
+        bm.export_batch(seqs, max_blocks, 0, tables_out=tab_h.numpy(), lens_out=len_h.numpy())
+        d_tab.copy_(tab_h)
+        d_len.copy_(len_h)
+        if ev is not None:
+            ev[0].record()
+        pkv.pa_decode(q, k, v, d_tab, d_len, max_len, partition_tokens=512, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    T = torch.cuda.Event
+    # Parent token, then the forks.
+    d_slot, _, _ = append(parents, np.full(P, 7, dtype=np.int32))
+    pkv.pa_write_kv(k, v, kn[:P], vn[:P], d_slot)
+    for p in parents:
+        for c in range(1, F):
+            bm.fork(int(p), int(p) + c)
+    torch.cuda.synchronize()
+    # Round 1: the copy-on-write round, timed.
+    toks = np.arange(B, dtype=np.int32)
+    cow_ev, round_ev = (T(enable_timing=True), T(enable_timing=True)), (T(enable_timing=True), T(enable_timing=True))
+    d_slot, d_pairs, npairs = append(seqs, toks)
+    round_ev[0].record()
+    cow_ev[0].record()
+    pkv.pa_copy_blocks([k], [v], d_pairs)
+    cow_ev[1].record()
+    pkv.pa_write_kv(k, v, kn, vn, d_slot)
+    decode(L0 + 2)
+    round_ev[1].record()
+    torch.cuda.synchronize()
+    cow_ms, round_ms = cow_ev[0].elapsed_time(cow_ev[1]), round_ev[0].elapsed_time(round_ev[1])
+    # Rounds 2..X untimed (the flow up to 2305 tokens per sequence).
+    for r in range(2, X + 1):
+        d_slot, _, n = append(seqs, toks)
+        assert n == 0
+        pkv.pa_write_kv(k, v, kn, vn, d_slot)
+    for w in range(args.warmup):
+        d_slot, _, _ = append(seqs, toks)
+        pkv.pa_write_kv(k, v, kn, vn, d_slot)
+        decode(L0 + 1 + X + w + 1)
+    torch.cuda.synchronize()
+    evs = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
+    dec = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
+    lens, uniq = [], []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        n = L0 + 1 + X + args.warmup + i + 1
+        d_slot, _, _ = append(seqs, toks)
+        evs[i][0].record()
+        pkv.pa_write_kv(k, v, kn, vn, d_slot)
+        decode(n, dec[i])
+        evs[i][1].record()
+        lens.append(n)
+        # unique blocks read: the shared prefix once per prompt plus every
+        # sequence's private blocks (this step's exact table contents)
+        uniq.append(len(np.unique(tab_h.numpy()[:, :-(-n // bs)])) * bs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_ms = np.array([a.elapsed_time(b) for a, b in dec])
+    per_tok = 2 * H * D * 2
+    logical = np.array(lens, dtype=np.float64) * B * per_tok
+    unique = np.array(uniq, dtype=np.float64) * per_tok
+    value = float(logical.sum() / (step_ms.sum() * 1e-3) / 1e9)
+    achieved_u = float(unique.mean() / (dec_ms.mean() * 1e-3) / 1e9)
+    cow_bytes = npairs * 2 * 2 * k[0].numel() * 2          # K and V, read + write
+    return {
+        "metric": "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(step_ms.mean()), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "fork_cow", "prompts": P, "forks": F, "prompt_len": L0,
+                   "appended": X, "q_heads": cfg["hq"], "kv_heads": H, "head_dim": D,
+                   "block_size": bs, "num_blocks": NB, "partition_tokens": 512,
+                   "timing": "GPU events per step (write + decode); value counts logical "
+                             "KV bytes (shared prefix blocks once per sequence)"},
+        "seqs_per_s": round(B * args.steps / (step_ms.sum() * 1e-3), 1),
+        "gpu_step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(step_ms, [10, 50, 90])],
+        "unique_kv_gbs": round(float(unique.sum() / (step_ms.sum() * 1e-3) / 1e9), 2),
+        "used_blocks": int(NB - bm.num_free_blocks),
+        "cow_round": {"pairs": npairs, "copy_ms": round(cow_ms, 4),
+                      "copy_gbs": round(cow_bytes / (cow_ms * 1e-3) / 1e9, 2),
+                      "round_ms": round(round_ms, 4)},
+        "roofline": {"kernel": "pa_decode (split-KV phase 1 + reduce), unique bytes",
+                     "bound": "hbm", "achieved": round(achieved_u, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved_u / PEAK_HBM_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(float(dec_ms.mean()), 5),
+                     "algorithmic_bytes_per_launch": int(unique.mean())},
+        "cpu_baseline": None,
+        "wall_s": round(wall, 3),
+    }
+
+
+LENGTH_NOTES = {
+    "mixed_7b": "log-uniform [50, 4096], PCG64 seed 0, +1 token per step",
+    "13b_layer": "10 x 4096, +1 token per step",
+    "gqa_long": "32 x 32768, +1 token per step",
+}
 
 
 def main():
@@ -144,141 +462,17 @@ def main():
     import paged_kv_cache_136_amd as pkv
     import workloads
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg = workloads.CONFIGS["mixed_7b"]
-    L, H, D, bs, NB = cfg["layers"], cfg["hkv"], cfg["d"], cfg["bs"], cfg["num_blocks"]
-    lens0 = workloads.lengths("mixed_7b")                 # includes the step's new token
-    B = len(lens0)
-    S = args.warmup + args.steps
-    max_len_final = int(lens0.max()) + S - 1
-    max_blocks = -(-max_len_final // bs)
-
-    # Host block manager: free list scrambled by a seeded permutation, then
-    # each sequence admitted with its prompt (length - 1 tokens).
-    bm = pkv.BlockManager(NB, bs, enable_prefix_cache=False)
-    workloads.scramble_free_list(bm, workloads.block_order(NB, seed=1))
-    toks = workloads.token_ids(int(lens0.max()), seed=2)
-    for i in range(B):
-        bm.allocate(i, toks[:int(lens0[i]) - 1])
-    seqs = np.arange(B, dtype=np.int64)
-
-    # Device inputs, resident in HBM: the KV pool of every layer, and each
-    # layer's query and new K/V rows.
-    pool = torch.empty((L, 2, NB, bs, H, D), dtype=torch.float16, device=dev)
-    g = torch.Generator(device=dev)
-    g.manual_seed(3)
-    for layer in range(L):
-        pool[layer].normal_(generator=g)
-    q = workloads.normal_torch((L, B, cfg["hq"], D), 4, torch.float16, dev)
-    k_new = workloads.normal_torch((L, B, H, D), 5, torch.float16, dev)
-    v_new = workloads.normal_torch((L, B, H, D), 6, torch.float16, dev)
-    out = torch.empty((L, B, cfg["hq"], D), dtype=torch.float32, device=dev)
-    ws_bytes = pkv.pa_decode_workspace_bytes(B, cfg["hq"], D, max_len_final, args.partition_tokens)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    d_tab = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
-    d_len = torch.empty(B, dtype=torch.int32, device=dev)
-    d_slot = torch.empty(B, dtype=torch.int64, device=dev)
-    d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
-    # Two pinned host buffer sets: the host fills one while the other's
-    # upload may still be queued.
-    pin = [dict(tab=torch.empty((B, max_blocks), dtype=torch.int32).pin_memory(),
-                len=torch.empty(B, dtype=torch.int32).pin_memory(),
-                slot=torch.empty(B, dtype=torch.int64).pin_memory(),
-                pairs=torch.empty((B, 2), dtype=torch.int32).pin_memory(),
-                ev=torch.cuda.Event()) for _ in range(2)]
-    for p in pin:
-        p["ev"].record()
-    new_tok = np.full(B, 7, dtype=np.int32)
-    k_layers = [pool[layer, 0] for layer in range(L)]
-    v_layers = [pool[layer, 1] for layer in range(L)]
-    torch.cuda.synchronize()
-
-    host_s = []
-
-    def step(s, ev_pairs=None):
-        p = pin[s % 2]
-        p["ev"].synchronize()                 # its previous upload has run
-        h0 = time.perf_counter()
-        slots, pairs = bm.append_slots(seqs, new_tok)
-        p["slot"].numpy()[:] = slots
-        bm.export_batch(seqs, max_blocks, 0, tables_out=p["tab"].numpy(), lens_out=p["len"].numpy())
-        host_s.append(time.perf_counter() - h0)
-        d_tab.copy_(p["tab"], non_blocking=True)
-        d_len.copy_(p["len"], non_blocking=True)
-        d_slot.copy_(p["slot"], non_blocking=True)
-        if len(pairs):
-            p["pairs"].numpy()[:len(pairs)] = pairs
-            d_pairs[:len(pairs)].copy_(p["pairs"][:len(pairs)], non_blocking=True)
-        p["ev"].record()
-        if len(pairs):
-            pkv.pa_copy_blocks(k_layers, v_layers, d_pairs[:len(pairs)])
-        max_len = int(lens0.max()) + s
-        for layer in range(L):
-            pkv.pa_write_kv(k_layers[layer], v_layers[layer], k_new[layer], v_new[layer], d_slot)
-            if ev_pairs is not None:
-                ev_pairs[layer][0].record()
-            pkv.pa_decode(q[layer], k_layers[layer], v_layers[layer], d_tab, d_len, max_len,
-                          partition_tokens=args.partition_tokens, out=out[layer], workspace=ws)
-            if ev_pairs is not None:
-                ev_pairs[layer][1].record()
-
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(L)] for _ in range(args.steps)]
-    host_s.clear()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Algorithmic KV bytes: valid tokens' K and V rows, every layer.
-    per_token_layer = 2 * H * D * 2
-    step_tokens = [int(lens0.sum()) + B * (args.warmup + i) for i in range(args.steps)]
-    kv_bytes = sum(step_tokens) * per_token_layer * L
-    value = kv_bytes / wall / 1e9
-    dec_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in events])   # [steps, L]
-    launch_bytes = np.array(step_tokens, dtype=np.float64) * per_token_layer   # per launch
-    # Average algorithmic bytes per launch / average launch duration.
-    achieved = float(launch_bytes.mean() / (dec_ms.mean() * 1e-3) / 1e9)
-    traffic = load_traffic()
-
-    result = {
-        "metric": "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic",
-        "config": {"workload": "mixed_7b", "layers": L, "batch": B, "q_heads": cfg["hq"],
-                   "kv_heads": H, "head_dim": D, "block_size": bs, "num_blocks": NB,
-                   "lengths": "log-uniform [50, 4096], PCG64 seed 0, +1 token per step",
-                   "mean_context": round(float(np.mean(step_tokens)) / B, 1),
-                   "partition_tokens": args.partition_tokens},
-        "seqs_per_s": round(B * args.steps / wall, 1),
-        "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
-        "kv_bytes_per_step": int(kv_bytes // args.steps),
-        "host_bm_ms_per_step": round(1e3 * float(np.mean(host_s)), 4),
-        "roofline": {"kernel": "pa_decode (split-KV phase 1 + reduce), one layer",
-                     "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic,
-                     "avg_launch_ms": round(float(dec_ms.mean()), 5),
-                     "algorithmic_bytes_per_launch": int(launch_bytes.mean())},
-    }
-    if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(lens0, H, D, bs, args.cpu_seconds)
+    torch.cuda.set_device(0)
+    if args.workload == "fork_cow":
+        result = run_fork_cow(args, torch, pkv, workloads)
     else:
-        result["cpu_baseline"] = None
+        wb = DecodeBench(args.workload, args, torch, pkv, workloads)
+        result = wb.run()
+        if args.cpu_seconds > 0:
+            result["cpu_baseline"] = cpu_baseline(wb.lens0, wb.hq, wb.H, wb.D, wb.bs, wb.dtype,
+                                                  args.cpu_seconds, wb.L, args.workload)
+        else:
+            result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
 
 
