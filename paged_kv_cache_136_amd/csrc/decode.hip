@@ -58,6 +58,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 #ifndef PKV_NBUF
 #define PKV_NBUF 3                 // K/V blocks in flight per wave (1, 2 groups)
 #endif
+#ifndef PKV_NBUF_G4
+#define PKV_NBUF_G4 1              // same, query group of 4 (VGPR-limited)
+#endif
 
 struct DecodeArgs {
   float* out;            // [B][Hq][D]
@@ -359,7 +362,7 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
   switch (group) {
     case 1: decode_phase1<DT, D, 1, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
     case 2: decode_phase1<DT, D, 2, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
-    case 4: decode_phase1<DT, D, 4, 2><<<grid, kThreads, 0, st>>>(a); break;
+    case 4: decode_phase1<DT, D, 4, PKV_NBUF_G4><<<grid, kThreads, 0, st>>>(a); break;
     case 8: decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }

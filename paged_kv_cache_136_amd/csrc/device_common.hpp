@@ -67,7 +67,9 @@ __device__ __forceinline__ void unpack16<PA_DTYPE_BF16>(const uint4& w, float* f
 //   OFF 32   : ds_bpermute, lane ^ 32
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  // Every source lane of these permutations is valid; with bound_ctrl set
+  // the old operand is dead and the move can fold into the consuming VALU op.
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
 template <int OFF>
