@@ -1,0 +1,176 @@
+// Stress driver for the host block manager through its C ABI only.
+// Seeded random operation streams (allocate / append_slot / append_slots /
+// fork / free / export / queries) with the P06 invariants checked after
+// every operation and the full dump compared across every failed operation
+// (all-or-nothing).  Built by tests/test_bm_sanitizers.py with g++ and the
+// address + undefined-behaviour sanitizers; exits non-zero on any failure.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+#include "pagedkv.h"
+
+#define REQUIRE(c)                                                               \
+  do {                                                                           \
+    if (!(c)) {                                                                  \
+      std::fprintf(stderr, "FAIL %s:%d %s (%s)\n", __FILE__, __LINE__, #c,       \
+                   pa_last_error());                                             \
+      std::exit(1);                                                              \
+    }                                                                            \
+  } while (0)
+
+struct Dump {
+  std::vector<int32_t> ref, fr, ev;
+  std::vector<int8_t> has;
+  int32_t nf = 0, ne = 0;
+  bool operator==(const Dump& o) const {
+    return ref == o.ref && has == o.has && nf == o.nf && ne == o.ne &&
+           std::vector<int32_t>(fr.begin(), fr.begin() + nf) ==
+               std::vector<int32_t>(o.fr.begin(), o.fr.begin() + o.nf) &&
+           std::vector<int32_t>(ev.begin(), ev.begin() + ne) ==
+               std::vector<int32_t>(o.ev.begin(), o.ev.begin() + o.ne);
+  }
+};
+
+static Dump dump(pa_bm* bm, int nb) {
+  Dump d;
+  d.ref.resize(nb);
+  d.has.resize(nb);
+  d.fr.resize(nb);
+  d.ev.resize(nb);
+  REQUIRE(pa_bm_dump(bm, d.ref.data(), d.has.data(), d.fr.data(), &d.nf, d.ev.data(), &d.ne) == PA_OK);
+  return d;
+}
+
+static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops) {
+  std::mt19937 rng(seed);
+  pa_bm* bm = pa_bm_create(nb, bs, prefix);
+  REQUIRE(bm);
+  std::vector<int64_t> live;
+  int64_t next = 1;
+  long oob = 0, cow = 0, hits = 0;
+  for (int it = 0; it < ops; ++it) {
+    const int r = rng() % 100;
+    if (r < 30 || live.empty()) {
+      int n = rng() % (4 * bs + 2);
+      std::vector<int32_t> toks(n);
+      for (auto& t : toks) t = rng() % alphabet;
+      std::vector<int32_t> table((n + bs - 1) / bs + 1);
+      int32_t nbk = -1;
+      Dump before = dump(bm, nb);
+      int st = pa_bm_allocate(bm, next, toks.data(), n, table.data(), (int32_t)table.size(), &nbk);
+      if (st == PA_ERR_OUT_OF_BLOCKS) {
+        ++oob;
+        REQUIRE(dump(bm, nb) == before);
+      } else {
+        REQUIRE(st == PA_OK && nbk == (n + bs - 1) / bs);
+        int32_t c = -1;
+        REQUIRE(pa_bm_num_cached_tokens(bm, next, &c) == PA_OK);
+        hits += c > 0;
+        live.push_back(next++);
+      }
+    } else if (r < 55) {
+      int64_t s = live[rng() % live.size()];
+      int64_t slot = -2;
+      int32_t src = -2, dst = -2, len0 = -1, len1 = -1;
+      REQUIRE(pa_bm_seq_len(bm, s, &len0) == PA_OK);
+      Dump before = dump(bm, nb);
+      int st = pa_bm_append_slot(bm, s, (int32_t)(rng() % alphabet), &slot, &src, &dst);
+      if (st == PA_ERR_OUT_OF_BLOCKS) {
+        ++oob;
+        REQUIRE(dump(bm, nb) == before);
+        REQUIRE(pa_bm_seq_len(bm, s, &len1) == PA_OK && len1 == len0);
+      } else {
+        REQUIRE(st == PA_OK);
+        int64_t again = -1;
+        REQUIRE(pa_bm_slot(bm, s, len0, &again) == PA_OK && again == slot);
+        cow += src >= 0;
+        REQUIRE((src >= 0) == (dst >= 0));
+      }
+    } else if (r < 65) {
+      // batched append over a few live sequences (distinct ids)
+      std::vector<int64_t> ids;
+      for (int k = 0; k < 3 && k < (int)live.size(); ++k) ids.push_back(live[(rng() % live.size())]);
+      std::sort(ids.begin(), ids.end());
+      ids.erase(std::unique(ids.begin(), ids.end()), ids.end());
+      std::vector<int32_t> toks(ids.size(), 1);
+      std::vector<int64_t> slots(ids.size());
+      std::vector<int32_t> pairs(2 * ids.size());
+      int32_t ncow = -1, ndone = -1;
+      int st = pa_bm_append_slots(bm, ids.data(), toks.data(), (int32_t)ids.size(), slots.data(),
+                                  pairs.data(), &ncow, &ndone);
+      REQUIRE(st == PA_OK || st == PA_ERR_OUT_OF_BLOCKS);
+      REQUIRE(ndone >= 0 && ndone <= (int32_t)ids.size() && ncow >= 0 && ncow <= ndone);
+      if (st != PA_OK) ++oob;
+    } else if (r < 75) {
+      int64_t p = live[rng() % live.size()];
+      REQUIRE(pa_bm_fork(bm, p, next) == PA_OK);
+      REQUIRE(pa_bm_fork(bm, p, next) == PA_ERR_INVALID);   // child exists
+      live.push_back(next++);
+    } else if (r < 90) {
+      size_t i = rng() % live.size();
+      REQUIRE(pa_bm_free(bm, live[i]) == PA_OK);
+      live.erase(live.begin() + i);
+    } else {
+      // export a random subset with a table width that may be too small
+      std::vector<int64_t> ids(live.begin(), live.begin() + std::min<size_t>(live.size(), 4));
+      int32_t width = rng() % 8;
+      std::vector<int32_t> tabs(ids.size() * width + 1), lens(ids.size() + 1);
+      int st = pa_bm_export_batch(bm, ids.data(), (int32_t)ids.size(), tabs.data(), width, -1,
+                                  lens.data());
+      REQUIRE(st == PA_OK || st == PA_ERR_INVALID);
+      if (st == PA_OK)
+        for (size_t k = 0; k < ids.size(); ++k) {
+          int32_t n = -1;
+          REQUIRE(pa_bm_seq_len(bm, ids[k], &n) == PA_OK && n == lens[k]);
+        }
+    }
+    REQUIRE(pa_bm_check_invariants(bm) == PA_OK);
+  }
+  for (int64_t s : live) REQUIRE(pa_bm_free(bm, s) == PA_OK);
+  REQUIRE(pa_bm_check_invariants(bm) == PA_OK);
+  REQUIRE(pa_bm_num_free_blocks(bm) == nb);
+  REQUIRE(pa_bm_num_seqs(bm) == 0);
+  REQUIRE(oob > 0);
+  if (prefix) REQUIRE(hits > 0);
+  pa_bm_destroy(bm);
+  std::printf("seed %u nb %d bs %d prefix %d: oob %ld cow %ld hits %ld\n", seed, nb, bs, prefix, oob, cow, hits);
+}
+
+static void bad_arguments() {
+  REQUIRE(pa_bm_create(0, 16, 1) == nullptr);
+  REQUIRE(pa_bm_create(4, 0, 1) == nullptr);
+  REQUIRE(pa_bm_allocate(nullptr, 1, nullptr, 0, nullptr, 0, nullptr) == PA_ERR_INVALID);
+  pa_bm* bm = pa_bm_create(4, 2, 1);
+  REQUIRE(bm);
+  int32_t tab[4];
+  REQUIRE(pa_bm_allocate(bm, 1, nullptr, 3, tab, 4, nullptr) == PA_ERR_INVALID);  // tokens NULL
+  int32_t toks[3] = {1, 2, 3};
+  REQUIRE(pa_bm_allocate(bm, 1, toks, -1, tab, 4, nullptr) == PA_ERR_INVALID);
+  REQUIRE(pa_bm_allocate(bm, 1, toks, 3, tab, 1, nullptr) == PA_ERR_INVALID);  // cap too small
+  REQUIRE(pa_bm_allocate(bm, 1, toks, 3, tab, 2, nullptr) == PA_OK);
+  REQUIRE(pa_bm_allocate(bm, 1, toks, 3, tab, 2, nullptr) == PA_ERR_INVALID);  // exists
+  REQUIRE(pa_bm_append_slot(bm, 99, 1, nullptr, nullptr, nullptr) == PA_ERR_INVALID);
+  REQUIRE(pa_bm_free(bm, 99) == PA_OK);
+  int64_t slot;
+  REQUIRE(pa_bm_slot(bm, 1, 3, &slot) == PA_ERR_INVALID);
+  REQUIRE(pa_bm_slot(bm, 1, -1, &slot) == PA_ERR_INVALID);
+  int32_t n;
+  REQUIRE(pa_bm_get_table(bm, 1, tab, 1, &n) == PA_ERR_INVALID);
+  REQUIRE(pa_bm_can_allocate(bm, -1) == 0);
+  REQUIRE(pa_bm_check_invariants(bm) == PA_OK);
+  pa_bm_destroy(bm);
+}
+
+int main() {
+  bad_arguments();
+  run(1, 8, 2, 1, 3, 20000);
+  run(2, 12, 4, 1, 2, 20000);
+  run(3, 24, 16, 1, 1, 5000);
+  run(4, 10, 3, 0, 3, 20000);
+  run(5, 6, 1, 1, 2, 20000);
+  std::printf("bm_stress ok\n");
+  return 0;
+}
