@@ -12,9 +12,8 @@
 // results a second kernel combines.
 //
 // Phase 1 -- one workgroup of 4 waves per (KV head, sequence, partition):
-//   * the partition's block-table slice is staged in LDS once (and every
-//     entry range-checked);
-//   * wave w takes the partition's blocks w, w+4, w+8, ...;
+//   * wave w takes the partition's blocks w, w+4, w+8, ..., reading their ids
+//     from the block table with scalar loads (range-checked);
 //   * a token row of one KV head (head_dim elements) is read by
 //     LPR = head_dim*elem/16 lanes with one 16-byte load each, so one load
 //     instruction covers 64/LPR rows and a 16-token block takes 16*LPR/64
@@ -47,7 +46,6 @@ namespace {
 constexpr int kWaves = 4;          // waves per phase-1 workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 16;         // tokens per KV block
-constexpr int kTableChunk = 256;   // table entries staged in LDS at a time
 constexpr float kLog2e = 1.4426950408889634f;
 // Buffer-descriptor word 3 for raw (untyped) dword access on CDNA:
 // DATA_FORMAT = 32-bit, everything else 0.
@@ -57,6 +55,12 @@ constexpr int kRsrcWord3 = 0x00020000;
 #endif
 #ifndef PKV_NBUF
 #define PKV_NBUF 3                 // K/V blocks in flight per wave (1, 2 groups)
+#endif
+#ifndef PKV_NBUF_MFMA
+#define PKV_NBUF_MFMA 1            // same, matrix-core path (groups of 4 and 8)
+#endif
+#ifndef PKV_MFMA_K_LDS
+#define PKV_MFMA_K_LDS 1           // K rows staged through LDS (row-layout loads) on the MFMA path
 #endif
 #ifndef PKV_NBUF_G4
 #define PKV_NBUF_G4 1              // same, query group of 4 (VGPR-limited)
@@ -97,6 +101,7 @@ __device__ __forceinline__ int num_parts_of(int n, int part_blocks) {
 // that a row group that has seen only masked rows stays NaN-free
 // (alpha = 2^0 = 1, p = 2^-inf = 0).
 constexpr float kMinusBig = -1.0e30f;
+constexpr float kRescaleLog2 = 8.0f;   // lazy-rescale threshold, log2 domain
 
 template <int DT, int D, int G>
 struct RowState {
@@ -160,8 +165,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   constexpr int LPB = kBlock / RPI;       // loads per block (K or V)
   static_assert(LPR >= 1 && LPR <= 64 && RPI * LPR == 64 && LPB * RPI == kBlock, "shape");
 
-  __shared__ int32_t s_tab[kTableChunk];
-  __shared__ int32_t s_bad;
+  __shared__ int32_t s_bad[kWaves];
   __shared__ float s_m[kWaves][G], s_l[kWaves][G];
   __shared__ float s_o[kWaves][G][D];
 
@@ -215,7 +219,19 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   const int first = part * a.part_blocks;
   const int last = min(nblk, first + a.part_blocks);   // exclusive
   const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
-  if (tid == 0) s_bad = 0;
+  // Block ids come straight from the table with scalar loads (uniform
+  // addresses, served by the scalar cache; tables are tiny and stay in L2),
+  // so a wave starts streaming without any LDS staging or barrier.  An id
+  // outside the pool is replaced by block 0 (never read out of range) and
+  // flags the sequence; its output becomes NaN after the merge.
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  bool bad_ids = false;
+  auto block_id = [&](int j) -> int {
+    const int32_t e = trow[j];
+    const bool ok = e >= 0 && e < a.num_blocks;
+    bad_ids |= !ok;
+    return ok ? e : 0;
+  };
 
   auto load_block = [&](int blk, uint4 (&kw)[LPB], uint4 (&vw)[LPB]) {
     const size_t boff = static_cast<size_t>(blk) * block_bytes;
@@ -240,35 +256,23 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       consume_block<DT, D, G, LPB, RPI, true>(st, q, kw, vw, a.scale_log2, r, vr);
   };
 
-  for (int base = first; base < last; base += kTableChunk) {
-    const int cnt = min(kTableChunk, last - base);
-    __syncthreads();                       // previous chunk fully consumed
-    for (int i = tid; i < cnt; i += kThreads) {
-      const int32_t e = trow[base + i];
-      const bool ok = e >= 0 && e < a.num_blocks;
-      s_tab[i] = ok ? e : 0;
-      if (!ok) s_bad = 1;
-    }
-    __syncthreads();
-    if (s_bad) break;
-    // This wave's blocks in the chunk are w, w+4, ...; NBUF of them are in
-    // flight in a register ring (the loop is unrolled by NBUF so each ring
-    // slot is a fixed set of registers).
-    uint4 kr[NBUF][LPB], vr[NBUF][LPB];
+  // This wave's blocks are first+wv, first+wv+4, ...; NBUF of them are in
+  // flight in a register ring (the loop is unrolled by NBUF so each ring
+  // slot is a fixed set of registers).
+  uint4 kr[NBUF][LPB], vr[NBUF][LPB];
+#pragma unroll
+  for (int sl = 0; sl < NBUF; ++sl) {
+    const int jj = first + wv + sl * kWaves;
+    if (jj < last) load_block(block_id(jj), kr[sl], vr[sl]);
+  }
+  for (int j = first + wv; j < last; j += NBUF * kWaves) {
 #pragma unroll
     for (int sl = 0; sl < NBUF; ++sl) {
-      const int jj = w + sl * kWaves;
-      if (jj < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[jj]), kr[sl], vr[sl]);
-    }
-    for (int j = w; j < cnt; j += NBUF * kWaves) {
-#pragma unroll
-      for (int sl = 0; sl < NBUF; ++sl) {
-        const int jj = j + sl * kWaves;
-        if (jj < cnt) {
-          consume(kr[sl], vr[sl], base + jj);
-          const int jn = jj + NBUF * kWaves;
-          if (jn < cnt) load_block(__builtin_amdgcn_readfirstlane(s_tab[jn]), kr[sl], vr[sl]);
-        }
+      const int jj = j + sl * kWaves;
+      if (jj < last) {
+        consume(kr[sl], vr[sl], jj);
+        const int jn = jj + NBUF * kWaves;
+        if (jn < last) load_block(block_id(jn), kr[sl], vr[sl]);
       }
     }
   }
@@ -295,10 +299,11 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       s_m[w][hh] = st.m[hh];
       s_l[w][hh] = st.l[hh];
     }
+    s_bad[w] = bad_ids;
   }
   __syncthreads();
 
-  const bool bad = s_bad != 0;
+  const bool bad = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
   for (int i = tid; i < G * D; i += kThreads) {
     const int hh = i / D, d = i % D;
     float M = s_m[0][hh];
@@ -320,6 +325,292 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       a.ws_o[bhp * D + d] = res;
       if (d == 0) {
         a.ws_m[bhp] = bad ? 0.f : M;
+        a.ws_l[bhp] = bad ? __builtin_nanf("") : L;
+      }
+    }
+  }
+}
+
+// ---- Phase 1 on the matrix cores: query groups of 4 or 8, 16-bit K/V ------
+// With G query heads per KV head the block's QK^T and PV are small
+// contractions (16 tokens x D x G), so they run as MFMAs and the vector ALU
+// keeps only the softmax.  Lane coordinates: t = lane % 16, qa = lane / 16.
+//  QK   S = K Q^T with v_mfma_f32_16x16x32: A = K (token t, dims 32j+8qa..),
+//       B = Q^T (head t, same dims; zero for t >= G).  C: lane (qa, t),
+//       reg r holds S[token 4qa+r][head t].
+//  softmax  per lane = per head t; the block max is reduced over the four
+//       qa lanes of a head (2 lane exchanges per block for all heads).
+//  PV   O^T = V^T P^T with v_mfma_f32_16x16x16: A = V^T for 16 dims (read
+//       from a wave-private LDS copy of the block with ds_read_tr16_b64),
+//       B = P^T, which is exactly the lane's four p values.  P is split into
+//       high and low 16-bit parts (two MFMAs) so the 16-bit rounding of P
+//       (2^-9 for bf16) does not reach the output (2^-18 after the split).
+//       C: lane (qa, t), reg r holds O[head t][dim 16n + 4qa + r], so the
+//       rescale by alpha is lane-local.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT> struct MfmaOps;
+template <> struct MfmaOps<PA_DTYPE_BF16> {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 x4 __attribute__((ext_vector_type(4)));
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) x4 lds_x4;
+  static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint2 read_tr(lds_x4* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
+  }
+  static __device__ __forceinline__ void split(const float (&p)[4], uint2& hi, uint2& lo) {
+    x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = static_cast<__bf16>(p[i]);
+      l[i] = static_cast<__bf16>(p[i] - static_cast<float>(h[i]));
+    }
+    hi = __builtin_bit_cast(uint2, h);
+    lo = __builtin_bit_cast(uint2, l);
+  }
+};
+template <> struct MfmaOps<PA_DTYPE_F16> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x4 __attribute__((ext_vector_type(4)));
+  typedef __fp16 tr4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+  typedef __attribute__((address_space(3))) tr4 lds_x4;
+  static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint2 read_tr(lds_x4* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(p));
+  }
+  static __device__ __forceinline__ void split(const float (&p)[4], uint2& hi, uint2& lo) {
+    x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = static_cast<_Float16>(p[i]);
+      l[i] = static_cast<_Float16>(p[i] - static_cast<float>(h[i]));
+    }
+    hi = __builtin_bit_cast(uint2, h);
+    lo = __builtin_bit_cast(uint2, l);
+  }
+};
+
+template <int DT, int D, int G, int NBUF>
+__global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
+  static_assert(DT != PA_DTYPE_F32 && (D == 64 || D == 128) && (G == 4 || G == 8), "shape");
+  using M = MfmaOps<DT>;
+  constexpr int ELEM = 2;
+  constexpr int KSTEPS = D / 32;          // QK MFMAs per block
+  constexpr int NT = D / 16;              // PV dim tiles per block
+  constexpr int LPR = D * ELEM / 16;      // lanes per row in the V row loads
+  constexpr int RPI = 64 / LPR;           // rows per V load instruction
+  constexpr int VLOADS = kBlock / RPI;    // V loads per block
+  constexpr int VROW = D * ELEM + 32;     // padded LDS row (bytes)
+
+  __shared__ int32_t s_bad[kWaves];
+  __shared__ __attribute__((aligned(16))) char s_v[kWaves][kBlock * VROW];
+  __shared__ __attribute__((aligned(16))) char s_k[PKV_MFMA_K_LDS ? kWaves : 1][kBlock * VROW];
+  __shared__ float s_m[kWaves][G], s_l[kWaves][G];
+  __shared__ float s_o[kWaves][G][D];
+
+  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = lane & 15, qa = lane >> 4;
+  const int n = a.lens[b];
+  const bool valid = len_valid(n, a);
+  const int nblk = valid ? (n + kBlock - 1) / kBlock : 0;
+  const int nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
+  if (part >= nparts) return;
+  const int h0 = g * G;
+
+  if (!valid || n == 0) {
+    const float fill = valid ? 0.f : __builtin_nanf("");
+    for (int i = tid; i < G * D; i += kThreads)
+      a.out[(static_cast<size_t>(b) * a.hq + h0 + i / D) * D + i % D] = fill;
+    return;
+  }
+
+  // Q^T as the QK B operand: head t, dims 32j + 8qa .. +8 (zero past G).
+  uint4 qb[KSTEPS];
+#pragma unroll
+  for (int j = 0; j < KSTEPS; ++j)
+    qb[j] = t < G ? *reinterpret_cast<const uint4*>(
+                        a.q + ((static_cast<size_t>(b) * a.hq + h0 + t) * D + 32 * j + 8 * qa) * ELEM)
+                  : make_uint4(0u, 0u, 0u, 0u);
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kMinusBig, lsum = 0.f;
+
+  const uint32_t row_bytes = static_cast<uint32_t>(a.hkv) * D * ELEM;
+  const uint32_t block_bytes = row_bytes * kBlock;
+  // K in MFMA A layout: token t, dims 32j + 8qa; V in row layout: token
+  // i*RPI + vr, dims 8vc .. +8.
+  const uint32_t k_off = t * row_bytes + static_cast<uint32_t>(g * D + 8 * qa) * ELEM;
+  const int vr = lane / LPR, vc = lane % LPR;
+  const uint32_t v_off = vr * row_bytes + static_cast<uint32_t>(g * D + 8 * vc) * ELEM;
+  char* lds_v = s_v[w];
+  typedef typename M::lds_x4 lds_x4;
+  // Transpose-read address: lane 16qa + 4e + q points at the 4 dims
+  // 16n + 4q .. +3 of token 4qa + e; the instruction then hands lane
+  // 16qa + j the four tokens 4qa .. 4qa+3 of dim 16n + j.
+  lds_x4* tr_base = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[w]) +
+                              (4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
+
+  const int first = part * a.part_blocks;
+  const int last = min(nblk, first + a.part_blocks);
+  const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
+  // Block ids come straight from the table with scalar loads (uniform
+  // addresses, served by the scalar cache; tables are tiny and stay in L2),
+  // so a wave starts streaming without any LDS staging or barrier.  An id
+  // outside the pool is replaced by block 0 (never read out of range) and
+  // flags the sequence; its output becomes NaN after the merge.
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  bool bad_ids = false;
+  auto block_id = [&](int j) -> int {
+    const int32_t e = trow[j];
+    const bool ok = e >= 0 && e < a.num_blocks;
+    bad_ids |= !ok;
+    return ok ? e : 0;
+  };
+
+  auto load_block = [&](int blk, uint4 (&kw)[KSTEPS], uint4 (&vw)[VLOADS]) {
+    const size_t boff = static_cast<size_t>(blk) * block_bytes;
+    const auto kd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.k + boff), 0,
+                                                      static_cast<int>(block_bytes), kRsrcWord3);
+    const auto vd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.v + boff), 0,
+                                                      static_cast<int>(block_bytes), kRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j)
+      kw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            kd, PKV_MFMA_K_LDS ? v_off : k_off + 64 * j,
+                                            PKV_MFMA_K_LDS ? j * RPI * row_bytes : 0, PKV_LOAD_AUX));
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i)
+      vw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            vd, v_off, i * RPI * row_bytes, PKV_LOAD_AUX));
+  };
+
+  auto consume = [&](const uint4 (&kw)[KSTEPS], const uint4 (&vw)[VLOADS], int gblk) {
+    const int valid_rows = min(kBlock, n - gblk * kBlock);
+    // V block -> wave-private LDS rows (rows past the length as zeros, so
+    // poisoned slots never meet a zero weight inside the MFMA).
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int row = i * RPI + vr;
+      const uint4 val = row < valid_rows ? vw[i] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(lds_v + row * VROW + 16 * vc) = val;
+    }
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (PKV_MFMA_K_LDS) {
+      // K rows through LDS too: row-layout loads, MFMA-layout reads.
+      static_assert(KSTEPS == VLOADS, "K row loads reuse the V row mapping");
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i)
+        *reinterpret_cast<uint4*>(s_k[w] + (i * RPI + vr) * VROW + 16 * vc) = kw[i];
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        const uint4 kk = *reinterpret_cast<const uint4*>(s_k[w] + t * VROW + (32 * j + 8 * qa) * ELEM);
+        sacc = M::qk(kk, qb[j], sacc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) sacc = M::qk(kw[j], qb[j], sacc);
+    }
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (4 * qa + r < valid_rows) ? sacc[r] * a.scale_log2 : -INFINITY;
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = group_max<16, 64>(bm);
+    // Lazy rescaling: the running max moves only when some head's block max
+    // exceeds it by more than 2^kRescaleLog2 (p then stays <= 2^8).  One
+    // wave-uniform test covers every head, and the common path leaves the
+    // accumulators to the MFMAs alone.
+    if (__any(bm > m + kRescaleLog2)) {
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - m);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    uint2 ph, pl;
+    M::split(p, ph, pl);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint2 vt = M::read_tr(tr_base + 4 * nt);   // 16 dims = 32 bytes = 4 x 8 B
+      acc[nt] = M::pv(vt, ph, acc[nt]);
+      acc[nt] = M::pv(vt, pl, acc[nt]);
+    }
+  };
+
+  uint4 kr[NBUF][KSTEPS], vrg[NBUF][VLOADS];
+#pragma unroll
+  for (int sl = 0; sl < NBUF; ++sl) {
+    const int jj = first + wv + sl * kWaves;
+    if (jj < last) load_block(block_id(jj), kr[sl], vrg[sl]);
+  }
+  for (int j = first + wv; j < last; j += NBUF * kWaves) {
+#pragma unroll
+    for (int sl = 0; sl < NBUF; ++sl) {
+      const int jj = j + sl * kWaves;
+      if (jj < last) {
+        consume(kr[sl], vrg[sl], jj);
+        const int jn = jj + NBUF * kWaves;
+        if (jn < last) load_block(block_id(jn), kr[sl], vrg[sl]);
+      }
+    }
+  }
+
+  // Wave result per head t: m is already uniform over the four qa lanes;
+  // the partial sums of the four token quarters add up.
+  lsum = group_sum<16, 64>(lsum);
+  if (t < G) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[w][t][16 * nt + 4 * qa + r] = acc[nt][r];
+    if (qa == 0) {
+      s_m[w][t] = m;
+      s_l[w][t] = lsum;
+    }
+  }
+  if (lane == 0) s_bad[w] = bad_ids;
+  __syncthreads();
+
+  const bool bad = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int hh = i / D, d = i % D;
+    float Mx = s_m[0][hh];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) Mx = fmaxf(Mx, s_m[ww][hh]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = fast_exp2(s_m[ww][hh] - Mx);
+      L = fmaf(s_l[ww][hh], f, L);
+      O = fmaf(s_o[ww][hh][d], f, O);
+    }
+    const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
+    const float res = bad ? __builtin_nanf("") : O / L;
+    if (nparts == 1) {
+      a.out[bh * D + d] = res;
+    } else {
+      const size_t bhp = bh * a.num_parts + part;
+      a.ws_o[bhp * D + d] = res;
+      if (d == 0) {
+        a.ws_m[bhp] = bad ? 0.f : Mx;
         a.ws_l[bhp] = bad ? __builtin_nanf("") : L;
       }
     }
@@ -362,8 +653,14 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
   switch (group) {
     case 1: decode_phase1<DT, D, 1, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
     case 2: decode_phase1<DT, D, 2, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
-    case 4: decode_phase1<DT, D, 4, PKV_NBUF_G4><<<grid, kThreads, 0, st>>>(a); break;
-    case 8: decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a); break;
+    case 4:
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, PKV_NBUF_MFMA><<<grid, kThreads, 0, st>>>(a);
+      else decode_phase1<DT, D, 4, PKV_NBUF_G4><<<grid, kThreads, 0, st>>>(a);
+      break;
+    case 8:
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, PKV_NBUF_MFMA><<<grid, kThreads, 0, st>>>(a);
+      else decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a);
+      break;
     default: return hipErrorInvalidValue;
   }
   if (a.num_parts > 1) decode_reduce<D><<<dim3(a.hq, B), 64, 0, st>>>(a);
