@@ -619,8 +619,14 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
 
 // Phase 2: out = sum_p w_p * o_p with w_p = l_p 2^(m_p - M) / sum_q l_q 2^(m_q - M).
 template <int D>
-__global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
+  // One workgroup per (query head, sequence).  The four waves take every
+  // fourth partition (so four partial rows are in flight at once), each lane
+  // owning D/64 adjacent dims, and the four partial sums meet in LDS.
+  constexpr int PER = D / 64;
+  static_assert(PER == 1 || PER == 2, "head_dim 64 or 128");
+  __shared__ float s_acc[kWaves][D];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = a.lens[b];
   if (!len_valid(n, a)) return;
   const int nparts = num_parts_of(n, a.part_blocks);
@@ -635,16 +641,24 @@ __global__ __launch_bounds__(64) void decode_reduce(DecodeArgs a) {
   for (int p = lane; p < nparts; p += 64) L += pl[p] * fast_exp2(pm[p] - M);
   L = group_sum<1, 64>(L);
   const float inv = 1.f / L;
-  constexpr int PER = D / 64;
   float acc[PER] = {};
-  for (int p = 0; p < nparts; ++p) {
+  const float* po = a.ws_o + bh * a.num_parts * D + PER * lane;
+#pragma unroll 4
+  for (int p = __builtin_amdgcn_readfirstlane(w); p < nparts; p += kWaves) {
     const float wgt = pl[p] * fast_exp2(pm[p] - M) * inv;
-    const float* po = a.ws_o + (bh * a.num_parts + p) * D;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, po[lane + 64 * e], acc[e]);
+    if constexpr (PER == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(po + static_cast<size_t>(p) * D);
+      acc[0] = fmaf(wgt, v.x, acc[0]);
+      acc[1] = fmaf(wgt, v.y, acc[1]);
+    } else {
+      acc[0] = fmaf(wgt, po[static_cast<size_t>(p) * D], acc[0]);
+    }
   }
 #pragma unroll
-  for (int e = 0; e < PER; ++e) a.out[bh * D + lane + 64 * e] = acc[e];
+  for (int e = 0; e < PER; ++e) s_acc[w][PER * lane + e] = acc[e];
+  __syncthreads();
+  if (tid < D)
+    a.out[bh * D + tid] = (s_acc[0][tid] + s_acc[1][tid]) + (s_acc[2][tid] + s_acc[3][tid]);
 }
 
 template <int DT, int D>
@@ -663,7 +677,7 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
       break;
     default: return hipErrorInvalidValue;
   }
-  if (a.num_parts > 1) decode_reduce<D><<<dim3(a.hq, B), 64, 0, st>>>(a);
+  if (a.num_parts > 1) decode_reduce<D><<<dim3(a.hq, B), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
