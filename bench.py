@@ -43,7 +43,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixed_7b",
-                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow"],
+                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap"],
                    help="mixed_7b is the headline workload; the others are reported lines")
     p.add_argument("--partition-tokens", type=int, default=-1,
                    help="split-KV partition size (default: the workload's, 512)")
@@ -438,6 +438,76 @@ def run_fork_cow(args, torch, pkv, workloads):
     }
 
 
+def run_swap(args, torch, pkv, workloads):
+    """Preemption traffic at the Llama-7B shape (32 layers x 32 KV heads x
+    128 dims, fp16, block 16): the victim is one 4096-token sequence (256
+    blocks scattered through a 1024-block pool).  A step swaps it out
+    (every layer's K and V, 2 GiB, into one pinned host buffer) and back in
+    (into 256 other scattered blocks).  Beside it, the same 2 GiB as one
+    contiguous DMA copy each way: the host link's ceiling on this machine."""
+    L, H, D, bs, NB, n = 32, 32, 128, 16, 1024, 256
+    dev = torch.device("cuda:0")
+    ks = [workloads.normal_torch((NB, bs, H, D), 60 + 2 * i, torch.float16, dev) for i in range(L)]
+    vs = [workloads.normal_torch((NB, bs, H, D), 61 + 2 * i, torch.float16, dev) for i in range(L)]
+    order = workloads.block_order(NB, 3)
+    out_blocks = torch.from_numpy(np.ascontiguousarray(order[:n], dtype=np.int32)).to(dev)
+    in_blocks = torch.from_numpy(np.ascontiguousarray(order[n:2 * n], dtype=np.int32)).to(dev)
+    rec = pkv.swap_record_bytes(ks)
+    total = n * rec
+    host = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    flat = torch.empty(total, dtype=torch.uint8, device=dev)
+    T = torch.cuda.Event
+    for _ in range(max(args.warmup, 1)):
+        pkv.pa_swap_out(ks, vs, out_blocks, host)
+        pkv.pa_swap_in(ks, vs, in_blocks, host)
+    torch.cuda.synchronize()
+    ev = [[T(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        pkv.pa_swap_out(ks, vs, out_blocks, host)
+        e[1].record()
+        pkv.pa_swap_in(ks, vs, in_blocks, host)
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    in_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    dma = [[T(enable_timing=True) for _ in range(3)] for _ in range(3)]
+    for e in dma:
+        e[0].record()
+        host.copy_(flat, non_blocking=True)
+        e[1].record()
+        flat.copy_(host, non_blocking=True)
+        e[2].record()
+    torch.cuda.synchronize()
+    d2h = float(np.median([a.elapsed_time(b) for a, b, _ in dma]))
+    h2d = float(np.median([b.elapsed_time(c) for _, b, c in dma]))
+    gbs = lambda ms: total / (ms * 1e-3) / 1e9
+    out_gbs, in_gbs = gbs(float(out_ms.mean())), gbs(float(in_ms.mean()))
+    step_ms = out_ms + in_ms
+    link_peak = 64.0        # PCIe 5.0 x16, per direction (published)
+    return {
+        "metric": "preemption swap: host-link GB/s (blocks out to pinned host memory and back)",
+        "value": round(gbs(float(step_ms.mean()) / 2), 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(float(step_ms.mean()), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "swap", "layers": L, "kv_heads": H, "head_dim": D, "block_size": bs,
+                   "pool_blocks": NB, "victim_blocks": n, "bytes_each_way": total,
+                   "timing": "GPU events around each call"},
+        "swap_out_gbs": round(out_gbs, 2), "swap_in_gbs": round(in_gbs, 2),
+        "dma_contiguous_gbs": {"d2h": round(gbs(d2h), 2), "h2d": round(gbs(h2d), 2)},
+        "roofline": {"kernel": "pa_swap_out / pa_swap_in", "bound": "host-link",
+                     "achieved": round(min(out_gbs, in_gbs), 2), "peak": link_peak, "unit": "GB/s",
+                     "frac": round(min(out_gbs, in_gbs) / link_peak, 4), "traffic": None,
+                     "avg_launch_ms": round(float(max(out_ms.mean(), in_ms.mean())), 5),
+                     "algorithmic_bytes_per_launch": total},
+        "cpu_baseline": None,
+        "wall_s": round(wall, 3),
+    }
+
+
 LENGTH_NOTES = {
     "mixed_7b": "log-uniform [50, 4096], PCG64 seed 0, +1 token per step",
     "13b_layer": "10 x 4096, +1 token per step",
@@ -465,6 +535,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "fork_cow":
         result = run_fork_cow(args, torch, pkv, workloads)
+    elif args.workload == "swap":
+        result = run_swap(args, torch, pkv, workloads)
     else:
         wb = DecodeBench(args.workload, args, torch, pkv, workloads)
         result = wb.run()

@@ -8,6 +8,8 @@
  *     fork and copy-on-write append);
  *   - pa_write_kv: scatter new tokens' K/V into their slots;
  *   - pa_copy_blocks: the copy-on-write block copy;
+ *   - pa_swap_out / pa_swap_in: whole blocks of every layer to and from
+ *     pinned host memory when a sequence is preempted and resumed;
  *   - pa_decode: attention of one query token per sequence over K/V that
  *     live in fixed-size blocks scattered through HBM, found through the
  *     sequence's block table, with split-KV partitions and a final reduce.
@@ -15,7 +17,8 @@
  * Pages cited:
  *   [A130]  "qaqbuyan.com article 130" (vLLM PagedAttention walk-through):
  *           KV-cache and block-size formulas, BlockTable, paged_attention
- *           pseudocode, BlockAllocator, paged_attention_kernel listing.
+ *           pseudocode, BlockAllocator, continuous-batching scheduler
+ *           (_preempt_request), paged_attention_kernel listing.
  *   [D31]   "day31" (blog.ans20xx.com): toy block allocator, toy COW append
  *           (fork_sequence / ensure_private_last_block / append_with_cow).
  *   [P06]   "P06 · BlockManager: paged KV + prefix cache" (kuanzhou.online
@@ -144,6 +147,39 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
  * are dropped.  Never fails; an unknown seq is a no-op returning PA_OK. */
 int pa_bm_free(pa_bm* bm, int64_t seq);
 
+/* Preemption ([A130] continuous-batching scheduler, _preempt_request: the
+ * victim's KV goes to CPU memory and its blocks are freed).  Copies the
+ * table of `seq` (logical order) into table_out[0..cap), *nblocks_out = its
+ * length, then frees the blocks exactly as pa_bm_free does; the sequence
+ * keeps only its tokens and is "swapped out".  The caller copies those
+ * blocks' bytes to host memory (pa_swap_out) before any later write into
+ * them -- on the same stream, stream order guarantees that.
+ * PA_ERR_INVALID for an unknown seq or a too small table_out (nothing
+ * changed).  A swapped-out id cannot be allocated or forked onto;
+ * pa_bm_free drops it. */
+int pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* table_out, int32_t cap, int32_t* nblocks_out);
+
+/* Resume a swapped-out sequence: the [P06] allocate over its saved tokens
+ * (the pages show no swap-in; this is the reading used).  Full prefix
+ * blocks still registered come back as hits -- their KV never left the
+ * GPU -- so only logical blocks first_restore.. need their host copy
+ * (pa_swap_in into table[first_restore..]).  *first_restore_out = number of
+ * hit blocks = num_cached_tokens / block_size.  All or nothing:
+ * PA_ERR_OUT_OF_BLOCKS leaves every state unchanged and the sequence still
+ * swapped out.  PA_ERR_INVALID if seq is not swapped out or cap is too
+ * small. */
+int pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* table_out, int32_t cap, int32_t* nblocks_out,
+                  int32_t* first_restore_out);
+
+/* 1 if seq is swapped out, 0 if not, -1 if bm is NULL. */
+int32_t pa_bm_is_swapped(const pa_bm* bm, int64_t seq);
+
+/* Swapped-out sequences in ascending id order: seqs_out[0..*n_out) and
+ * their lengths lens_out[0..*n_out).  With both arrays NULL only *n_out is
+ * set.  PA_ERR_INVALID if cap is too small (nothing written). */
+int pa_bm_swapped(const pa_bm* bm, int64_t* seqs_out, int32_t* lens_out, int32_t cap,
+                  int32_t* n_out);
+
 /* Flat slot of token `pos` (0 <= pos < len) of `seq` ([P06] spec overview).
  * PA_ERR_INVALID for an unknown seq or pos out of range. */
 int pa_bm_slot(const pa_bm* bm, int64_t seq, int32_t pos, int64_t* slot_out);
@@ -212,6 +248,39 @@ int pa_write_kv(void* k_cache, void* v_cache, const void* k_new, const void* v_n
 int pa_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                    int64_t block_bytes, int32_t num_blocks, const int32_t* pairs,
                    int32_t num_pairs, void* stream);
+
+/* Preemption copy to host memory ([A130] continuous-batching scheduler,
+ * _preempt_request: each of the victim's blocks is copied to CPU memory).
+ * For list entry i < n with b = blocks[i], and layer l < num_layers, the
+ * record at byte offset ((i * num_layers + l) * 2 + c) * block_bytes of
+ * host_dst receives K_l[b] (c = 0) or V_l[b] (c = 1), block_bytes bytes.
+ *   k_caches/v_caches: HOST arrays of num_layers device pointers (the
+ *     per-layer caches, layout above).
+ *   blocks: device int32 [n]; an entry outside [0, num_blocks) is skipped
+ *     (its record is left untouched).
+ *   host_dst: pinned host memory from hipHostMalloc (torch pin_memory) of
+ *     host_bytes >= n * num_layers * 2 * block_bytes bytes; the GPU writes it
+ *     directly over the host link.
+ * Errors (nothing launched): PA_ERR_INVALID if host_dst is not host memory
+ * that HIP maps for the device (checked at both ends of the range), if
+ * host_bytes is too small, or for bad sizes / misalignment (block_bytes a
+ * positive multiple of 16; caches and host_dst 16-byte aligned).
+ * Asynchronous on `stream`: the host record is complete once the stream
+ * has passed this call (synchronize before reading it on the host). */
+int pa_swap_out(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                int64_t block_bytes, int32_t num_blocks, const int32_t* blocks, int32_t n,
+                void* host_dst, int64_t host_bytes, void* stream);
+
+/* The inverse copy: for list entry i < n with b = blocks[i] and every layer
+ * l, K_l[b] and V_l[b] receive the host_src records laid out as in
+ * pa_swap_out (entry i's records at ((i * num_layers + l) * 2 + c) *
+ * block_bytes).  To resume a sequence, pass table[first_restore..] from
+ * pa_bm_swap_in and the records of those logical blocks.  Same arguments,
+ * checks and errors as pa_swap_out; destinations must be distinct.  The
+ * host buffer must stay unchanged until the stream has passed this call. */
+int pa_swap_in(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+               int64_t block_bytes, int32_t num_blocks, const int32_t* blocks, int32_t n,
+               const void* host_src, int64_t host_bytes, void* stream);
 
 /* Workspace bytes pa_decode needs for these sizes (0 when one partition
  * covers max_context_len, i.e. partition_tokens == 0 or >= max_context_len). */

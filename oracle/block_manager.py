@@ -37,6 +37,16 @@ design notes):
   ``KeyError``/``ValueError``; free of an unknown sequence is a no-op (as the
   article-130 ``BlockAllocator.free`` ignores unknown ids).  allocate with no
   tokens is allowed and yields an empty table.
+* Preemption ("qaqbuyan.com article 130", continuous-batching scheduler,
+  ``_preempt_request``): the victim's blocks are copied to host memory and
+  freed.  ``swap_out`` returns the table whose blocks the caller copies and
+  frees it exactly as ``free`` does, keeping the token list.  The page does
+  not show the way back; ``swap_in`` is read as the P06 allocate over the
+  saved tokens, so full prefix blocks that are still registered come back as
+  hits (their KV never left the GPU) and only the blocks from the first
+  non-hit on are restored from host memory.  A swapped sequence holds no
+  blocks; its id cannot be allocated or forked onto, and ``free`` drops its
+  saved tokens.
 """
 
 from collections import OrderedDict, deque
@@ -67,6 +77,8 @@ class RefBlockManager:
         self.tokens = {}
         self.hashes = {}
         self.cached = {}
+        # Preempted sequences: id -> token list (no blocks held).
+        self.swapped = {}
         # Exact prefix keys: (parent key, block tokens) -> integer.
         self._intern = {}
 
@@ -124,7 +136,7 @@ class RefBlockManager:
     # ----- operations ----------------------------------------------------
     def allocate(self, seq, tokens):
         """P06 operations table, allocate row: steps 1-3 read, 4-7 write."""
-        if seq in self.tables:
+        if seq in self.tables or seq in self.swapped:
             raise ValueError(f"sequence {seq!r} already allocated")
         tokens = list(tokens)
         n = len(tokens)
@@ -198,7 +210,7 @@ class RefBlockManager:
 
     def fork(self, parent, child):
         """day31 fork_sequence: share every block of the parent (ref+1)."""
-        if child in self.tables:
+        if child in self.tables or child in self.swapped:
             raise ValueError(f"sequence {child!r} already exists")
         table = self.tables[parent]
         self.tables[child] = list(table)
@@ -211,6 +223,7 @@ class RefBlockManager:
     def free(self, seq):
         """P06 free: reverse walk, ref-1; at 0 a keyed block goes to the
         newest end of the evictable pool, any other block to the free list."""
+        self.swapped.pop(seq, None)
         if seq not in self.tables:
             return
         for b in reversed(self.tables[seq]):
@@ -221,6 +234,31 @@ class RefBlockManager:
                 else:
                     self.free_list.append(b)
         del self.tables[seq], self.tokens[seq], self.hashes[seq], self.cached[seq]
+
+    # ----- preemption ----------------------------------------------------
+    def swap_out(self, seq):
+        """article-130 ``_preempt_request``: the caller copies the returned
+        blocks (logical order) to host memory; they are then freed in the
+        P06 reverse order and the sequence keeps only its tokens."""
+        table = list(self.tables[seq])          # KeyError: unknown sequence
+        tokens = list(self.tokens[seq])
+        self.free(seq)
+        self.swapped[seq] = tokens
+        return table
+
+    def swap_in(self, seq):
+        """Bring a preempted sequence back through the P06 allocate (all or
+        nothing: OutOfBlocks leaves it swapped and the state unchanged).
+        Returns (table, first_restore): logical blocks before first_restore
+        were prefix hits whose KV is still on the GPU; the caller restores
+        the host copies of blocks first_restore.. into table[first_restore:]."""
+        tokens = self.swapped.pop(seq)          # KeyError: not swapped out
+        try:
+            table = self.allocate(seq, tokens)
+        except OutOfBlocks:
+            self.swapped[seq] = tokens
+            raise
+        return table, self.cached[seq] // self.bs
 
     # ----- queries -------------------------------------------------------
     def slot(self, seq, pos) -> int:
@@ -249,6 +287,7 @@ class RefBlockManager:
             "tables": {s: list(t) for s, t in self.tables.items()},
             "lens": {s: len(t) for s, t in self.tokens.items()},
             "cached": dict(self.cached),
+            "swapped": {s: len(t) for s, t in self.swapped.items()},
         }
 
     def check_invariants(self):
@@ -280,6 +319,8 @@ class RefBlockManager:
             n = len(self.tokens[s])
             assert c % self.bs == 0, "I5: cached % bs"
             assert c < n or (n == 0 and c == 0), "I5: cached >= len"
+        # A swapped-out sequence holds no blocks.
+        assert not (set(self.swapped) & set(self.tables)), "swapped seq holds blocks"
         # Tables are tight: exactly ceil(len/bs) blocks.
         for s, t in self.tables.items():
             assert len(t) == math.ceil(len(self.tokens[s]) / self.bs)

@@ -50,3 +50,44 @@ def ref_copy_blocks(k_caches, v_caches, pairs, inplace=False):
             k_out[layer][d] = k_out[layer][s]
             v_out[layer][d] = v_out[layer][s]
     return k_out, v_out
+
+
+def ref_swap_out(k_caches, v_caches, blocks):
+    """Copy blocks to host memory: the preempted sequence's KV leaves the GPU.
+
+    "qaqbuyan.com article 130", continuous-batching scheduler,
+    ``_preempt_request``: each of the victim's physical blocks is copied to
+    CPU memory before it is freed.  Returns one array
+    ``[len(blocks), num_layers, 2, block_size, num_heads, head_dim]``: for
+    list entry i and layer l, ``[i, l, 0]`` is ``K_l[blocks[i]]`` and
+    ``[i, l, 1]`` is ``V_l[blocks[i]]``.
+    """
+    blocks = [int(b) for b in blocks]
+    L = len(k_caches)
+    shape = (len(blocks), L, 2) + tuple(k_caches[0].shape[1:])
+    out = np.empty(shape, dtype=k_caches[0].dtype)
+    for i, b in enumerate(blocks):
+        for layer in range(L):
+            out[i, layer, 0] = k_caches[layer][b]
+            out[i, layer, 1] = v_caches[layer][b]
+    return out
+
+
+def ref_swap_in(k_caches, v_caches, blocks, host, inplace=False):
+    """Restore host copies into (fresh) blocks: the inverse of ref_swap_out.
+
+    For list entry i and every layer l: ``K_l[blocks[i]] = host[i, l, 0]``
+    and ``V_l[blocks[i]] = host[i, l, 1]``.  Blocks must be distinct.
+    Returns new per-layer lists, or with ``inplace`` writes into the given
+    arrays and returns them.
+    """
+    blocks = [int(b) for b in blocks]
+    assert len(set(blocks)) == len(blocks), "duplicate destination block"
+    assert host.shape[0] == len(blocks) and host.shape[1] == len(k_caches)
+    k_out = list(k_caches) if inplace else [k.copy() for k in k_caches]
+    v_out = list(v_caches) if inplace else [v.copy() for v in v_caches]
+    for i, b in enumerate(blocks):
+        for layer in range(len(k_out)):
+            k_out[layer][b] = host[i, layer, 0]
+            v_out[layer][b] = host[i, layer, 1]
+    return k_out, v_out

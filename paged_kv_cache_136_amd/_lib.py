@@ -35,6 +35,10 @@ SIGNATURES = {
     "pa_bm_append_slots": (ctypes.c_int, [c_vp, P_i64, P_i32, c_i32, P_i64, P_i32, P_i32, P_i32]),
     "pa_bm_fork": (ctypes.c_int, [c_vp, c_i64, c_i64]),
     "pa_bm_free": (ctypes.c_int, [c_vp, c_i64]),
+    "pa_bm_swap_out": (ctypes.c_int, [c_vp, c_i64, P_i32, c_i32, P_i32]),
+    "pa_bm_swap_in": (ctypes.c_int, [c_vp, c_i64, P_i32, c_i32, P_i32, P_i32]),
+    "pa_bm_is_swapped": (c_i32, [c_vp, c_i64]),
+    "pa_bm_swapped": (ctypes.c_int, [c_vp, P_i64, P_i32, c_i32, P_i32]),
     "pa_bm_slot": (ctypes.c_int, [c_vp, c_i64, c_i32, P_i64]),
     "pa_bm_num_free_blocks": (c_i32, [c_vp]),
     "pa_bm_can_allocate": (c_i32, [c_vp, c_i32]),
@@ -50,6 +54,10 @@ SIGNATURES = {
                                    c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (ctypes.c_int, [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_i32, c_i64,
                                       c_i32, c_vp, c_i32, c_vp]),
+    "pa_swap_out": (ctypes.c_int, [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_i32, c_i64,
+                                   c_i32, c_vp, c_i32, c_vp, c_i64, c_vp]),
+    "pa_swap_in": (ctypes.c_int, [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_i32, c_i64,
+                                  c_i32, c_vp, c_i32, c_vp, c_i64, c_vp]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_vp]),

@@ -20,7 +20,8 @@ class BlockManager:
 
     Mirrors the "P06 · BlockManager" page's interface (allocate,
     append_slot, free, slot, num_free_blocks, can_allocate,
-    num_cached_tokens) plus the "day31" fork.
+    num_cached_tokens), the "day31" fork, and swap-out/in of a preempted
+    sequence ("qaqbuyan.com article 130", continuous-batching scheduler).
     """
 
     def __init__(self, num_blocks, block_size, enable_prefix_cache=True):
@@ -73,6 +74,38 @@ class BlockManager:
 
     def free(self, seq):
         check(lib().pa_bm_free(self._h, int(seq)))
+
+    def swap_out(self, seq):
+        """Preempt ``seq``: returns its table (the blocks whose bytes go to
+        host memory, logical order) and frees them; the tokens are kept."""
+        cap = -(-self.seq_len(seq) // self.bs)
+        table = np.empty(max(cap, 1), dtype=np.int32)
+        n = ctypes.c_int32()
+        check(lib().pa_bm_swap_out(self._h, int(seq), _i32p(table), cap, ctypes.byref(n)))
+        return table[:n.value].tolist()
+
+    def swap_in(self, seq):
+        """Resume a swapped-out ``seq``.  Returns (table, first_restore):
+        blocks table[first_restore:] need their host copies back."""
+        cap = -(-dict(self.swapped()).get(int(seq), 0) // self.bs)
+        table = np.empty(max(cap, 1), dtype=np.int32)
+        n, first = ctypes.c_int32(), ctypes.c_int32()
+        check(lib().pa_bm_swap_in(self._h, int(seq), _i32p(table), cap, ctypes.byref(n),
+                                  ctypes.byref(first)))
+        return table[:n.value].tolist(), first.value
+
+    def is_swapped(self, seq):
+        return lib().pa_bm_is_swapped(self._h, int(seq)) == 1
+
+    def swapped(self):
+        """[(seq, len)] of the swapped-out sequences, ascending ids."""
+        n = ctypes.c_int32()
+        check(lib().pa_bm_swapped(self._h, None, None, 0, ctypes.byref(n)))
+        ids = np.empty(max(n.value, 1), dtype=np.int64)
+        lens = np.empty(max(n.value, 1), dtype=np.int32)
+        check(lib().pa_bm_swapped(self._h, ids.ctypes.data_as(P_i64), _i32p(lens), n.value,
+                                  ctypes.byref(n)))
+        return list(zip(ids[:n.value].tolist(), lens[:n.value].tolist()))
 
     # ---- queries --------------------------------------------------------
     def slot(self, seq, pos):
@@ -149,4 +182,5 @@ class BlockManager:
             "tables": {s: self.get_table(s) for s in seqs},
             "lens": {s: self.seq_len(s) for s in seqs},
             "cached": {s: self.num_cached_tokens(s) for s in seqs},
+            "swapped": dict(self.swapped()),
         }

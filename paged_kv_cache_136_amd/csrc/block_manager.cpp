@@ -9,7 +9,9 @@
 // I1-I5, details (fixed sentinel, contiguous match, coarse can_allocate,
 // prefix cache switch, duplicate-content rule) and algorithm notes
 // (take-block helper, append order, reverse free).  Fork and COW append:
-// "day31", toy COW append.
+// "day31", toy COW append.  Preemption: "qaqbuyan.com article 130",
+// continuous-batching scheduler (the victim's blocks go to host memory and
+// are freed); the way back is the allocate path over the saved tokens.
 //
 // Data layout (all O(1) per step, no allocation on the append path once a
 // sequence's vectors have grown):
@@ -76,6 +78,7 @@ struct pa_bm {
   std::vector<uint8_t> in_pool;
   int32_t ev_head = -1, ev_tail = -1, nevict = 0;
   std::unordered_map<int64_t, Seq> seqs;
+  std::unordered_map<int64_t, std::vector<int32_t>> swapped;  // preempted: tokens only
   mutable std::mutex mu;
 
   int32_t num_free() const { return nfree + nevict; }
@@ -185,12 +188,10 @@ pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size, int32_t enable_prefi
 
 void pa_bm_destroy(pa_bm* bm) { delete bm; }
 
-int pa_bm_allocate(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n,
-                   int32_t* table_out, int32_t cap, int32_t* nblocks_out) {
-  if (!bm) return fail(PA_ERR_INVALID, "pa_bm_allocate: null manager");
-  std::lock_guard<std::mutex> lock(bm->mu);
-  if (n < 0 || (n > 0 && !tokens)) return fail(PA_ERR_INVALID, "pa_bm_allocate: bad tokens");
-  if (bm->seqs.count(seq)) return fail(PA_ERR_INVALID, "pa_bm_allocate: sequence exists");
+// The allocate row of the operations table; the caller holds the lock and
+// has checked that `seq` is neither live nor swapped out.
+static int allocate_locked(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n,
+                           int32_t* table_out, int32_t cap, int32_t* nblocks_out) {
   const int32_t bs = bm->bs;
   const int32_t nblocks = (n + bs - 1) / bs;
   if (table_out && cap < nblocks) return fail(PA_ERR_INVALID, "pa_bm_allocate: table_out too small");
@@ -243,8 +244,19 @@ int pa_bm_allocate(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n,
   if (table_out) std::copy(s.table.begin(), s.table.end(), table_out);
   if (nblocks_out) *nblocks_out = nblocks;
   bm->seqs.emplace(seq, std::move(s));
-  pkv::clear_error();
   return PA_OK;
+}
+
+int pa_bm_allocate(pa_bm* bm, int64_t seq, const int32_t* tokens, int32_t n,
+                   int32_t* table_out, int32_t cap, int32_t* nblocks_out) {
+  if (!bm) return fail(PA_ERR_INVALID, "pa_bm_allocate: null manager");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  if (n < 0 || (n > 0 && !tokens)) return fail(PA_ERR_INVALID, "pa_bm_allocate: bad tokens");
+  if (bm->seqs.count(seq) || bm->swapped.count(seq))
+    return fail(PA_ERR_INVALID, "pa_bm_allocate: sequence exists");
+  int st = allocate_locked(bm, seq, tokens, n, table_out, cap, nblocks_out);
+  if (st == PA_OK) pkv::clear_error();
+  return st;
 }
 
 static int append_locked(pa_bm* bm, int64_t seq, int32_t token, int64_t* slot_out,
@@ -328,7 +340,8 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   std::lock_guard<std::mutex> lock(bm->mu);
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return fail(PA_ERR_INVALID, "pa_bm_fork: unknown parent");
-  if (bm->seqs.count(child)) return fail(PA_ERR_INVALID, "pa_bm_fork: child exists");
+  if (bm->seqs.count(child) || bm->swapped.count(child))
+    return fail(PA_ERR_INVALID, "pa_bm_fork: child exists");
   Seq s = it->second;
   for (int32_t b : s.table) ++bm->ref[b];
   bm->seqs.emplace(child, std::move(s));
@@ -339,11 +352,79 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
 int pa_bm_free(pa_bm* bm, int64_t seq) {
   if (!bm) return fail(PA_ERR_INVALID, "pa_bm_free: null manager");
   std::lock_guard<std::mutex> lock(bm->mu);
+  bm->swapped.erase(seq);
   auto it = bm->seqs.find(seq);
   if (it != bm->seqs.end()) {
     bm->free_seq(it->second);
     bm->seqs.erase(it);
   }
+  pkv::clear_error();
+  return PA_OK;
+}
+
+int pa_bm_swap_out(pa_bm* bm, int64_t seq, int32_t* table_out, int32_t cap, int32_t* nblocks_out) {
+  if (!bm || !nblocks_out) return fail(PA_ERR_INVALID, "pa_bm_swap_out: null argument");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return fail(PA_ERR_INVALID, "pa_bm_swap_out: unknown sequence");
+  Seq& s = it->second;
+  const int32_t nblocks = static_cast<int32_t>(s.table.size());
+  if (nblocks > cap || (!table_out && nblocks > 0))
+    return fail(PA_ERR_INVALID, "pa_bm_swap_out: table_out too small");
+  std::copy(s.table.begin(), s.table.end(), table_out);
+  *nblocks_out = nblocks;
+  bm->free_seq(s);
+  bm->swapped.emplace(seq, std::move(s.tokens));
+  bm->seqs.erase(it);
+  pkv::clear_error();
+  return PA_OK;
+}
+
+int pa_bm_swap_in(pa_bm* bm, int64_t seq, int32_t* table_out, int32_t cap, int32_t* nblocks_out,
+                  int32_t* first_restore_out) {
+  if (!bm || !nblocks_out || !first_restore_out)
+    return fail(PA_ERR_INVALID, "pa_bm_swap_in: null argument");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  auto it = bm->swapped.find(seq);
+  if (it == bm->swapped.end()) return fail(PA_ERR_INVALID, "pa_bm_swap_in: sequence is not swapped out");
+  const std::vector<int32_t>& toks = it->second;
+  const int32_t n = static_cast<int32_t>(toks.size());
+  if (!table_out && n > 0) return fail(PA_ERR_INVALID, "pa_bm_swap_in: null table_out");
+  int st = allocate_locked(bm, seq, toks.data(), n, table_out, cap, nblocks_out);
+  if (st != PA_OK) return st;                 // still swapped out, nothing changed
+  *first_restore_out = bm->seqs.at(seq).cached / bm->bs;
+  bm->swapped.erase(it);
+  pkv::clear_error();
+  return PA_OK;
+}
+
+int32_t pa_bm_is_swapped(const pa_bm* bm, int64_t seq) {
+  if (!bm) return -1;
+  std::lock_guard<std::mutex> lock(bm->mu);
+  return bm->swapped.count(seq) ? 1 : 0;
+}
+
+int pa_bm_swapped(const pa_bm* bm, int64_t* seqs_out, int32_t* lens_out, int32_t cap,
+                  int32_t* n_out) {
+  if (!bm || !n_out) return fail(PA_ERR_INVALID, "pa_bm_swapped: null argument");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  const int32_t n = static_cast<int32_t>(bm->swapped.size());
+  if (!seqs_out && !lens_out) {   // count only
+    *n_out = n;
+    pkv::clear_error();
+    return PA_OK;
+  }
+  if (n > cap || (n > 0 && (!seqs_out || !lens_out)))
+    return fail(PA_ERR_INVALID, "pa_bm_swapped: output too small");
+  std::vector<int64_t> ids;
+  ids.reserve(n);
+  for (const auto& kv : bm->swapped) ids.push_back(kv.first);
+  std::sort(ids.begin(), ids.end());
+  for (int32_t i = 0; i < n; ++i) {
+    seqs_out[i] = ids[i];
+    lens_out[i] = static_cast<int32_t>(bm->swapped.at(ids[i]).size());
+  }
+  *n_out = n;
   pkv::clear_error();
   return PA_OK;
 }
@@ -474,6 +555,8 @@ int pa_bm_check_invariants(const pa_bm* bm) {
     int32_t b = kv.second;
     if (!bm->has_hash[b] || bm->block_hash[b] != kv.first) return fail(PA_ERR_INVALID, "I3");
   }
+  for (const auto& kv : bm->swapped)
+    if (bm->seqs.count(kv.first)) return fail(PA_ERR_INVALID, "swapped-out sequence holds blocks");
   std::vector<int32_t> count(nb, 0);
   for (const auto& kv : bm->seqs) {
     const Seq& s = kv.second;

@@ -76,6 +76,54 @@ def pa_copy_blocks(k_caches, v_caches, pairs, stream=None):
                                _stream(stream)))
 
 
+def _layer_ptrs(k_caches, v_caches):
+    k_caches, v_caches = list(k_caches), list(v_caches)
+    if len(k_caches) != len(v_caches):
+        raise ValueError("K and V layer counts differ")
+    _dev(*k_caches, *v_caches)
+    shape = k_caches[0].shape
+    for t in k_caches + v_caches:
+        if t.shape != shape or t.dtype != k_caches[0].dtype:
+            raise ValueError("all caches must share shape and dtype")
+    L = len(k_caches)
+    kp = (c_vp * L)(*[t.data_ptr() for t in k_caches])
+    vp = (c_vp * L)(*[t.data_ptr() for t in v_caches])
+    block_bytes = k_caches[0][0].numel() * k_caches[0].element_size()
+    return kp, vp, L, block_bytes, shape[0]
+
+
+def swap_record_bytes(k_caches):
+    """Host bytes one block takes in a swap record (every layer, K and V)."""
+    k_caches = list(k_caches)
+    return len(k_caches) * 2 * k_caches[0][0].numel() * k_caches[0].element_size()
+
+
+def _swap(fn, k_caches, v_caches, blocks, host, stream):
+    if not k_caches:
+        return
+    _dev(blocks)
+    if blocks.dtype != torch.int32 or blocks.dim() != 1:
+        raise ValueError("blocks must be an int32 [n] device tensor")
+    if host.is_cuda or not host.is_contiguous():
+        raise ValueError("host buffer must be a contiguous host tensor (pin_memory=True)")
+    kp, vp, L, block_bytes, nb = _layer_ptrs(k_caches, v_caches)
+    host_bytes = host.numel() * host.element_size()
+    check(fn(kp, vp, L, block_bytes, nb, blocks.data_ptr(), blocks.shape[0], host.data_ptr(),
+             host_bytes, _stream(stream)))
+
+
+def pa_swap_out(k_caches, v_caches, blocks, host, stream=None):
+    """Copy the listed blocks of every layer's K and V into the pinned host
+    tensor ``host``: entry i's records fill bytes [i*R, (i+1)*R) with
+    R = swap_record_bytes(k_caches) (layer-major, K then V)."""
+    _swap(lib().pa_swap_out, list(k_caches), list(v_caches), blocks, host, stream)
+
+
+def pa_swap_in(k_caches, v_caches, blocks, host, stream=None):
+    """Restore host records (layout of pa_swap_out) into the listed blocks."""
+    _swap(lib().pa_swap_in, list(k_caches), list(v_caches), blocks, host, stream)
+
+
 def pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partition_tokens):
     return lib().pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len,
                                            partition_tokens)

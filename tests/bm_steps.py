@@ -1,8 +1,9 @@
 """Runs a golden block-manager script against any manager object.
 
 The manager must offer allocate/append_slot/free/fork/slot/num_free_blocks/
-num_cached_tokens/get_table/dump with the oracle's semantics; sequence names
-from the pages ("x", "a", ...) are mapped to small integers.
+num_cached_tokens/get_table/swap_out/swap_in/dump with the oracle's
+semantics; sequence names from the pages ("x", "a", ...) are mapped to small
+integers.
 """
 
 
@@ -29,6 +30,27 @@ def run_steps(bm, spec, oob_exc):
             else:
                 got = bm.allocate(sid(st["seq"]), st["tokens"])
                 assert list(got) == exp, f"{where}: got {got}"
+        elif op == "swap_out":
+            got = bm.swap_out(sid(st["seq"]))
+            assert list(got) == exp, f"{where}: got {got}"
+        elif op == "swap_in":
+            if exp == "OutOfBlocks":
+                before = bm.dump()
+                try:
+                    bm.swap_in(sid(st["seq"]))
+                except oob_exc:
+                    pass
+                else:
+                    raise AssertionError(f"{where}: no OutOfBlocks")
+                if st.get("state_unchanged"):
+                    assert bm.dump() == before, f"{where}: state changed"
+            else:
+                table, first = bm.swap_in(sid(st["seq"]))
+                assert (list(table), first) == (exp["table"], exp["first_restore"]), \
+                    f"{where}: got {table}, {first}"
+        elif op == "swapped":
+            want = {sid(k): v for k, v in exp.items()}
+            assert bm.dump()["swapped"] == want, f"{where}: got {bm.dump()['swapped']}"
         elif op == "append_slot":
             slot, _cow = bm.append_slot(sid(st["seq"]), st["token"])
             assert slot == exp, f"{where}: got {slot}"

@@ -48,12 +48,12 @@ static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops
   std::mt19937 rng(seed);
   pa_bm* bm = pa_bm_create(nb, bs, prefix);
   REQUIRE(bm);
-  std::vector<int64_t> live;
+  std::vector<int64_t> live, swapped;
   int64_t next = 1;
-  long oob = 0, cow = 0, hits = 0;
+  long oob = 0, cow = 0, hits = 0, swap_hits = 0;
   for (int it = 0; it < ops; ++it) {
     const int r = rng() % 100;
-    if (r < 30 || live.empty()) {
+    if (r < 25 || live.empty()) {
       int n = rng() % (4 * bs + 2);
       std::vector<int32_t> toks(n);
       for (auto& t : toks) t = rng() % alphabet;
@@ -71,7 +71,7 @@ static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops
         hits += c > 0;
         live.push_back(next++);
       }
-    } else if (r < 55) {
+    } else if (r < 50) {
       int64_t s = live[rng() % live.size()];
       int64_t slot = -2;
       int32_t src = -2, dst = -2, len0 = -1, len1 = -1;
@@ -89,7 +89,7 @@ static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops
         cow += src >= 0;
         REQUIRE((src >= 0) == (dst >= 0));
       }
-    } else if (r < 65) {
+    } else if (r < 58) {
       // batched append over a few live sequences (distinct ids)
       std::vector<int64_t> ids;
       for (int k = 0; k < 3 && k < (int)live.size(); ++k) ids.push_back(live[(rng() % live.size())]);
@@ -104,12 +104,58 @@ static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops
       REQUIRE(st == PA_OK || st == PA_ERR_OUT_OF_BLOCKS);
       REQUIRE(ndone >= 0 && ndone <= (int32_t)ids.size() && ncow >= 0 && ncow <= ndone);
       if (st != PA_OK) ++oob;
-    } else if (r < 75) {
+    } else if (r < 65) {
       int64_t p = live[rng() % live.size()];
       REQUIRE(pa_bm_fork(bm, p, next) == PA_OK);
       REQUIRE(pa_bm_fork(bm, p, next) == PA_ERR_INVALID);   // child exists
       live.push_back(next++);
-    } else if (r < 90) {
+    } else if (r < 71) {
+      // preempt: swap out, with a too-small table first (must change nothing)
+      size_t i = rng() % live.size();
+      int64_t s = live[i];
+      int32_t len = -1, n = -1;
+      REQUIRE(pa_bm_seq_len(bm, s, &len) == PA_OK);
+      const int32_t nbk = (len + bs - 1) / bs;
+      std::vector<int32_t> table(nbk + 1, -7);
+      if (nbk > 0) {
+        Dump before = dump(bm, nb);
+        REQUIRE(pa_bm_swap_out(bm, s, table.data(), nbk - 1, &n) == PA_ERR_INVALID);
+        REQUIRE(dump(bm, nb) == before);
+      }
+      REQUIRE(pa_bm_swap_out(bm, s, table.data(), nbk, &n) == PA_OK && n == nbk);
+      REQUIRE(table[nbk] == -7);
+      REQUIRE(pa_bm_is_swapped(bm, s) == 1);
+      REQUIRE(pa_bm_swap_out(bm, s, table.data(), nbk, &n) == PA_ERR_INVALID);
+      live.erase(live.begin() + i);
+      swapped.push_back(s);
+    } else if (r < 77 && !swapped.empty()) {
+      size_t i = rng() % swapped.size();
+      int64_t s = swapped[i];
+      int32_t cnt = -1;
+      REQUIRE(pa_bm_swapped(bm, nullptr, nullptr, 0, &cnt) == PA_OK && cnt == (int32_t)swapped.size());
+      std::vector<int64_t> ids(cnt);
+      std::vector<int32_t> lens(cnt);
+      REQUIRE(pa_bm_swapped(bm, ids.data(), lens.data(), cnt, &cnt) == PA_OK);
+      int32_t len = -1;
+      for (int32_t k = 0; k < cnt; ++k) if (ids[k] == s) len = lens[k];
+      REQUIRE(len >= 0);
+      const int32_t nbk = (len + bs - 1) / bs;
+      std::vector<int32_t> table(nbk + 1, -7);
+      int32_t n = -1, first = -1;
+      Dump before = dump(bm, nb);
+      int st = pa_bm_swap_in(bm, s, table.data(), nbk, &n, &first);
+      if (st == PA_ERR_OUT_OF_BLOCKS) {
+        ++oob;
+        REQUIRE(dump(bm, nb) == before && pa_bm_is_swapped(bm, s) == 1);
+      } else {
+        REQUIRE(st == PA_OK && n == nbk && first >= 0 && first <= nbk && table[nbk] == -7);
+        int32_t c = -1;
+        REQUIRE(pa_bm_num_cached_tokens(bm, s, &c) == PA_OK && c == first * bs);
+        swap_hits += first > 0;
+        swapped.erase(swapped.begin() + i);
+        live.push_back(s);
+      }
+    } else if (r < 92) {
       size_t i = rng() % live.size();
       REQUIRE(pa_bm_free(bm, live[i]) == PA_OK);
       live.erase(live.begin() + i);
@@ -130,13 +176,15 @@ static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops
     REQUIRE(pa_bm_check_invariants(bm) == PA_OK);
   }
   for (int64_t s : live) REQUIRE(pa_bm_free(bm, s) == PA_OK);
+  for (int64_t s : swapped) REQUIRE(pa_bm_free(bm, s) == PA_OK && pa_bm_is_swapped(bm, s) == 0);
   REQUIRE(pa_bm_check_invariants(bm) == PA_OK);
   REQUIRE(pa_bm_num_free_blocks(bm) == nb);
   REQUIRE(pa_bm_num_seqs(bm) == 0);
   REQUIRE(oob > 0);
-  if (prefix) REQUIRE(hits > 0);
+  if (prefix) REQUIRE(hits > 0 && swap_hits > 0);
   pa_bm_destroy(bm);
-  std::printf("seed %u nb %d bs %d prefix %d: oob %ld cow %ld hits %ld\n", seed, nb, bs, prefix, oob, cow, hits);
+  std::printf("seed %u nb %d bs %d prefix %d: oob %ld cow %ld hits %ld swap hits %ld\n", seed, nb,
+              bs, prefix, oob, cow, hits, swap_hits);
 }
 
 static void bad_arguments() {

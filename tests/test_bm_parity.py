@@ -49,6 +49,10 @@ def _apply(bm, op, args, oob):
             return ("ok", bm.fork(*args))
         if op == "free":
             return ("ok", bm.free(*args))
+        if op == "swap_out":
+            return ("ok", bm.swap_out(*args))
+        if op == "swap_in":
+            return ("ok", bm.swap_in(*args))
     except oob:
         return ("oob", None)
     raise ValueError(op)
@@ -61,17 +65,22 @@ def test_random_stream_parity(seed, bs, nblocks, prefix, alphabet):
     rng = random.Random(seed)
     lib_bm = BlockManager(nblocks, bs, prefix)
     ref_bm = oracle.RefBlockManager(nblocks, bs, prefix)
-    live, nxt = [], 1
-    counts = {"oob": 0, "hit": 0, "cow": 0}
+    live, swapped, nxt = [], [], 1
+    counts = {"oob": 0, "hit": 0, "cow": 0, "swap_hit": 0}
     for _ in range(2000):
         r = rng.random()
-        if r < 0.3 or not live:
+        if r < 0.25 or not live:
             toks = [rng.randrange(alphabet) for _ in range(rng.randrange(0, 4 * bs + 2))]
             op, args = "allocate", (nxt, toks)
-        elif r < 0.65:
+        elif r < 0.55:
             op, args = "append", (rng.choice(live), rng.randrange(alphabet))
-        elif r < 0.8:
+        elif r < 0.67:
             op, args = "fork", (rng.choice(live), nxt)
+        elif r < 0.75:
+            op, args = "swap_out", (live.pop(rng.randrange(len(live))),)
+            swapped.append(args[0])
+        elif r < 0.83 and swapped:
+            op, args = "swap_in", (swapped[rng.randrange(len(swapped))],)
         else:
             op, args = "free", (live.pop(rng.randrange(len(live))),)
         got = _apply(lib_bm, op, args, OutOfBlocks)
@@ -79,6 +88,10 @@ def test_random_stream_parity(seed, bs, nblocks, prefix, alphabet):
         assert got == want, (op, args)
         if got[0] == "oob":
             counts["oob"] += 1
+        elif op == "swap_in":
+            swapped.remove(args[0])
+            live.append(args[0])
+            counts["swap_hit"] += got[1][1] > 0
         elif op in ("allocate", "fork"):
             live.append(nxt)
             nxt += 1
@@ -87,14 +100,14 @@ def test_random_stream_parity(seed, bs, nblocks, prefix, alphabet):
         elif op == "append" and got[1][1] is not None:
             counts["cow"] += 1
         _same(lib_bm, ref_bm)
-    for s in live:
+    for s in live + swapped:
         lib_bm.free(s)
         ref_bm.free(s)
     _same(lib_bm, ref_bm)
-    assert lib_bm.num_free_blocks == nblocks
+    assert lib_bm.num_free_blocks == nblocks and not lib_bm.swapped()
     assert counts["oob"] > 0
     if prefix:
-        assert counts["hit"] > 0
+        assert counts["hit"] > 0 and counts["swap_hit"] > 0
 
 
 def test_append_slots_batched_matches_single():
@@ -130,6 +143,18 @@ def test_export_batch_and_errors():
     bm.free(99)                                     # no-op
     with pytest.raises(Exception):
         bm.slot(6, 2)                               # pos out of range
+    with pytest.raises(Exception):
+        bm.swap_out(99)                             # unknown id
+    with pytest.raises(Exception):
+        bm.swap_in(6)                               # live, not swapped out
+    assert bm.swap_out(6) == [3] and bm.is_swapped(6)
+    with pytest.raises(Exception):
+        bm.allocate(6, [1])                         # swapped-out id is taken
+    with pytest.raises(Exception):
+        bm.fork(5, 6)
+    bm.free(6)                                      # drops the swapped record
+    assert not bm.is_swapped(6) and bm.swapped() == []
+    bm.allocate(6, [1])
 
 
 def test_config1_tables_and_scrambled_order():

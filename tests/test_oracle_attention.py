@@ -19,6 +19,7 @@ import pytest
 import torch
 
 from oracle import (RefBlockManager, ref_copy_blocks, ref_decode, ref_decode_one,
+                    ref_swap_in, ref_swap_out,
                     ref_write_kv)
 
 
@@ -195,6 +196,62 @@ def test_copy_blocks_definition():
         ref_copy_blocks(ks, vs, [(1, 3), (2, 3)])
     with pytest.raises(AssertionError):
         ref_copy_blocks(ks, vs, [(1, 3), (3, 4)])
+
+
+def test_swap_copies_definition():
+    """Preemption copies (article 130, scheduler, _preempt_request): the host
+    record of list entry i, layer l is K_l/V_l of block i, and restoring it
+    into other blocks reproduces those bytes there and nowhere else."""
+    rng = np.random.default_rng(8)
+    ks = [rng.standard_normal((6, 4, 2, 3)) for _ in range(3)]
+    vs = [rng.standard_normal((6, 4, 2, 3)) for _ in range(3)]
+    host = ref_swap_out(ks, vs, [4, 1])
+    assert host.shape == (2, 3, 2, 4, 2, 3)
+    for layer in range(3):
+        assert np.array_equal(host[0, layer, 0], ks[layer][4])
+        assert np.array_equal(host[1, layer, 1], vs[layer][1])
+    k2, v2 = ref_swap_in(ks, vs, [0, 5], host)
+    for layer in range(3):
+        assert np.array_equal(k2[layer][0], ks[layer][4]) and np.array_equal(k2[layer][5], ks[layer][1])
+        assert np.array_equal(v2[layer][0], vs[layer][4]) and np.array_equal(v2[layer][5], vs[layer][1])
+        assert np.array_equal(k2[layer][1:5], ks[layer][1:5])
+    with pytest.raises(AssertionError):
+        ref_swap_in(ks, vs, [2, 2], host)
+
+
+@pytest.mark.parametrize("prefix", [False, True])
+def test_swap_round_trip_keeps_attention(prefix):
+    """A preempted sequence that comes back attends to exactly the same K/V:
+    decode after swap-out, reuse of its blocks by another sequence, and
+    swap-in (restoring only blocks from first_restore on) equals decode
+    before.  Its own full prefix blocks are the hits when the cache is on."""
+    rng = np.random.default_rng(9)
+    bs, nb, H, D = 4, 8, 2, 8
+    bm = RefBlockManager(nb, bs, prefix)
+    k = rng.standard_normal((nb, bs, H, D))
+    v = rng.standard_normal((nb, bs, H, D))
+    toks = list(range(100, 114))                  # 14 tokens: blocks 0-3
+    t0 = bm.allocate(1, toks)
+    q = rng.standard_normal((1, H, D))
+    before = ref_decode(q, k, v, np.array([t0]), np.array([14]))
+    host = ref_swap_out([k], [v], bm.swap_out(1))
+    # Another sequence takes six blocks: the four free ones, block 3 and
+    # (prefix cache on: by evicting the oldest keyed block) block 2, and
+    # overwrites them; then it finishes.
+    t2 = bm.allocate(2, list(range(200, 224)))
+    assert sorted(t2) == [2, 3, 4, 5, 6, 7]
+    for b in t2:
+        k[b] = rng.standard_normal((bs, H, D))
+        v[b] = rng.standard_normal((bs, H, D))
+    bm.free(2)
+    t1, first = bm.swap_in(1)
+    # Cache on: blocks 0 and 1 are still keyed (hits); block 2's key went
+    # with its eviction.  Cache off: everything comes back from host.
+    assert first == (2 if prefix else 0)
+    assert t1[:first] == t0[:first]
+    (k,), (v,) = ref_swap_in([k], [v], t1[first:], host[first:])
+    after = ref_decode(q, k, v, np.array([t1]), np.array([14]))
+    assert np.array_equal(after, before)
 
 
 # ---- planted mistakes: each must fail a pin -------------------------------

@@ -16,7 +16,7 @@ from oracle import OutOfBlocks, RefBlockManager, contiguous_tables, tail_waste_t
 from tests.bm_steps import run_steps
 
 GOLDEN_SCRIPTS = ["bm_example1.json", "bm_example2.json", "bm_example3.json",
-                  "bm_eviction_trace.json"]
+                  "bm_eviction_trace.json", "bm_swap_nocache.json", "bm_swap_prefix.json"]
 
 
 def make(spec, cls=RefBlockManager):
@@ -210,26 +210,39 @@ def _state(bm):
 def random_stream(bm, rng, n_ops, alphabet=3, max_prompt=12, check=True):
     """Seeded random operation stream; checks I1-I5 after every op and that a
     failing operation leaves the state unchanged."""
-    live, next_id, stats = [], 1, {"oob": 0, "hits": 0, "cow": 0}
+    live, swapped, next_id = [], [], 1
+    stats = {"oob": 0, "hits": 0, "cow": 0, "swap_hits": 0}
     for _ in range(n_ops):
         r = rng.random()
         before = _state(bm) if check else None
         try:
-            if r < 0.3 or not live:
+            if r < 0.25 or not live:
                 n = rng.randrange(0, max_prompt)
                 toks = [rng.randrange(alphabet) for _ in range(n)]
                 bm.allocate(next_id, toks)
                 stats["hits"] += bm.num_cached_tokens(next_id) > 0
                 live.append(next_id)
                 next_id += 1
-            elif r < 0.65:
+            elif r < 0.55:
                 s = rng.choice(live)
                 _, cow = bm.append_slot(s, rng.randrange(alphabet))
                 stats["cow"] += cow is not None
-            elif r < 0.8:
+            elif r < 0.67:
                 bm.fork(rng.choice(live), next_id)
                 live.append(next_id)
                 next_id += 1
+            elif r < 0.75:
+                s = live.pop(rng.randrange(len(live)))
+                table = bm.swap_out(s)
+                assert len(table) == -(-len(bm.swapped[s]) // bm.bs)
+                swapped.append(s)
+            elif r < 0.83 and swapped:
+                s = swapped[rng.randrange(len(swapped))]
+                table, first = bm.swap_in(s)
+                swapped.remove(s)
+                live.append(s)
+                assert first * bm.bs == bm.num_cached_tokens(s)
+                stats["swap_hits"] += first > 0
             else:
                 s = live.pop(rng.randrange(len(live)))
                 bm.free(s)
@@ -239,9 +252,10 @@ def random_stream(bm, rng, n_ops, alphabet=3, max_prompt=12, check=True):
                 assert _state(bm) == before, "state changed by a failed op"
         if check:
             bm.check_invariants()
-    for s in live:
+    for s in live + swapped:
         bm.free(s)
     bm.check_invariants()
+    assert not bm.swapped
     assert bm.num_free_blocks == bm.num_blocks
     return stats
 
@@ -251,7 +265,7 @@ def test_random_stream_invariants(seed, bs, nblocks):
     stats = random_stream(RefBlockManager(nblocks, bs), random.Random(seed), 3000)
     # The stream must actually reach the interesting cases (with bs == 1 no
     # block is ever partly filled, so no copy-on-write can happen).
-    assert stats["oob"] > 0 and stats["hits"] > 0
+    assert stats["oob"] > 0 and stats["hits"] > 0 and stats["swap_hits"] > 0
     assert (stats["cow"] > 0) == (bs > 1)
 
 
@@ -371,6 +385,34 @@ class ForwardFree(RefBlockManager):
         del self.tables[seq], self.tokens[seq], self.hashes[seq], self.cached[seq]
 
 
+class SwapInWithoutHits(RefBlockManager):
+    """Mistake: swap_in restores every block, ignoring still-cached prefix
+    blocks (fresh blocks for all, nothing revived)."""
+    def swap_in(self, seq):
+        tokens = self.swapped.pop(seq)
+        table = [self._take_block() for _ in range(-(-len(tokens) // self.bs))]
+        self.tables[seq], self.tokens[seq] = table, tokens
+        self.hashes[seq], self.cached[seq] = self._chain(tokens), 0
+        return list(table), 0
+
+
+class SwapOutForwardFree(RefBlockManager):
+    """Mistake: swap_out releases the table front to back."""
+    def swap_out(self, seq):
+        table = list(self.tables[seq])
+        self.swapped[seq] = list(self.tokens[seq])
+        ForwardFree.free(self, seq)
+        return table
+
+
+class SwapInNotAtomic(RefBlockManager):
+    """Mistake: a failed swap_in loses the saved tokens."""
+    def swap_in(self, seq):
+        tokens = self.swapped.pop(seq)
+        table = self.allocate(seq, tokens)
+        return table, self.cached[seq] // self.bs
+
+
 def partial_block_pin(cls, golden):
     bm = cls(8, 4)
     t = bm.allocate(1, list(range(10)))
@@ -423,6 +465,9 @@ PITFALLS = [
     (CoarseCapacityCheck, golden_pin("bm_example3.json")),
     (ReviveWithoutRemoval, golden_pin("bm_example3.json")),
     (TokenBeforeBlock, append_atomicity_pin),
+    (SwapInWithoutHits, golden_pin("bm_swap_prefix.json")),
+    (SwapOutForwardFree, golden_pin("bm_swap_nocache.json")),
+    (SwapInNotAtomic, golden_pin("bm_swap_nocache.json")),
 ]
 
 
