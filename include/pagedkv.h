@@ -251,36 +251,41 @@ int pa_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_lay
 
 /* Preemption copy to host memory ([A130] continuous-batching scheduler,
  * _preempt_request: each of the victim's blocks is copied to CPU memory).
- * For list entry i < n with b = blocks[i], and layer l < num_layers, the
- * record at byte offset ((i * num_layers + l) * 2 + c) * block_bytes of
- * host_dst receives K_l[b] (c = 0) or V_l[b] (c = 1), block_bytes bytes.
+ * The host buffer is an array of records of R = num_layers * 2 *
+ * block_bytes bytes; a record holds one block of every layer, layer l's K
+ * at byte (2l) * block_bytes and its V at (2l + 1) * block_bytes.  For
+ * list entry i < n with b = blocks[i], record r = host_slots[i] (or r = i
+ * when host_slots is NULL) receives K_l[b] and V_l[b] for every layer l.
  *   k_caches/v_caches: HOST arrays of num_layers device pointers (the
  *     per-layer caches, layout above).
- *   blocks: device int32 [n]; an entry outside [0, num_blocks) is skipped
- *     (its record is left untouched).
+ *   blocks: device int32 [n]; host_slots: device int32 [n] or NULL.  An
+ *     entry whose block is outside [0, num_blocks) or whose record is
+ *     outside the buffer is skipped (its record is left untouched).
  *   host_dst: pinned host memory from hipHostMalloc (torch pin_memory) of
- *     host_bytes >= n * num_layers * 2 * block_bytes bytes; the GPU writes it
- *     directly over the host link.
+ *     host_bytes bytes (floor(host_bytes / R) records; without host_slots
+ *     at least n of them); the GPU writes it directly over the host link.
  * Errors (nothing launched): PA_ERR_INVALID if host_dst is not host memory
- * that HIP maps for the device (checked at both ends of the range), if
- * host_bytes is too small, or for bad sizes / misalignment (block_bytes a
+ * that HIP maps for the device (checked at both ends of the records), if
+ * it holds too few records, or for bad sizes / misalignment (block_bytes a
  * positive multiple of 16; caches and host_dst 16-byte aligned).
- * Asynchronous on `stream`: the host record is complete once the stream
- * has passed this call (synchronize before reading it on the host). */
+ * Asynchronous on `stream`: the records are complete once the stream has
+ * passed this call (synchronize before reading them on the host). */
 int pa_swap_out(void* const* k_caches, void* const* v_caches, int32_t num_layers,
-                int64_t block_bytes, int32_t num_blocks, const int32_t* blocks, int32_t n,
-                void* host_dst, int64_t host_bytes, void* stream);
+                int64_t block_bytes, int32_t num_blocks, const int32_t* blocks,
+                const int32_t* host_slots, int32_t n, void* host_dst, int64_t host_bytes,
+                void* stream);
 
 /* The inverse copy: for list entry i < n with b = blocks[i] and every layer
- * l, K_l[b] and V_l[b] receive the host_src records laid out as in
- * pa_swap_out (entry i's records at ((i * num_layers + l) * 2 + c) *
- * block_bytes).  To resume a sequence, pass table[first_restore..] from
+ * l, K_l[b] and V_l[b] receive the record host_slots[i] (or i) laid out as
+ * in pa_swap_out.  To resume a sequence, pass table[first_restore..] from
  * pa_bm_swap_in and the records of those logical blocks.  Same arguments,
- * checks and errors as pa_swap_out; destinations must be distinct.  The
- * host buffer must stay unchanged until the stream has passed this call. */
+ * checks and errors as pa_swap_out; destination blocks must be distinct.
+ * The host records must stay unchanged until the stream has passed this
+ * call. */
 int pa_swap_in(void* const* k_caches, void* const* v_caches, int32_t num_layers,
-               int64_t block_bytes, int32_t num_blocks, const int32_t* blocks, int32_t n,
-               const void* host_src, int64_t host_bytes, void* stream);
+               int64_t block_bytes, int32_t num_blocks, const int32_t* blocks,
+               const int32_t* host_slots, int32_t n, const void* host_src, int64_t host_bytes,
+               void* stream);
 
 /* Workspace bytes pa_decode needs for these sizes (0 when one partition
  * covers max_context_len, i.e. partition_tokens == 0 or >= max_context_len). */

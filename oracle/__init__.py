@@ -28,6 +28,8 @@ Modules:
 * :mod:`oracle.block_manager` -- ``RefBlockManager`` (P06 spec + day31 fork/COW).
 * :mod:`oracle.kv_ops`        -- ``ref_write_kv``, ``ref_copy_blocks``,
   ``ref_swap_out``, ``ref_swap_in``.
+* :mod:`oracle.scheduler`     -- ``RefScheduler`` (article-130 continuous
+  batching with preemption over ``RefBlockManager``).
 * :mod:`oracle.attention`     -- ``ref_decode`` (fp64 gather + softmax attention).
 * :mod:`oracle.arithmetic`    -- the pages' memory formulas.
 
@@ -42,10 +44,11 @@ from .arithmetic import (block_bytes, blocks_needed, contiguous_tables,
 from .attention import ref_decode, ref_decode_one
 from .block_manager import OutOfBlocks, RefBlockManager
 from .kv_ops import ref_copy_blocks, ref_swap_in, ref_swap_out, ref_write_kv
+from .scheduler import RefScheduler
 
 __all__ = [
     "OutOfBlocks", "RefBlockManager", "ref_write_kv", "ref_copy_blocks",
-    "ref_swap_out", "ref_swap_in",
+    "ref_swap_out", "ref_swap_in", "RefScheduler",
     "ref_decode", "ref_decode_one", "kv_cache_bytes",
     "kv_bytes_per_token", "block_bytes", "blocks_needed", "tail_waste_tokens",
     "contiguous_tables",

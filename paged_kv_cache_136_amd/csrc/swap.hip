@@ -13,8 +13,11 @@
 // Host-side reads have microsecond latency, so every lane keeps several
 // 16-byte loads in flight before storing.
 //
-// Host record layout: entry i of the block list, layer l, c = 0 (K) / 1 (V)
-// at byte ((i * num_layers + l) * 2 + c) * block_bytes.
+// Host record layout: a record is one block of every layer, R = num_layers
+// * 2 * block_bytes bytes; within it, layer l, c = 0 (K) / 1 (V) sits at
+// byte (l * 2 + c) * block_bytes.  Entry i of the block list uses record
+// host_slots[i] (a slot of a host swap pool), or record i when no slot
+// list is given.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -35,6 +38,8 @@ struct SwapArgs {
   uint4* v[kMaxLayersPerLaunch];
   uint4* host;              // device-visible address of the host records
   const int32_t* blocks;
+  const int32_t* host_slots;  // record of each entry; nullptr = entry index
+  int64_t num_records;        // records the host buffer holds
   int64_t chunks_per_block;
   int32_t num_blocks;
   int32_t layer0;           // first layer of this launch
@@ -47,10 +52,10 @@ __global__ __launch_bounds__(kSwapThreads) void swap_kernel(SwapArgs a) {
   const int i = blockIdx.y;
   const int layer = blockIdx.z >> 1, c = blockIdx.z & 1;
   const int32_t b = a.blocks[i];
-  if (b < 0 || b >= a.num_blocks) return;
+  const int64_t r = a.host_slots ? a.host_slots[i] : i;
+  if (b < 0 || b >= a.num_blocks || r < 0 || r >= a.num_records) return;
   uint4* cache = (c ? a.v[layer] : a.k[layer]) + static_cast<int64_t>(b) * a.chunks_per_block;
-  uint4* rec = a.host + ((static_cast<int64_t>(i) * a.num_layers + a.layer0 + layer) * 2 + c) *
-                            a.chunks_per_block;
+  uint4* rec = a.host + ((r * a.num_layers + a.layer0 + layer) * 2 + c) * a.chunks_per_block;
   const uint4* src = TO_HOST ? cache : rec;
   uint4* dst = TO_HOST ? rec : cache;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kSwapThreads;
@@ -96,18 +101,25 @@ void* mapped_host_range(const void* p, int64_t bytes) {
 
 template <bool TO_HOST>
 int swap_impl(const char* name, void* const* k_caches, void* const* v_caches, int32_t num_layers,
-              int64_t block_bytes, int32_t num_blocks, const int32_t* blocks, int32_t n,
-              const void* host, int64_t host_bytes, void* stream) {
+              int64_t block_bytes, int32_t num_blocks, const int32_t* blocks,
+              const int32_t* host_slots, int32_t n, const void* host, int64_t host_bytes,
+              void* stream) {
   const std::string who(name);
   if (num_layers < 0 || n < 0 || num_blocks <= 0 || block_bytes <= 0 || block_bytes % 16)
     return fail(PA_ERR_INVALID, who + ": bad sizes (block_bytes must be a positive multiple of 16)");
   if (num_layers == 0 || n == 0) { clear_error(); return PA_OK; }
   if (!k_caches || !v_caches || !blocks || !host) return fail(PA_ERR_INVALID, who + ": null pointer");
   if (n > 65535) return fail(PA_ERR_UNSUPPORTED, who + ": more than 65535 blocks per call");
-  const int64_t need = static_cast<int64_t>(n) * num_layers * 2 * block_bytes;
-  if (host_bytes < need)
+  const int64_t record = static_cast<int64_t>(num_layers) * 2 * block_bytes;
+  const int64_t num_records = host_bytes / record;
+  if (!host_slots && num_records < n)
     return fail(PA_ERR_INVALID, who + ": host buffer holds " + std::to_string(host_bytes) +
-                                    " bytes, " + std::to_string(need) + " needed");
+                                    " bytes, " + std::to_string(n * record) + " needed");
+  if (num_records < 1)
+    return fail(PA_ERR_INVALID, who + ": host buffer holds " + std::to_string(host_bytes) +
+                                    " bytes, at least one record (" + std::to_string(record) +
+                                    ") needed");
+  const int64_t need = num_records * record;
   if (reinterpret_cast<uintptr_t>(host) & 15)
     return fail(PA_ERR_INVALID, who + ": host buffer must be 16-byte aligned");
   for (int32_t l = 0; l < num_layers; ++l) {
@@ -132,6 +144,8 @@ int swap_impl(const char* name, void* const* k_caches, void* const* v_caches, in
     }
     a.host = static_cast<uint4*>(dev_host);
     a.blocks = blocks;
+    a.host_slots = host_slots;
+    a.num_records = num_records;
     a.chunks_per_block = cpb;
     a.num_blocks = num_blocks;
     a.layer0 = l0;
@@ -152,14 +166,16 @@ using namespace pkv;
 
 extern "C" int pa_swap_out(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                            int64_t block_bytes, int32_t num_blocks, const int32_t* blocks,
-                           int32_t n, void* host_dst, int64_t host_bytes, void* stream) {
+                           const int32_t* host_slots, int32_t n, void* host_dst,
+                           int64_t host_bytes, void* stream) {
   return swap_impl<true>("pa_swap_out", k_caches, v_caches, num_layers, block_bytes, num_blocks,
-                         blocks, n, host_dst, host_bytes, stream);
+                         blocks, host_slots, n, host_dst, host_bytes, stream);
 }
 
 extern "C" int pa_swap_in(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                           int64_t block_bytes, int32_t num_blocks, const int32_t* blocks,
-                          int32_t n, const void* host_src, int64_t host_bytes, void* stream) {
+                          const int32_t* host_slots, int32_t n, const void* host_src,
+                          int64_t host_bytes, void* stream) {
   return swap_impl<false>("pa_swap_in", k_caches, v_caches, num_layers, block_bytes, num_blocks,
-                          blocks, n, host_src, host_bytes, stream);
+                          blocks, host_slots, n, host_src, host_bytes, stream);
 }

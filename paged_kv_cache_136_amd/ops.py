@@ -98,30 +98,36 @@ def swap_record_bytes(k_caches):
     return len(k_caches) * 2 * k_caches[0][0].numel() * k_caches[0].element_size()
 
 
-def _swap(fn, k_caches, v_caches, blocks, host, stream):
+def _swap(fn, k_caches, v_caches, blocks, host, host_slots, stream):
     if not k_caches:
         return
     _dev(blocks)
     if blocks.dtype != torch.int32 or blocks.dim() != 1:
         raise ValueError("blocks must be an int32 [n] device tensor")
+    if host_slots is not None:
+        _dev(host_slots)
+        if host_slots.dtype != torch.int32 or host_slots.shape != blocks.shape:
+            raise ValueError("host_slots must be an int32 [n] device tensor like blocks")
     if host.is_cuda or not host.is_contiguous():
         raise ValueError("host buffer must be a contiguous host tensor (pin_memory=True)")
     kp, vp, L, block_bytes, nb = _layer_ptrs(k_caches, v_caches)
     host_bytes = host.numel() * host.element_size()
-    check(fn(kp, vp, L, block_bytes, nb, blocks.data_ptr(), blocks.shape[0], host.data_ptr(),
-             host_bytes, _stream(stream)))
+    slots_ptr = host_slots.data_ptr() if host_slots is not None else None
+    check(fn(kp, vp, L, block_bytes, nb, blocks.data_ptr(), slots_ptr, blocks.shape[0],
+             host.data_ptr(), host_bytes, _stream(stream)))
 
 
-def pa_swap_out(k_caches, v_caches, blocks, host, stream=None):
-    """Copy the listed blocks of every layer's K and V into the pinned host
-    tensor ``host``: entry i's records fill bytes [i*R, (i+1)*R) with
-    R = swap_record_bytes(k_caches) (layer-major, K then V)."""
-    _swap(lib().pa_swap_out, list(k_caches), list(v_caches), blocks, host, stream)
+def pa_swap_out(k_caches, v_caches, blocks, host, host_slots=None, stream=None):
+    """Copy the listed blocks of every layer's K and V into records of the
+    pinned host tensor ``host`` (R = swap_record_bytes(k_caches) bytes each,
+    layer-major, K then V): entry i goes to record host_slots[i], or to
+    record i without a slot list."""
+    _swap(lib().pa_swap_out, list(k_caches), list(v_caches), blocks, host, host_slots, stream)
 
 
-def pa_swap_in(k_caches, v_caches, blocks, host, stream=None):
+def pa_swap_in(k_caches, v_caches, blocks, host, host_slots=None, stream=None):
     """Restore host records (layout of pa_swap_out) into the listed blocks."""
-    _swap(lib().pa_swap_in, list(k_caches), list(v_caches), blocks, host, stream)
+    _swap(lib().pa_swap_in, list(k_caches), list(v_caches), blocks, host, host_slots, stream)
 
 
 def pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partition_tokens):
