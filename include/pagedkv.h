@@ -183,6 +183,9 @@ int pa_bm_swapped(const pa_bm* bm, int64_t* seqs_out, int32_t* lens_out, int32_t
 /* Flat slot of token `pos` (0 <= pos < len) of `seq` ([P06] spec overview).
  * PA_ERR_INVALID for an unknown seq or pos out of range. */
 int pa_bm_slot(const pa_bm* bm, int64_t seq, int32_t pos, int64_t* slot_out);
+/* The manager's block size and pool size; -1 if bm is NULL. */
+int32_t pa_bm_block_size(const pa_bm* bm);
+int32_t pa_bm_num_blocks(const pa_bm* bm);
 /* Free + evictable block count; -1 if bm is NULL. */
 int32_t pa_bm_num_free_blocks(const pa_bm* bm);
 /* [P06] details: coarse check ceil(n_tokens/block_size) <= num_free_blocks
@@ -219,6 +222,75 @@ int pa_bm_check_invariants(const pa_bm* bm);
  * pointer may be NULL to skip that output. */
 int pa_bm_dump(const pa_bm* bm, int32_t* ref, int8_t* has_hash, int32_t* free_order,
                int32_t* n_free, int32_t* evict_order, int32_t* n_evict);
+
+/* ==== continuous-batching scheduler (host) =============================== */
+
+/* [A130] continuous-batching section: the step timeline and the scheduler's
+ * step (finish, admit first come first served, run, append; preempt the
+ * request with the most generated tokens when no block is left).  It
+ * drives a pa_bm (which must outlive it and is used for nothing else while
+ * the scheduler runs) and only decides: the caller does each step's device
+ * work from the plan, in this order -- swap-in copies (pa_swap_in), prompt
+ * K/V writes, swap-out copies (pa_swap_out), copy-on-write copies
+ * (pa_copy_blocks), the batch's K/V writes (pa_write_kv), decode.  Blocks a
+ * preemption frees can be handed out again in the same step, so the
+ * swap-out copies must precede every write of that step's appends.
+ * Readings where the page stops short: the admitting step runs the prompt
+ * and yields the first token; a request whose budget is met leaves at the
+ * next step; preempted requests resume before new admissions, oldest
+ * first; the victim is chosen among running requests that have neither
+ * appended nor been admitted in this step (the failing request always is
+ * one), ties to the earliest; host swap space is a FIFO pool of
+ * `host_slots` block records (pa_swap_out's record layout); a victim that
+ * does not fit there is recomputed: freed and put back at the front of the
+ * waiting queue with every token it produced as its prompt. */
+typedef struct pa_sched pa_sched;
+
+/* One step's plan, in caller-owned host arrays.  Capacities (checked
+ * before the step starts, so a step never stops half done): every id
+ * array, batch, slots, prefill_counts and cow_pairs (pairs) hold ids_cap >=
+ * max_batch entries; swap_in / swap_out hold pairs_cap >= host_slots pairs;
+ * prefill_slots holds prefill_cap >= num_blocks * block_size entries.
+ * pa_sched_step fills the n_* counts. */
+typedef struct pa_sched_plan {
+  int32_t ids_cap, pairs_cap, prefill_cap;
+  int64_t* finished;    int32_t n_finished;    /* left at this step */
+  int64_t* resumed;     int32_t n_resumed;     /* swapped in */
+  int64_t* admitted;    int32_t n_admitted;    /* prompt runs this step */
+  int64_t* preempted;   int32_t n_preempted;   /* swapped out or recomputed */
+  int64_t* recomputed;  int32_t n_recomputed;  /* the preempted ones sent back to waiting */
+  int32_t* swap_in;     int32_t n_swap_in;     /* [n][2] (host record, block) */
+  int32_t* swap_out;    int32_t n_swap_out;    /* [n][2] (block, host record) */
+  int64_t* prefill_slots; int32_t n_prefill_slots;  /* uncached prompt tokens' slots */
+  int32_t* prefill_counts;                     /* [n_admitted] slots per admitted request */
+  int64_t* batch;       int64_t* slots;  int32_t n_batch;  /* appended: decode batch */
+  int32_t* cow_pairs;   int32_t n_cow;         /* [n][2] (src, dst) */
+} pa_sched_plan;
+
+/* NULL on bad arguments (max_batch > 0, host_slots >= 0). */
+pa_sched* pa_sched_create(pa_bm* bm, int32_t max_batch, int32_t host_slots);
+/* Frees the scheduler only; blocks its requests hold stay in the manager. */
+void pa_sched_destroy(pa_sched* s);
+/* Queue a request (id unused by the scheduler and the manager, n >= 1
+ * prompt tokens, max_new_tokens >= 1). */
+int pa_sched_add_request(pa_sched* s, int64_t id, const int32_t* prompt, int32_t n,
+                         int32_t max_new_tokens);
+/* Run one step's decisions and fill the plan.  PA_ERR_INVALID if the
+ * previous step was not committed or the plan is too small. */
+int pa_sched_step(pa_sched* s, pa_sched_plan* plan);
+/* Tokens produced by the step just planned: exactly one for each request
+ * in its batch and each one it admitted (any order).  PA_ERR_INVALID
+ * (nothing changed) otherwise. */
+int pa_sched_commit(pa_sched* s, const int64_t* ids, const int32_t* tokens, int32_t n);
+/* State queries (arrays NULL = count only; PA_ERR_INVALID if too small):
+ * running requests in batch order with their generated counts; waiting
+ * ids front to back; swapped ids oldest first with their host records
+ * (num_records[i] each, concatenated); free host records front to back. */
+int pa_sched_running(pa_sched* s, int64_t* ids, int32_t* generated, int32_t cap, int32_t* n_out);
+int pa_sched_waiting(pa_sched* s, int64_t* ids, int32_t cap, int32_t* n_out);
+int pa_sched_swapped(pa_sched* s, int64_t* ids, int32_t* num_records, int32_t cap,
+                     int32_t* records, int32_t records_cap, int32_t* n_out);
+int pa_sched_host_free(pa_sched* s, int32_t* records, int32_t cap, int32_t* n_out);
 
 /* ==== device operations (gfx950) ========================================= */
 

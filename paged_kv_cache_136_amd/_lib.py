@@ -40,6 +40,8 @@ SIGNATURES = {
     "pa_bm_is_swapped": (c_i32, [c_vp, c_i64]),
     "pa_bm_swapped": (ctypes.c_int, [c_vp, P_i64, P_i32, c_i32, P_i32]),
     "pa_bm_slot": (ctypes.c_int, [c_vp, c_i64, c_i32, P_i64]),
+    "pa_bm_block_size": (c_i32, [c_vp]),
+    "pa_bm_num_blocks": (c_i32, [c_vp]),
     "pa_bm_num_free_blocks": (c_i32, [c_vp]),
     "pa_bm_can_allocate": (c_i32, [c_vp, c_i32]),
     "pa_bm_num_cached_tokens": (ctypes.c_int, [c_vp, c_i64, P_i32]),
@@ -50,6 +52,15 @@ SIGNATURES = {
     "pa_bm_export_batch": (ctypes.c_int, [c_vp, P_i64, c_i32, P_i32, c_i32, c_i32, P_i32]),
     "pa_bm_check_invariants": (ctypes.c_int, [c_vp]),
     "pa_bm_dump": (ctypes.c_int, [c_vp, P_i32, P_i8, P_i32, P_i32, P_i32, P_i32]),
+    "pa_sched_create": (c_vp, [c_vp, c_i32, c_i32]),
+    "pa_sched_destroy": (None, [c_vp]),
+    "pa_sched_add_request": (ctypes.c_int, [c_vp, c_i64, P_i32, c_i32, c_i32]),
+    "pa_sched_step": (ctypes.c_int, [c_vp, c_vp]),
+    "pa_sched_commit": (ctypes.c_int, [c_vp, P_i64, P_i32, c_i32]),
+    "pa_sched_running": (ctypes.c_int, [c_vp, P_i64, P_i32, c_i32, P_i32]),
+    "pa_sched_waiting": (ctypes.c_int, [c_vp, P_i64, c_i32, P_i32]),
+    "pa_sched_swapped": (ctypes.c_int, [c_vp, P_i64, P_i32, c_i32, P_i32, c_i32, P_i32]),
+    "pa_sched_host_free": (ctypes.c_int, [c_vp, P_i32, c_i32, P_i32]),
     "pa_write_kv": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                    c_i32, c_i32, c_vp]),
     "pa_copy_blocks": (ctypes.c_int, [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_i32, c_i64,

@@ -441,6 +441,9 @@ int pa_bm_slot(const pa_bm* bm, int64_t seq, int32_t pos, int64_t* slot_out) {
   return PA_OK;
 }
 
+int32_t pa_bm_block_size(const pa_bm* bm) { return bm ? bm->bs : -1; }
+int32_t pa_bm_num_blocks(const pa_bm* bm) { return bm ? bm->nb : -1; }
+
 int32_t pa_bm_num_free_blocks(const pa_bm* bm) {
   if (!bm) return -1;
   std::lock_guard<std::mutex> lock(bm->mu);

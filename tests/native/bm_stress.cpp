@@ -5,6 +5,7 @@
 // (all-or-nothing).  Built by tests/test_bm_sanitizers.py with g++ and the
 // address + undefined-behaviour sanitizers; exits non-zero on any failure.
 #include <algorithm>
+#include <map>
 #include <cstdio>
 #include <cstdlib>
 #include <random>
@@ -212,8 +213,86 @@ static void bad_arguments() {
   pa_bm_destroy(bm);
 }
 
+// Continuous-batching scheduler: seeded request streams with commits after
+// every step; the manager's invariants and the host-record count must hold
+// after every step, every request must finish with exactly its budget, and
+// everything must drain back to an empty pool.
+static void run_sched(uint32_t seed, int nb, int bs, int batch, int host, int prefix) {
+  std::mt19937 rng(seed);
+  pa_bm* bm = pa_bm_create(nb, bs, prefix);
+  REQUIRE(bm);
+  pa_sched* s = pa_sched_create(bm, batch, host);
+  REQUIRE(s);
+  const int cap_ids = batch, cap_pairs = std::max(host, 1), cap_pre = nb * bs;
+  std::vector<int64_t> fin(cap_ids), res(cap_ids), adm(cap_ids), pre(cap_ids), rec(cap_ids),
+      pslots(cap_pre), batch_ids(cap_ids), slots(cap_ids);
+  std::vector<int32_t> swin(2 * cap_pairs), swout(2 * cap_pairs), pcnt(cap_ids), cow(2 * cap_ids);
+  pa_sched_plan p{};
+  p.ids_cap = cap_ids; p.pairs_cap = cap_pairs; p.prefill_cap = cap_pre;
+  p.finished = fin.data(); p.resumed = res.data(); p.admitted = adm.data(); p.preempted = pre.data();
+  p.recomputed = rec.data(); p.swap_in = swin.data(); p.swap_out = swout.data();
+  p.prefill_slots = pslots.data(); p.prefill_counts = pcnt.data(); p.batch = batch_ids.data();
+  p.slots = slots.data(); p.cow_pairs = cow.data();
+  pa_sched_plan small = p;
+  small.prefill_cap = cap_pre - 1;
+  REQUIRE(pa_sched_step(s, &small) == PA_ERR_INVALID);          // refused before any change
+  std::map<int64_t, int> budget, produced;
+  int64_t next = 1;
+  long preempted = 0, resumed = 0;
+  const int n_req = 80;
+  for (int step = 0; step < 20000; ++step) {
+    while (next <= n_req && rng() % 10 < 3) {
+      std::vector<int32_t> prompt(1 + rng() % (3 * bs));
+      for (auto& t : prompt) t = rng() % 4;
+      budget[next] = 1 + rng() % (4 * bs);
+      REQUIRE(pa_sched_add_request(s, next, prompt.data(), (int32_t)prompt.size(), budget[next]) == PA_OK);
+      ++next;
+    }
+    REQUIRE(pa_sched_step(s, &p) == PA_OK);
+    if (p.n_batch + p.n_admitted > 0) {                           // tokens owed: commit first
+      pa_sched_plan again = p;
+      REQUIRE(pa_sched_step(s, &again) == PA_ERR_INVALID);
+    }
+    for (int i = 0; i < p.n_finished; ++i) REQUIRE(produced[fin[i]] == budget[fin[i]]);
+    preempted += p.n_preempted;
+    resumed += p.n_resumed;
+    REQUIRE(p.n_batch <= batch && p.n_swap_in <= host && p.n_swap_out <= host);
+    std::vector<int64_t> ids(batch_ids.begin(), batch_ids.begin() + p.n_batch);
+    ids.insert(ids.end(), adm.begin(), adm.begin() + p.n_admitted);
+    std::vector<int32_t> toks(ids.size());
+    for (auto& t : toks) t = rng() % 4;
+    for (int64_t id : ids) ++produced[id];
+    REQUIRE(pa_bm_check_invariants(bm) == PA_OK);
+    int32_t nfree = -1, nswap = -1, nrun = -1, nwait = -1;
+    REQUIRE(pa_sched_host_free(s, nullptr, 0, &nfree) == PA_OK);
+    REQUIRE(pa_sched_swapped(s, nullptr, nullptr, 0, nullptr, 0, &nswap) == PA_OK);
+    std::vector<int64_t> sid(nswap + 1);
+    std::vector<int32_t> scnt(nswap + 1), srec(host + 1);
+    REQUIRE(pa_sched_swapped(s, sid.data(), scnt.data(), nswap, srec.data(), host, &nswap) == PA_OK);
+    int held = 0;
+    for (int i = 0; i < nswap; ++i) held += scnt[i];
+    REQUIRE(held + nfree == host);
+    REQUIRE(pa_sched_running(s, nullptr, nullptr, 0, &nrun) == PA_OK && nrun <= batch);
+    REQUIRE(pa_sched_waiting(s, nullptr, 0, &nwait) == PA_OK);
+    REQUIRE(pa_sched_commit(s, ids.data(), toks.data(), (int32_t)ids.size()) == PA_OK);
+    if (next > n_req && nrun == 0 && nwait == 0 && nswap == 0) break;
+  }
+  REQUIRE((int)produced.size() == n_req);
+  for (auto& kv : budget) REQUIRE(produced[kv.first] == kv.second);
+  REQUIRE(pa_bm_num_free_blocks(bm) == nb && pa_bm_num_seqs(bm) == 0);
+  REQUIRE(preempted > 0);
+  if (host > 0) REQUIRE(resumed > 0);
+  pa_sched_destroy(s);
+  pa_bm_destroy(bm);
+  std::printf("sched seed %u: preempted %ld resumed %ld\n", seed, preempted, resumed);
+}
+
 int main() {
   bad_arguments();
+  run_sched(11, 12, 4, 4, 16, 1);
+  run_sched(12, 10, 2, 5, 6, 1);
+  run_sched(13, 16, 4, 6, 0, 1);
+  run_sched(14, 9, 3, 4, 40, 0);
   run(1, 8, 2, 1, 3, 20000);
   run(2, 12, 4, 1, 2, 20000);
   run(3, 24, 16, 1, 1, 5000);

@@ -1,4 +1,5 @@
-"""The host block manager under AddressSanitizer and UBSan (CPU only).
+"""The host block manager and scheduler under AddressSanitizer and UBSan
+(CPU only).
 
 tests/native/bm_stress.cpp drives the C ABI with seeded random operation
 streams, checks the P06 invariants after every operation and the full dump
@@ -24,7 +25,8 @@ def test_block_manager_under_sanitizers(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(ROOT, "tests", "native", "bm_stress.cpp"),
-           os.path.join(CSRC, "block_manager.cpp"), os.path.join(CSRC, "status.cpp"),
+           os.path.join(CSRC, "block_manager.cpp"), os.path.join(CSRC, "scheduler.cpp"),
+           os.path.join(CSRC, "status.cpp"),
            "-o", str(exe)]
     build = subprocess.run(cmd, capture_output=True, text=True)
     assert build.returncode == 0, build.stderr
