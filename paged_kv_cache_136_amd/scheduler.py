@@ -11,6 +11,24 @@ import numpy as np
 from ._lib import P_i32, P_i64, check, lib
 
 
+def plan_lists(a):
+    """A plan from step_arrays() as plain lists (pairs as tuples, prompt
+    slots grouped per admitted request)."""
+    prefill, o = [], 0
+    for rid, n in zip(a["admitted"].tolist(), a["prefill_counts"].tolist()):
+        prefill.append((rid, a["prefill_slots"][o:o + n].tolist()))
+        o += n
+    return {
+        "finished": a["finished"].tolist(), "resumed": a["resumed"].tolist(),
+        "admitted": a["admitted"].tolist(), "preempted": a["preempted"].tolist(),
+        "recomputed": a["recomputed"].tolist(),
+        "swap_in": [tuple(x) for x in a["swap_in"].tolist()],
+        "swap_out": [tuple(x) for x in a["swap_out"].tolist()], "prefill": prefill,
+        "batch": a["batch"].tolist(), "slots": a["slots"].tolist(),
+        "cow": [tuple(x) for x in a["cow"].tolist()],
+    }
+
+
 class Plan(ctypes.Structure):
     """Mirror of pa_sched_plan (field order and types as in pagedkv.h)."""
     _fields_ = [
@@ -92,20 +110,7 @@ class Scheduler:
     def step(self):
         """Run one step; returns the plan with the oracle scheduler's keys
         and list values (parity tests)."""
-        a = self.step_arrays()
-        prefill, o = [], 0
-        for rid, n in zip(a["admitted"].tolist(), a["prefill_counts"].tolist()):
-            prefill.append((rid, a["prefill_slots"][o:o + n].tolist()))
-            o += n
-        return {
-            "finished": a["finished"].tolist(), "resumed": a["resumed"].tolist(),
-            "admitted": a["admitted"].tolist(), "preempted": a["preempted"].tolist(),
-            "recomputed": a["recomputed"].tolist(),
-            "swap_in": [tuple(x) for x in a["swap_in"].tolist()],
-            "swap_out": [tuple(x) for x in a["swap_out"].tolist()], "prefill": prefill,
-            "batch": a["batch"].tolist(), "slots": a["slots"].tolist(),
-            "cow": [tuple(x) for x in a["cow"].tolist()],
-        }
+        return plan_lists(self.step_arrays())
 
     def commit(self, tokens):
         """{request id: token} for every request of the last step's batch

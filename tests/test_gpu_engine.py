@@ -1,0 +1,131 @@
+"""GPU parity of the continuous-batching loop ("qaqbuyan.com article 130",
+continuous-batching section): the library's scheduler driving the device
+calls, against the oracle scheduler driving the oracle's copies and
+float64 decode, step by step.
+
+Every step's plan must be identical, every cache byte bit-exact after the
+step, and every layer's decode output within the attention tolerance.
+Requests share prompt prefixes (prefix hits), the pool is small enough to
+force preemption, and the host swap pool is either roomy (swap-out/in) or
+absent (recompute).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, make_cache, say
+
+pytestmark = pytest.mark.gpu
+
+pkv = pytest.importorskip("paged_kv_cache_136_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(t):
+    return t.detach().contiguous().view(torch.int16).cpu().numpy()
+
+
+@pytest.mark.parametrize("host", [24, 0])
+def test_serve_loop_matches_oracle(host):
+    from paged_kv_cache_136_amd.engine import DecodeEngine
+    from paged_kv_cache_136_amd.scheduler import plan_lists
+    L, nb, bs, hkv, hq, d, batch = 2, 20, 16, 2, 4, 64, 6
+    say("serve loop host", host)
+    ks, vs = zip(*[make_cache(nb, bs, hkv, d, "f16", seed=700 + 2 * i) for i in range(L)])
+    eng = DecodeEngine(L, nb, bs, hkv, hq, d, torch.float16, batch, host, True,
+                       partition_tokens=64, caches=(list(ks), list(vs)))
+    rbm = oracle.RefBlockManager(nb, bs, True)
+    rsc = oracle.RefScheduler(rbm, batch, host)
+    kb, vb = [_bits(k) for k in ks], [_bits(v) for v in vs]
+    hrec = np.zeros((max(host, 1), L, 2, bs, hkv, d), dtype=np.int16)
+
+    rng = np.random.default_rng(3)
+    system = workloads.token_ids(40, seed=77)
+    for rid in range(1, 25):
+        own = workloads.token_ids(int(rng.integers(1, 60)), seed=800 + rid)
+        prompt = (system[:int(rng.choice([0, 16, 33, 40]))] + own)
+        budget = int(rng.integers(5, 70))
+        eng.add_request(rid, prompt, budget)
+        rsc.add_request(rid, prompt, budget)
+
+    rows = {}
+
+    def kv_rows(layer, kind, plan):
+        n = len(plan["prefill_slots"]) if kind == "prefill" else len(plan["batch"])
+        seed = 100_000 * eng.step_no + 10 * layer + (0 if kind == "prefill" else 5)
+        k = workloads.normal_torch((n, hkv, d), seed, torch.float16, "cuda")
+        v = workloads.normal_torch((n, hkv, d), seed + 1, torch.float16, "cuda")
+        rows[(layer, kind)] = (k, v)
+        return k, v
+
+    def q_rows(layer, plan):
+        q = workloads.normal_torch((len(plan["batch"]), hq, d), 100_000 * eng.step_no + 10 * layer + 7,
+                                   torch.float16, "cuda")
+        rows[(layer, "q")] = q
+        return q
+
+    def sample(owed, outs):
+        return {i: (i * 131 + eng.step_no) % 50 for i in owed}
+
+    seen = {"preempted": 0, "recomputed": 0, "resumed": 0, "hits": 0}
+    for step in range(1, 600):
+        rows.clear()
+        plan_arrays, outs = eng.step(kv_rows, q_rows, sample)
+        got = plan_lists(plan_arrays)
+        want = rsc.step()
+        assert got == want, step
+        for key in ("preempted", "recomputed", "resumed"):
+            seen[key] += len(want[key])
+        seen["hits"] += sum(rbm.num_cached_tokens(r) > 0 for r in want["admitted"])
+        # The oracle applies the same device work, in the same order.
+        if want["swap_in"]:
+            recs, blocks = zip(*want["swap_in"])
+            oracle.ref_swap_in(kb, vb, blocks, hrec[list(recs)], inplace=True)
+        if want["prefill"]:
+            slots = [s for _, ss in want["prefill"] for s in ss]
+            for layer in range(L):
+                k, v = rows[(layer, "prefill")]
+                oracle.ref_write_kv(kb[layer], vb[layer], _bits(k), _bits(v), slots, inplace=True)
+        if want["swap_out"]:
+            blocks, recs = zip(*want["swap_out"])
+            hrec[list(recs)] = oracle.ref_swap_out(kb, vb, blocks)
+        if want["cow"]:
+            oracle.ref_copy_blocks(kb, vb, want["cow"], inplace=True)
+        if want["batch"]:
+            tables, lens = eng.bm.export_batch(want["batch"], max(-(-rbm.seq_len(i) // bs) for i in want["batch"]), 0)
+            assert lens.tolist() == [rbm.seq_len(i) for i in want["batch"]]
+            assert all(rbm.get_table(i) == tables[j, :len(rbm.get_table(i))].tolist()
+                       for j, i in enumerate(want["batch"]))
+            for layer in range(L):
+                k, v = rows[(layer, "decode")]
+                oracle.ref_write_kv(kb[layer], vb[layer], _bits(k), _bits(v), want["slots"], inplace=True)
+                ref = oracle.ref_decode(_bits(rows[(layer, "q")]).view(np.float16),
+                                        kb[layer].view(np.float16), vb[layer].view(np.float16),
+                                        tables, lens)
+                err = np.abs(outs[layer].cpu().numpy() - ref).max()
+                assert err <= TOL["f16"], (step, layer, err)
+        for layer in range(L):
+            assert np.array_equal(_bits(eng.k[layer]), kb[layer]), (step, layer)
+            assert np.array_equal(_bits(eng.v[layer]), vb[layer]), (step, layer)
+        rsc.commit(sample(want["batch"] + want["admitted"], None))
+        if eng.idle():
+            break
+    else:
+        raise AssertionError("the loop did not drain")
+    assert seen["preempted"] > 0 and seen["hits"] > 0
+    if host:
+        assert seen["resumed"] > 0
+    else:
+        assert seen["recomputed"] > 0
+    assert eng.bm.num_free_blocks == nb

@@ -81,6 +81,40 @@ def test_swap_out_in_bitexact(dtype, L, hkv, d):
         assert np.array_equal(_bits(ks[i]), before[i])
 
 
+def test_swap_through_host_record_slots():
+    """Entries go to (and come back from) scattered records of a swap pool;
+    a record index outside the pool is skipped."""
+    nb, bs, hkv, d, L = 24, 16, 2, 64, 2
+    say("swap host slots")
+    ks, vs = zip(*[make_cache(nb, bs, hkv, d, "bf16", seed=150 + 2 * i) for i in range(L)])
+    rec = pkv.swap_record_bytes(ks)
+    pool = _pinned(6 * rec)
+    pool.fill_(0x5A)
+    blocks = np.array([3, 17, 9, 0, 11], dtype=np.int32)
+    slots = np.array([4, 0, 5, 6, 2], dtype=np.int32)          # 6 is outside the 6-record pool
+    kb, vb = [_bits(k) for k in ks], [_bits(v) for v in vs]
+    pkv.pa_swap_out(ks, vs, torch.from_numpy(blocks).cuda(), pool,
+                    host_slots=torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    got = pool.numpy().view(np.int16).reshape((6, L, 2) + kb[0].shape[1:])
+    want = oracle.ref_swap_out(kb, vb, blocks)
+    for i, r in enumerate(slots):
+        if r < 6:
+            assert np.array_equal(got[r], want[i])
+    untouched = np.full(rec, 0x5A, dtype=np.uint8).view(np.int16).reshape(got.shape[1:])
+    for r in (1, 3):
+        assert np.array_equal(got[r], untouched)
+    # Back from records 2, 4, 0 into blocks 20, 21, 22.
+    back = np.array([20, 21, 22], dtype=np.int32)
+    recs = np.array([2, 4, 0], dtype=np.int32)
+    want_k, want_v = oracle.ref_swap_in(kb, vb, back, got[recs])
+    pkv.pa_swap_in(ks, vs, torch.from_numpy(back).cuda(), pool, host_slots=torch.from_numpy(recs).cuda())
+    torch.cuda.synchronize()
+    for i in range(L):
+        assert np.array_equal(_bits(ks[i]), want_k[i])
+        assert np.array_equal(_bits(vs[i]), want_v[i])
+
+
 def test_swap_rejects_unmapped_or_short_host_buffers():
     """Host buffers the GPU cannot address, or that are too short, are
     refused before anything is launched (the caches stay untouched)."""
@@ -101,7 +135,7 @@ def test_swap_rejects_unmapped_or_short_host_buffers():
     kp = (ctypes.c_void_p * 1)(k.data_ptr())
     vp = (ctypes.c_void_p * 1)(v.data_ptr())
     dev_buf = torch.empty(2 * rec, dtype=torch.uint8, device="cuda")
-    st = lib.pa_swap_out(kp, vp, 1, rec // 2, nb, blocks.data_ptr(), 2, dev_buf.data_ptr(),
+    st = lib.pa_swap_out(kp, vp, 1, rec // 2, nb, blocks.data_ptr(), None, 2, dev_buf.data_ptr(),
                          2 * rec, None)
     assert st == 2 and b"pinned" in lib.pa_last_error()     # device memory is not a host record
     torch.cuda.synchronize()
