@@ -16,6 +16,8 @@ device computes comes from the library's kernels.  The step ends with a
 stream synchronization, as a sampler reading the outputs would.
 """
 
+import time
+
 import numpy as np
 import torch
 
@@ -49,6 +51,7 @@ class DecodeEngine:
                                 pin_memory=True)
         self.ws = None                   # decode workspace, grown on demand
         self.step_no = 0
+        self.host_seconds = 0.0          # time in scheduler / block-manager calls
 
     def add_request(self, rid, prompt, max_new_tokens):
         self.sched.add_request(rid, prompt, max_new_tokens)
@@ -67,7 +70,9 @@ class DecodeEngine:
         requests) given the per-layer float32 decode outputs [B, Hq, D].
         Returns (plan, outs)."""
         self.step_no += 1
+        h0 = time.perf_counter()
         plan = self.sched.step_arrays()
+        self.host_seconds += time.perf_counter() - h0
         # 1. swap-in copies
         if len(plan["swap_in"]):
             pa_swap_in(self.k, self.v, self._i32(plan["swap_in"][:, 1]), self.host,
@@ -91,7 +96,9 @@ class DecodeEngine:
         if len(ids):
             B = len(ids)
             slots = torch.from_numpy(plan["slots"].copy()).to(self.dev)
+            h0 = time.perf_counter()
             tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
+            self.host_seconds += time.perf_counter() - h0
             max_len = int(lens.max())
             d_tab = torch.from_numpy(tables).to(self.dev)
             d_len = torch.from_numpy(lens).to(self.dev)
@@ -106,7 +113,10 @@ class DecodeEngine:
                                       workspace=self.ws))
         torch.cuda.current_stream().synchronize()
         owed = ids.tolist() + plan["admitted"].tolist()
-        self.sched.commit(sample(owed, outs))
+        toks = sample(owed, outs)
+        h0 = time.perf_counter()
+        self.sched.commit(toks)
+        self.host_seconds += time.perf_counter() - h0
         return plan, outs
 
     def _table_width(self, ids):
