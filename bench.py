@@ -43,7 +43,7 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixed_7b",
-                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap", "serve"],
+                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap", "serve", "beam"],
                    help="mixed_7b is the headline workload; the others are reported lines")
     p.add_argument("--partition-tokens", type=int, default=-1,
                    help="split-KV partition size (default: the workload's, 512)")
@@ -588,6 +588,122 @@ def run_serve(args, torch, pkv, workloads):
     }
 
 
+def run_beam(args, torch, pkv, workloads):
+    """Beam search: 64 prompts (lengths log-uniform in [50, 2048], prefix
+    cache on), 8 beams each, one layer of 32 KV heads x 128, fp16.  Every
+    step each group's 8 beams are re-forked from seeded parents at their
+    current (arbitrary) positions, the old beams freed, and all 512 beams
+    append a token: beams sharing a partly filled last block copy it
+    (pa_copy_blocks with many small pairs), then pa_write_kv and pa_decode
+    over the 512 beams.  Reported: step rate, copy pairs per step and the
+    copy kernel's rate, decode KV GB/s (logical and over unique blocks)."""
+    cfg = workloads.CONFIGS["beam"]
+    bs, NB, H, D, G, W = cfg["bs"], cfg["num_blocks"], cfg["hkv"], cfg["d"], cfg["groups"], cfg["beams"]
+    dev = torch.device("cuda:0")
+    bm = pkv.BlockManager(NB, bs, True)
+    k = workloads.normal_torch((NB, bs, H, D), 70, torch.float16, dev)
+    v = workloads.normal_torch((NB, bs, H, D), 71, torch.float16, dev)
+    lens0 = workloads.mixed_lengths(G, cfg["len_lo"], cfg["len_hi"], seed=7)
+    beams, nid = [], 1
+    for g in range(G):
+        bm.allocate(nid, workloads.token_ids(int(lens0[g]), seed=5000 + g))
+        beams.append([nid] * W)
+        nid += 1
+    B = G * W
+    rng = np.random.default_rng(8)
+    kn = workloads.normal_torch((B, H, D), 72, torch.float16, dev)
+    vn = workloads.normal_torch((B, H, D), 73, torch.float16, dev)
+    q = workloads.normal_torch((B, cfg["hq"], D), 74, torch.float16, dev)
+    out = torch.empty((B, cfg["hq"], D), dtype=torch.float32, device=dev)
+    maxlen = int(lens0.max()) + args.warmup + args.steps + 1
+    ws = torch.empty(max(pkv.pa_decode_workspace_bytes(B, cfg["hq"], D, maxlen, 512), 1),
+                     dtype=torch.uint8, device=dev)
+    width = -(-maxlen // bs)
+    T = torch.cuda.Event
+
+    def step(ev=None):
+        nonlocal beams, nid
+        h0 = time.perf_counter()
+        par, kid, old, new = [], [], [], []
+        for grp in beams:
+            ks = []
+            for p in workloads.beam_parents(rng, W):
+                par.append(grp[p])
+                kid.append(nid)
+                ks.append(nid)
+                nid += 1
+            new.append(ks)
+            old += sorted(set(grp))
+        bm.fork_batch(par, kid)
+        bm.free_batch(old)
+        beams = new
+        flat = np.array([s for g in beams for s in g], dtype=np.int64)
+        slots, pairs = bm.append_slots(flat, np.arange(B, dtype=np.int32))
+        tables, lens = bm.export_batch(flat, width, pad_block=0)
+        host = time.perf_counter() - h0
+        d_slot = torch.from_numpy(slots).to(dev)
+        d_pairs = torch.from_numpy(pairs).to(dev) if len(pairs) else None
+        d_tab = torch.from_numpy(tables).to(dev)
+        d_len = torch.from_numpy(lens).to(dev)
+        if ev is not None:
+            ev[0].record()
+        if d_pairs is not None:
+            pkv.pa_copy_blocks([k], [v], d_pairs)
+        if ev is not None:
+            ev[1].record()
+        pkv.pa_write_kv(k, v, kn, vn, d_slot)
+        if ev is not None:
+            ev[2].record()
+        pkv.pa_decode(q, k, v, d_tab, d_len, int(lens.max()), partition_tokens=512, out=out,
+                      workspace=ws)
+        if ev is not None:
+            ev[3].record()
+        uniq = len(np.unique(np.concatenate([tables[i, :-(-int(n) // bs)] for i, n in enumerate(lens)])))
+        return len(pairs), int(lens.sum()), uniq, host
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[T(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    info = []
+    t0 = time.perf_counter()
+    for e in evs:
+        info.append(step(e))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    copy_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    npairs = np.array([x[0] for x in info])
+    toks = np.array([x[1] for x in info], dtype=np.float64)
+    uniq = np.array([x[2] for x in info], dtype=np.float64)
+    per_tok = 2 * H * D * 2
+    block_kv = 2 * k[0].numel() * 2
+    copied = npairs * block_kv * 2              # read + write
+    with_pairs = npairs > 0
+    return {
+        "metric": "beam search over the paged cache: decode KV GB/s and beams/s",
+        "value": round(float(toks.sum() * per_tok / (step_ms.sum() * 1e-3) / 1e9), 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(float(step_ms.mean()), 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "beam", "groups": G, "beams": W, "prompt_lengths": "log-uniform [50, 2048], seed 7",
+                   "kv_heads": H, "q_heads": cfg["hq"], "head_dim": D, "block_size": bs, "num_blocks": NB,
+                   "partition_tokens": 512,
+                   "timing": "GPU events per step (COW copies + write + decode); value counts every "
+                             "beam's tokens (shared blocks once per beam)"},
+        "beams_per_s": round(B * args.steps / (step_ms.sum() * 1e-3), 1),
+        "unique_kv_gbs": round(float(uniq.sum() * bs * per_tok / (dec_ms.sum() * 1e-3) / 1e9), 2),
+        "cow_pairs_per_step": round(float(npairs.mean()), 1),
+        "copy_ms_per_step": round(float(copy_ms.mean()), 4),
+        "copy_gbs": round(float(copied[with_pairs].sum() / (copy_ms[with_pairs].sum() * 1e-3) / 1e9), 2)
+        if with_pairs.any() else None,
+        "decode_ms_per_step": round(float(dec_ms.mean()), 4),
+        "host_ms_per_step": round(float(np.mean([x[3] for x in info]) * 1e3), 4),
+        "roofline": None, "cpu_baseline": None, "wall_s": round(wall, 3),
+    }
+
+
 LENGTH_NOTES = {
     "mixed_7b": "log-uniform [50, 4096], PCG64 seed 0, +1 token per step",
     "13b_layer": "10 x 4096, +1 token per step",
@@ -619,6 +735,8 @@ def main():
         result = run_swap(args, torch, pkv, workloads)
     elif args.workload == "serve":
         result = run_serve(args, torch, pkv, workloads)
+    elif args.workload == "beam":
+        result = run_beam(args, torch, pkv, workloads)
     else:
         wb = DecodeBench(args.workload, args, torch, pkv, workloads)
         result = wb.run()

@@ -142,6 +142,16 @@ int pa_bm_append_slots(pa_bm* bm, const int64_t* seqs, const int32_t* tokens, in
  * needs a block.  PA_ERR_INVALID if parent is unknown or child exists. */
 int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child);
 
+/* pa_bm_fork(parents[i], children[i]) for i in [0, n), in order, under one
+ * lock (beam search forks every beam each step).  Stops at the first
+ * failing fork and returns its status; *n_done_out (if not NULL) is the
+ * number of forks done, which stay done. */
+int pa_bm_fork_batch(pa_bm* bm, const int64_t* parents, const int64_t* children, int32_t n,
+                     int32_t* n_done_out);
+
+/* pa_bm_free of seqs[0..n) in order, under one lock.  Never fails on ids. */
+int pa_bm_free_batch(pa_bm* bm, const int64_t* seqs, int32_t n);
+
 /* [P06] operations table, free row: reverse walk, ref-1, blocks at 0 to the
  * evictable pool (hashed) or free list (not hashed); the sequence's records
  * are dropped.  Never fails; an unknown seq is a no-op returning PA_OK. */

@@ -35,6 +35,8 @@ SIGNATURES = {
     "pa_bm_append_slots": (ctypes.c_int, [c_vp, P_i64, P_i32, c_i32, P_i64, P_i32, P_i32, P_i32]),
     "pa_bm_fork": (ctypes.c_int, [c_vp, c_i64, c_i64]),
     "pa_bm_free": (ctypes.c_int, [c_vp, c_i64]),
+    "pa_bm_fork_batch": (ctypes.c_int, [c_vp, P_i64, P_i64, c_i32, P_i32]),
+    "pa_bm_free_batch": (ctypes.c_int, [c_vp, P_i64, c_i32]),
     "pa_bm_swap_out": (ctypes.c_int, [c_vp, c_i64, P_i32, c_i32, P_i32]),
     "pa_bm_swap_in": (ctypes.c_int, [c_vp, c_i64, P_i32, c_i32, P_i32, P_i32]),
     "pa_bm_is_swapped": (c_i32, [c_vp, c_i64]),

@@ -75,6 +75,19 @@ class BlockManager:
     def free(self, seq):
         check(lib().pa_bm_free(self._h, int(seq)))
 
+    def fork_batch(self, parents, children):
+        """fork(parents[i], children[i]) in order under one lock."""
+        p = np.ascontiguousarray(parents, dtype=np.int64)
+        c = np.ascontiguousarray(children, dtype=np.int64)
+        assert p.shape == c.shape
+        check(lib().pa_bm_fork_batch(self._h, p.ctypes.data_as(P_i64), c.ctypes.data_as(P_i64),
+                                     len(p), None))
+
+    def free_batch(self, seqs):
+        """free(s) for every s, in order, under one lock."""
+        a = np.ascontiguousarray(seqs, dtype=np.int64)
+        check(lib().pa_bm_free_batch(self._h, a.ctypes.data_as(P_i64), len(a)))
+
     def swap_out(self, seq):
         """Preempt ``seq``: returns its table (the blocks whose bytes go to
         host memory, logical order) and frees them; the tokens are kept."""

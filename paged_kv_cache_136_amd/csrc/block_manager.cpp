@@ -349,6 +349,44 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
   return PA_OK;
 }
 
+int pa_bm_fork_batch(pa_bm* bm, const int64_t* parents, const int64_t* children, int32_t n,
+                     int32_t* n_done_out) {
+  if (!bm || n < 0 || (n > 0 && (!parents || !children)))
+    return fail(PA_ERR_INVALID, "pa_bm_fork_batch: bad arguments");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  int32_t done = 0;
+  int st = PA_OK;
+  for (; done < n; ++done) {
+    auto it = bm->seqs.find(parents[done]);
+    if (it == bm->seqs.end()) { st = fail(PA_ERR_INVALID, "pa_bm_fork_batch: unknown parent"); break; }
+    if (bm->seqs.count(children[done]) || bm->swapped.count(children[done])) {
+      st = fail(PA_ERR_INVALID, "pa_bm_fork_batch: child exists");
+      break;
+    }
+    Seq s = it->second;
+    for (int32_t b : s.table) ++bm->ref[b];
+    bm->seqs.emplace(children[done], std::move(s));
+  }
+  if (n_done_out) *n_done_out = done;
+  if (st == PA_OK) pkv::clear_error();
+  return st;
+}
+
+int pa_bm_free_batch(pa_bm* bm, const int64_t* seqs, int32_t n) {
+  if (!bm || n < 0 || (n > 0 && !seqs)) return fail(PA_ERR_INVALID, "pa_bm_free_batch: bad arguments");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  for (int32_t i = 0; i < n; ++i) {
+    bm->swapped.erase(seqs[i]);
+    auto it = bm->seqs.find(seqs[i]);
+    if (it != bm->seqs.end()) {
+      bm->free_seq(it->second);
+      bm->seqs.erase(it);
+    }
+  }
+  pkv::clear_error();
+  return PA_OK;
+}
+
 int pa_bm_free(pa_bm* bm, int64_t seq) {
   if (!bm) return fail(PA_ERR_INVALID, "pa_bm_free: null manager");
   std::lock_guard<std::mutex> lock(bm->mu);

@@ -107,9 +107,17 @@ static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops
       if (st != PA_OK) ++oob;
     } else if (r < 65) {
       int64_t p = live[rng() % live.size()];
-      REQUIRE(pa_bm_fork(bm, p, next) == PA_OK);
-      REQUIRE(pa_bm_fork(bm, p, next) == PA_ERR_INVALID);   // child exists
-      live.push_back(next++);
+      if (rng() % 2) {
+        REQUIRE(pa_bm_fork(bm, p, next) == PA_OK);
+        REQUIRE(pa_bm_fork(bm, p, next) == PA_ERR_INVALID);   // child exists
+        live.push_back(next++);
+      } else {                                                 // batched, last one fails
+        int64_t par[3] = {p, p, p}, kid[3] = {next, next + 1, next};
+        int32_t done = -1;
+        REQUIRE(pa_bm_fork_batch(bm, par, kid, 3, &done) == PA_ERR_INVALID && done == 2);
+        live.push_back(next++);
+        live.push_back(next++);
+      }
     } else if (r < 71) {
       // preempt: swap out, with a too-small table first (must change nothing)
       size_t i = rng() % live.size();
@@ -158,7 +166,12 @@ static void run(uint32_t seed, int nb, int bs, int prefix, int alphabet, int ops
       }
     } else if (r < 92) {
       size_t i = rng() % live.size();
-      REQUIRE(pa_bm_free(bm, live[i]) == PA_OK);
+      if (rng() % 2) {
+        REQUIRE(pa_bm_free(bm, live[i]) == PA_OK);
+      } else {
+        int64_t ids[2] = {live[i], -12345};
+        REQUIRE(pa_bm_free_batch(bm, ids, 2) == PA_OK);
+      }
       live.erase(live.begin() + i);
     } else {
       // export a random subset with a table width that may be too small

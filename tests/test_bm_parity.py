@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from paged_kv_cache_136_amd import BlockManager, OutOfBlocks
+from paged_kv_cache_136_amd import BlockManager, OutOfBlocks, PagedKVError
 from tests.bm_steps import run_steps
 from tests.test_oracle_block_manager import GOLDEN_SCRIPTS
 
@@ -184,3 +184,64 @@ def test_large_prompt_hits():
         bm.allocate(3, prompt)
     assert a.dump() == b.dump()
     assert a.num_cached_tokens(2) == 2048 and a.num_cached_tokens(3) == 2032
+
+
+def beam_flow(bm_lib, bm_ref, rng, prompts, W, steps, alphabet=9):
+    """Beam search on both managers: every step each group's W beams are
+    re-forked from seeded parents (batched on the library side), the old
+    beams freed, and every new beam appends (copy-on-write on shared partly
+    filled blocks).  Returns the COW pair count."""
+    beams, nid, cows = [], 1, 0
+    for g, toks in enumerate(prompts):
+        assert bm_lib.allocate(nid, toks) == bm_ref.allocate(nid, toks)
+        beams.append([nid] * W)          # W identical parents at the start
+        nid += 1
+    for _ in range(steps):
+        par, kid, old, new = [], [], [], []
+        for grp in beams:
+            ks = []
+            for p in workloads.beam_parents(rng, W):
+                par.append(grp[p])
+                kid.append(nid)
+                ks.append(nid)
+                nid += 1
+            new.append(ks)
+            old += sorted(set(grp))
+        bm_lib.fork_batch(par, kid)
+        for p, c in zip(par, kid):
+            bm_ref.fork(p, c)
+        bm_lib.free_batch(old)
+        for s in old:
+            bm_ref.free(s)
+        beams = new
+        flat = [s for g in beams for s in g]
+        toks = rng.integers(0, alphabet, len(flat))
+        slots, pairs = bm_lib.append_slots(flat, toks)
+        want = [bm_ref.append_slot(s, int(t)) for s, t in zip(flat, toks)]
+        assert slots.tolist() == [w[0] for w in want]
+        assert [tuple(p) for p in pairs.tolist()] == [w[1] for w in want if w[1]]
+        assert bm_lib.dump() == bm_ref.dump()
+        bm_lib.check_invariants()
+        cows += len(pairs)
+    return cows, beams
+
+
+def test_beam_flow_batched_fork_free():
+    rng = np.random.default_rng(0)
+    prompts = [list(range(100 * g, 100 * g + n)) for g, n in enumerate([5, 9, 12, 1])]
+    cows, beams = beam_flow(BlockManager(96, 4, True), oracle.RefBlockManager(96, 4, True),
+                            rng, prompts, W=3, steps=14)
+    assert cows > 0
+
+
+def test_fork_free_batch_errors():
+    bm = BlockManager(8, 4, True)
+    bm.allocate(1, [1, 2, 3])
+    with pytest.raises(PagedKVError):
+        bm.fork_batch([1, 1, 5], [2, 3, 4])        # 5 unknown: the first two stay done
+    assert bm.seq_ids() == [1, 2, 3]
+    with pytest.raises(PagedKVError):
+        bm.fork_batch([1], [2])                    # child exists
+    bm.free_batch([3, 99, 2])                      # unknown ids are no-ops
+    assert bm.seq_ids() == [1]
+    bm.check_invariants()

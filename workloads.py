@@ -19,6 +19,10 @@ Workloads (sizes as the pages give them; see the design notes for sources):
   fp16, 20480-block pool.
 * ``gqa_long``  -- 32 query / 8 KV heads x 128, bf16, 32 sequences x 32768,
   131072-block pool, 512-token split-KV partitions.
+* ``beam``      -- beam search ("day31" fork + COW at arbitrary positions):
+  64 prompts with lengths log-uniform in [50, 2048], 8 beams each, every
+  step each beam's continuation picks a parent beam; 32 heads x 128, fp16,
+  20480-block pool.
 """
 
 import numpy as np
@@ -39,6 +43,9 @@ CONFIGS = {
     "gqa_long": dict(layers=1, lens=[32768] * 32, hq=32, hkv=8, d=128,
                      dtype="bf16", bs=16, num_blocks=131072,
                      prefix_cache=False, partition_tokens=512),
+    "beam": dict(layers=1, groups=64, beams=8, len_lo=50, len_hi=2048, hq=32, hkv=32,
+                 d=128, dtype="f16", bs=16, num_blocks=20480, prefix_cache=True,
+                 partition_tokens=512),
 }
 
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -95,3 +102,10 @@ def normal_torch(shape, seed, dtype, device):
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return torch.randn(shape, generator=g, device=device, dtype=dtype)
+
+
+def beam_parents(rng, beams):
+    """Parents of the next ``beams`` beams of one group: a seeded draw with
+    replacement, sorted (a stand-in for top-k selection; some beams get
+    several children, some none)."""
+    return np.sort(rng.integers(0, beams, size=beams))
