@@ -30,7 +30,8 @@ Modules:
   ``ref_swap_out``, ``ref_swap_in``.
 * :mod:`oracle.scheduler`     -- ``RefScheduler`` (article-130 continuous
   batching with preemption over ``RefBlockManager``).
-* :mod:`oracle.attention`     -- ``ref_decode`` (fp64 gather + softmax attention).
+* :mod:`oracle.attention`     -- ``ref_decode`` (fp64 gather + softmax attention)
+  and ``ref_prefill`` (causal attention of an uncached suffix).
 * :mod:`oracle.arithmetic`    -- the pages' memory formulas.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
@@ -41,7 +42,7 @@ observable) -- parity unpinned for those values by design.
 
 from .arithmetic import (block_bytes, blocks_needed, contiguous_tables,
                          kv_bytes_per_token, kv_cache_bytes, tail_waste_tokens)
-from .attention import ref_decode, ref_decode_one
+from .attention import ref_decode, ref_decode_one, ref_prefill
 from .block_manager import OutOfBlocks, RefBlockManager
 from .kv_ops import ref_copy_blocks, ref_swap_in, ref_swap_out, ref_write_kv
 from .scheduler import RefScheduler
@@ -49,7 +50,7 @@ from .scheduler import RefScheduler
 __all__ = [
     "OutOfBlocks", "RefBlockManager", "ref_write_kv", "ref_copy_blocks",
     "ref_swap_out", "ref_swap_in", "RefScheduler",
-    "ref_decode", "ref_decode_one", "kv_cache_bytes",
+    "ref_decode", "ref_decode_one", "ref_prefill", "kv_cache_bytes",
     "kv_bytes_per_token", "block_bytes", "blocks_needed", "tail_waste_tokens",
     "contiguous_tables",
 ]

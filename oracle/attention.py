@@ -19,6 +19,9 @@ Readings:
 * A sequence with context length 0 has nothing to attend to; its output is 0.
 * Inputs of any float dtype are converted exactly to float64; all arithmetic
   is float64.
+* ``ref_prefill`` (the uncached suffix after a prefix hit) is the same
+  attention once per suffix token, each over the tokens up to and including
+  its own position.
 """
 
 import numpy as np
@@ -70,3 +73,44 @@ def ref_decode(q, k_cache, v_cache, block_tables, context_lens, scale=None):
                                        n, h // group, scale)
     return out
 
+
+
+def ref_prefill(q, k_cache, v_cache, block_tables, query_lens, context_lens, scale=None):
+    """Attention of a sequence's uncached suffix over its paged K/V, float64.
+
+    "P06 · BlockManager" spec overview and key-question answers: a prompt
+    whose first ``num_cached_tokens`` tokens are prefix hits needs a forward
+    pass only for the rest -- at least its last token, whose output yields
+    the next token.  "qaqbuyan.com article 130", system-prompt section: a
+    later request reuses the shared prompt's blocks and computes only what
+    follows them.  Each suffix token attends to every earlier token and to
+    itself (causal), through the block table, with the suffix's own K/V
+    already in the cache.
+
+    q:            [T, Hq, D], the suffix tokens of all sequences, sequence
+                  after sequence (query_lens[b] rows each)
+    query_lens:   [B] suffix length q_b of each sequence
+    context_lens: [B] total length n_b (prefix + suffix); query row i of
+                  sequence b is the token at position n_b - q_b + i
+    Returns float64 [T, Hq, D].
+    """
+    q = np.asarray(q)
+    T, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    assert hq % hkv == 0
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    assert int(np.sum(query_lens)) == T
+    out = np.zeros((T, hq, d), dtype=np.float64)
+    row = 0
+    for b in range(len(query_lens)):
+        qb, n = int(query_lens[b]), int(context_lens[b])
+        assert 0 <= qb <= n
+        for i in range(qb):
+            pos = n - qb + i
+            for h in range(hq):
+                out[row + i, h] = ref_decode_one(q[row + i, h], k_cache, v_cache, block_tables[b],
+                                                 pos + 1, h // group, scale)
+        row += qb
+    return out
