@@ -369,6 +369,34 @@ int pa_swap_in(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                const int32_t* host_slots, int32_t n, const void* host_src, int64_t host_bytes,
                void* stream);
 
+/* Prefill attention of uncached suffixes ([P06] spec overview and
+ * key-question answers: after num_cached_tokens prefix hits only the rest
+ * of a prompt needs a forward pass; [A130] system-prompt section: a request
+ * reuses the shared prompt's blocks and computes what follows).  Sequence
+ * b has total length n = context_lens[b] and suffix rows query_start[b] ..
+ * query_start[b+1]-1 of q (q_b rows); row i of it sits at position
+ * n - q_b + i and attends causally to tokens 0 .. n - q_b + i through the
+ * block table, its own K/V already written (pa_write_kv):
+ *   out[row][h] = softmax_t(scale * <q[row][h], K[slot(b,t)][g]>) V,
+ *   t <= position, g = h / (num_q_heads / num_kv_heads).
+ *   out:  device float32 [num_tokens][num_q_heads][head_dim] (written).
+ *   q:    device [num_tokens][num_q_heads][head_dim] in `dtype`.
+ *   k_cache, v_cache, block_tables, context_lens: as in pa_decode.
+ *   query_start: device int32 [B+1], nondecreasing, query_start[B] <=
+ *     num_tokens; max_query_len (host) >= every q_b.
+ * float16 / bfloat16 only (matrix-core path), head_dim 64 or 128,
+ * block_size 16; PA_ERR_UNSUPPORTED otherwise.  A sequence with q_b > n,
+ * q_b > max_query_len, n beyond the table, rows outside [0, num_tokens) or
+ * any of its first ceil(n / 16) table entries outside the pool gets NaN in
+ * all its rows (when its row range is valid); nothing is read or written
+ * out of range.  No workspace. */
+int pa_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* query_start, const int32_t* context_lens, int32_t B,
+               int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+               float scale, int32_t dtype, void* stream);
+
 /* Workspace bytes pa_decode needs for these sizes (0 when one partition
  * covers max_context_len, i.e. partition_tokens == 0 or >= max_context_len). */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,

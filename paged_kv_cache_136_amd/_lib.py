@@ -71,6 +71,8 @@ SIGNATURES = {
                                    c_i32, c_vp, c_vp, c_i32, c_vp, c_i64, c_vp]),
     "pa_swap_in": (ctypes.c_int, [ctypes.POINTER(c_vp), ctypes.POINTER(c_vp), c_i32, c_i64,
                                   c_i32, c_vp, c_vp, c_i32, c_vp, c_i64, c_vp]),
+    "pa_prefill": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
+                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_vp]),

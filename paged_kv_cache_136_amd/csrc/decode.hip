@@ -37,6 +37,7 @@
 #include <string>
 
 #include "device_common.hpp"
+#include "mfma_ops.hpp"
 #include "pagedkv.h"
 #include "status.hpp"
 
@@ -347,60 +348,6 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 //       (2^-9 for bf16) does not reach the output (2^-18 after the split).
 //       C: lane (qa, t), reg r holds O[head t][dim 16n + 4qa + r], so the
 //       rescale by alpha is lane-local.
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-template <int DT> struct MfmaOps;
-template <> struct MfmaOps<PA_DTYPE_BF16> {
-  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
-  typedef __bf16 x4 __attribute__((ext_vector_type(4)));
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) x4 lds_x4;
-  static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint2 read_tr(lds_x4* p) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
-  }
-  static __device__ __forceinline__ void split(const float (&p)[4], uint2& hi, uint2& lo) {
-    x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = static_cast<__bf16>(p[i]);
-      l[i] = static_cast<__bf16>(p[i] - static_cast<float>(h[i]));
-    }
-    hi = __builtin_bit_cast(uint2, h);
-    lo = __builtin_bit_cast(uint2, l);
-  }
-};
-template <> struct MfmaOps<PA_DTYPE_F16> {
-  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
-  typedef _Float16 x4 __attribute__((ext_vector_type(4)));
-  typedef __fp16 tr4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
-  typedef __attribute__((address_space(3))) tr4 lds_x4;
-  static __device__ __forceinline__ f32x4_t qk(const uint4& a, const uint4& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4_t pv(const uint2& a, const uint2& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint2 read_tr(lds_x4* p) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16(p));
-  }
-  static __device__ __forceinline__ void split(const float (&p)[4], uint2& hi, uint2& lo) {
-    x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = static_cast<_Float16>(p[i]);
-      l[i] = static_cast<_Float16>(p[i] - static_cast<float>(h[i]));
-    }
-    hi = __builtin_bit_cast(uint2, h);
-    lo = __builtin_bit_cast(uint2, l);
-  }
-};
-
 template <int DT, int D, int G, int NBUF>
 __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   static_assert(DT != PA_DTYPE_F32 && (D == 64 || D == 128) && (G == 4 || G == 8), "shape");

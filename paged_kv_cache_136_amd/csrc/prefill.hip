@@ -1,0 +1,288 @@
+// Prefill attention of an uncached suffix over the paged KV cache (gfx950).
+//
+// What is computed: "P06 · BlockManager" spec overview and key-question
+// answers -- after the first num_cached_tokens tokens of a prompt were
+// prefix hits, only the rest needs a forward pass (at least the last token,
+// whose output yields the next token); "qaqbuyan.com article 130",
+// system-prompt section -- a request reuses the shared prompt's blocks and
+// computes what follows.  Suffix token i of a sequence of total length n
+// and suffix length q sits at position n - q + i and attends, causally, to
+// every token 0 .. n - q + i through the block table (slot = table[pos/bs]
+// * bs + pos % bs), its own K/V already written.  Scale 1/sqrt(head_dim)
+// and float output as in the article's kernel listing.
+//
+// Design.  One workgroup of 4 waves per (query head, 64-query tile,
+// sequence); wave w owns 16 query rows.  The tile's K/V blocks are streamed
+// through LDS once for all four waves (double-buffered, one barrier per
+// block; the next block's loads are in flight while the current one is
+// used), with block ids read by scalar loads and range-checked.  Per block
+// and wave, on the matrix cores:
+//   S^T = K Q^T  v_mfma_f32_16x16x32, A = 16 keys from LDS, B = Q^T of the
+//                wave's 16 query rows (registers); lane (qa, t) gets the
+//                scores of keys 4qa .. 4qa+3 for query row t;
+//   causal mask  key position <= query position, element by element;
+//   softmax      online, exp2 domain, the running max moving only when a
+//                block max exceeds it by more than 2^8 (one wave-uniform
+//                test); per query row, the block max is a 2-step butterfly
+//                over the four qa lanes;
+//   O^T += V^T P^T  v_mfma_f32_16x16x16, A = V^T via transposed LDS reads,
+//                B = the lane's own four p values, split into a high and a
+//                low 16-bit part so P's rounding does not reach the output.
+// A wave skips blocks past its last query row but keeps loading and
+// synchronizing with the others.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "device_common.hpp"
+#include "mfma_ops.hpp"
+#include "pagedkv.h"
+#include "status.hpp"
+
+namespace pkv {
+namespace {
+
+constexpr int kPWaves = 4;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kPBlock = 16;                 // tokens per KV block
+constexpr int kQTile = 16 * kPWaves;        // query rows per workgroup
+constexpr float kPMinusBig = -1e30f;
+constexpr float kPRescaleLog2 = 8.f;
+
+struct PrefillArgs {
+  float* out;
+  const char* q;
+  const char* k;
+  const char* v;
+  const int32_t* tables;
+  const int32_t* qstart;       // [B + 1]
+  const int32_t* lens;         // [B]
+  int32_t num_tokens;          // rows of q and out
+  int32_t max_blocks, max_query_len, hq, hkv, num_blocks;
+  float scale_log2;
+};
+
+template <int DT, int D>
+__global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
+  using M = MfmaOps<DT>;
+  constexpr int ELEM = 2;
+  constexpr int KSTEPS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int VROW = D * ELEM + 32;           // padded LDS row (bytes)
+  constexpr int CHUNKS = kPBlock * D * ELEM / 16;   // 16-byte chunks per block (K or V)
+  constexpr int CPR = D * ELEM / 16;            // chunks per row
+  static_assert(CHUNKS <= kPThreads, "one chunk per thread");
+
+  __shared__ __attribute__((aligned(16))) char s_k[2][kPBlock * VROW];
+  __shared__ __attribute__((aligned(16))) char s_v[2][kPBlock * VROW];
+
+  const int h = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = lane & 15, qa = lane >> 4;
+  const int g = h / (a.hq / a.hkv);
+  const int q0 = a.qstart[b], q1 = a.qstart[b + 1], total = a.num_tokens;
+  const int ql = q1 - q0, n = a.lens[b];
+  const bool valid = ql >= 0 && ql <= a.max_query_len && ql <= n &&
+                     n <= a.max_blocks * kPBlock && q0 >= 0 && q1 <= total;
+  if (!valid) {
+    // Invalid lengths: NaN rows for this sequence's queries (when the row
+    // range itself is sane), written once by tile 0.
+    if (tile == 0 && q0 >= 0 && q1 <= total && q0 <= q1)
+      for (int i = tid; i < (q1 - q0) * D; i += kPThreads)
+        a.out[(static_cast<size_t>(q0 + i / D) * a.hq + h) * D + i % D] = __builtin_nanf("");
+    return;
+  }
+  const int row0 = tile * kQTile;
+  if (row0 >= ql) return;
+  const int cached = n - ql;
+  const int rows_here = min(kQTile, ql - row0);
+  const int last_pos_wg = cached + row0 + rows_here - 1;        // last query position of the tile
+  const int nblk = last_pos_wg / kPBlock + 1;
+  // This wave's query rows and the lane's query row t.
+  const int wrow0 = row0 + 16 * w;
+  const int wrows = max(0, min(16, ql - wrow0));
+  const int my_row = wrow0 + t;
+  const bool row_ok = t < wrows;
+  const int my_pos = row_ok ? cached + my_row : -1;
+  const int wave_last_pos = wrows > 0 ? cached + wrow0 + wrows - 1 : -1;
+
+  uint4 qb[KSTEPS];
+#pragma unroll
+  for (int j = 0; j < KSTEPS; ++j)
+    qb[j] = row_ok ? *reinterpret_cast<const uint4*>(
+                         a.q + ((static_cast<size_t>(q0 + my_row) * a.hq + h) * D + 32 * j + 8 * qa) * ELEM)
+                   : make_uint4(0u, 0u, 0u, 0u);
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kPMinusBig, lsum = 0.f;
+
+  const size_t row_bytes = static_cast<size_t>(a.hkv) * D * ELEM;
+  const size_t block_bytes = row_bytes * kPBlock;
+  const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
+  // Cooperative load mapping: thread tid < CHUNKS moves chunk (row, col).
+  const int c_row = tid / CPR, c_col = tid % CPR;
+  const bool loader = tid < CHUNKS;
+  const size_t c_off = c_row * row_bytes + static_cast<size_t>(g) * D * ELEM + c_col * 16;
+  const int lds_off = c_row * VROW + c_col * 16;
+  bool bad = false;
+  auto load = [&](int j, uint4& kr, uint4& vr) {
+    const int32_t e = trow[j];
+    const bool ok = e >= 0 && e < a.num_blocks;
+    bad |= !ok;
+    const size_t base = static_cast<size_t>(ok ? e : 0) * block_bytes + c_off;
+    if (loader) {
+      kr = *reinterpret_cast<const uint4*>(a.k + base);
+      vr = *reinterpret_cast<const uint4*>(a.v + base);
+      // Rows past the sequence's length stay out of the MFMAs as zeros
+      // (a zero weight times NaN poison would still be NaN).
+      if (j * kPBlock + c_row >= n) kr = vr = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto stash = [&](int buf, const uint4& kr, const uint4& vr) {
+    if (loader) {
+      *reinterpret_cast<uint4*>(s_k[buf] + lds_off) = kr;
+      *reinterpret_cast<uint4*>(s_v[buf] + lds_off) = vr;
+    }
+  };
+  typedef typename M::lds_x4 lds_x4;
+
+  uint4 kr = make_uint4(0u, 0u, 0u, 0u), vr = kr;
+  load(0, kr, vr);
+  stash(0, kr, vr);
+  __syncthreads();
+  for (int j = 0; j < nblk; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nblk) load(j + 1, kr, vr);
+    const int key0 = j * kPBlock;
+    if (key0 <= wave_last_pos) {
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const uint4 kk = *reinterpret_cast<const uint4*>(s_k[buf] + t * VROW + (32 * s + 8 * qa) * ELEM);
+        sacc = M::qk(kk, qb[s], sacc);
+      }
+      float sc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sc[r] = (key0 + 4 * qa + r <= my_pos) ? sacc[r] * a.scale_log2 : -INFINITY;
+      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      bm = group_max<16, 64>(bm);
+      if (__any(bm > m + kPRescaleLog2)) {
+        const float mn = fmaxf(m, bm);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - m);
+      lsum += (p[0] + p[1]) + (p[2] + p[3]);
+      uint2 ph, pl;
+      M::split(p, ph, pl);
+      lds_x4* tr = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[buf]) +
+                             (4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint2 vt = M::read_tr(tr + 4 * nt);
+        acc[nt] = M::pv(vt, ph, acc[nt]);
+        acc[nt] = M::pv(vt, pl, acc[nt]);
+      }
+    }
+    if (j + 1 < nblk) stash(buf ^ 1, kr, vr);
+    __syncthreads();
+  }
+  // The rest of the sequence's table too, so a bad entry anywhere in it
+  // gives NaN rows for the whole sequence, whichever tile reaches it.
+  // Every thread reads the same entries, so `bad` is uniform.
+  for (int j = nblk; j < (n + kPBlock - 1) / kPBlock; ++j) {
+    const int32_t e = trow[j];
+    bad |= !(e >= 0 && e < a.num_blocks);
+  }
+  const bool any_bad = bad;
+
+  lsum = group_sum<16, 64>(lsum);
+  if (row_ok) {
+    const float inv = 1.f / lsum;
+    float* orow = a.out + (static_cast<size_t>(q0 + my_row) * a.hq + h) * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float4 o;
+      o.x = any_bad ? __builtin_nanf("") : acc[nt][0] * inv;
+      o.y = any_bad ? __builtin_nanf("") : acc[nt][1] * inv;
+      o.z = any_bad ? __builtin_nanf("") : acc[nt][2] * inv;
+      o.w = any_bad ? __builtin_nanf("") : acc[nt][3] * inv;
+      *reinterpret_cast<float4*>(orow + 16 * nt + 4 * qa) = o;
+    }
+  }
+}
+
+template <int DT>
+hipError_t launch_prefill(const PrefillArgs& a, int B, int D, hipStream_t st) {
+  const int tiles = (a.max_query_len + kQTile - 1) / kQTile;
+  dim3 grid(a.hq, tiles, B);
+  if (D == 64)
+    prefill_mfma<DT, 64><<<grid, kPThreads, 0, st>>>(a);
+  else
+    prefill_mfma<DT, 128><<<grid, kPThreads, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* query_start, const int32_t* context_lens, int32_t B,
+                          int32_t num_tokens, int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                          int32_t dtype, void* stream) {
+  if (B < 0 || num_tokens < 0 || max_query_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq < 0)
+    return fail(PA_ERR_INVALID, "pa_prefill: bad sizes");
+  if (num_q_heads % num_kv_heads) return fail(PA_ERR_INVALID, "pa_prefill: Hq % Hkv != 0");
+  if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim must be 64 or 128");
+  if (block_size != kPBlock) return fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size must be 16");
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: float16 or bfloat16 only (matrix-core path)");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_prefill: bad scale");
+  if (B == 0 || num_tokens == 0 || max_query_len == 0) { clear_error(); return PA_OK; }
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
+    return fail(PA_ERR_INVALID, "pa_prefill: null pointer");
+  if (B > 65535 || (max_query_len + kQTile - 1) / kQTile > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: grid too large");
+  if (static_cast<size_t>(num_kv_heads) * head_dim * 2 * kPBlock * static_cast<size_t>(num_blocks) >
+      (static_cast<size_t>(1) << 47))
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: cache too large");
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
+       reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
+    return fail(PA_ERR_INVALID, "pa_prefill: buffers must be 16-byte aligned");
+  PrefillArgs a{};
+  a.out = out;
+  a.q = static_cast<const char*>(q);
+  a.k = static_cast<const char*>(k_cache);
+  a.v = static_cast<const char*>(v_cache);
+  a.tables = block_tables;
+  a.qstart = query_start;
+  a.lens = context_lens;
+  a.num_tokens = num_tokens;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = dtype == PA_DTYPE_F16 ? launch_prefill<PA_DTYPE_F16>(a, B, head_dim, st)
+                                         : launch_prefill<PA_DTYPE_BF16>(a, B, head_dim, st);
+  if (err != hipSuccess)
+    return fail(PA_ERR_DEVICE, std::string("pa_prefill: launch failed: ") + hipGetErrorString(err));
+  clear_error();
+  return PA_OK;
+}

@@ -170,3 +170,37 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
                           int(partition_tokens), _dtype_code(q), ws_ptr, ws_bytes,
                           _stream(stream)))
     return out
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, max_query_len,
+               scale=None, out=None, stream=None):
+    """Causal attention of uncached suffixes; returns float32 out [T, Hq, D].
+
+    q [T, Hq, D] holds the suffix rows of every sequence, sequence after
+    sequence (int32 query_start [B+1] on the GPU); context_lens int32 [B]
+    are total lengths; max_query_len is a host int bounding every suffix."""
+    _dev(q, k_cache, v_cache, block_tables, query_start, context_lens)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    B = context_lens.shape[0]
+    if v_cache.shape != k_cache.shape or d2 != d:
+        raise ValueError("shape mismatch")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and caches must share a dtype")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if query_start.dtype != torch.int32 or query_start.shape != (B + 1,):
+        raise ValueError("query_start must be int32 [B + 1]")
+    if context_lens.dtype != torch.int32:
+        raise ValueError("context_lens must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (T, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [T, Hq, D]")
+    check(lib().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           block_tables.data_ptr(), block_tables.shape[1], query_start.data_ptr(),
+                           context_lens.data_ptr(), B, T, int(max_query_len), hq, hkv, d, bs, nb,
+                           float(scale), _dtype_code(q), _stream(stream)))
+    return out
