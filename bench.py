@@ -43,7 +43,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixed_7b",
-                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap", "serve", "beam"],
+                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap", "serve", "beam",
+                            "prefill"],
                    help="mixed_7b is the headline workload; the others are reported lines")
     p.add_argument("--partition-tokens", type=int, default=-1,
                    help="split-KV partition size (default: the workload's, 512)")
@@ -704,6 +705,96 @@ def run_beam(args, torch, pkv, workloads):
     }
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0   # MI355X dense fp16 / bf16, published
+
+
+def run_prefill(args, torch, pkv, workloads):
+    """Prefill of uncached suffixes after a prefix hit: 16 sequences share a
+    1024-token system prompt (prefix-cache hits) and each adds a 1024-token
+    uncached suffix; one layer of 32 heads x 128, fp16, block 16.  The suffix
+    K/V are written (pa_write_kv) and pa_prefill computes their causal
+    attention over 2048-token contexts.  Reported: the kernel's rate in
+    TFLOP/s of algorithmic attention work (4 * head_dim flops per (query,
+    key, head) with key <= query), and K/V bytes read per second."""
+    B, sys_len, sfx, H, D, bs = 16, 1024, 1024, 32, 128, 16
+    n = sys_len + sfx
+    NB = B * (n // bs) + 64
+    dev = torch.device("cuda:0")
+    bm = pkv.BlockManager(NB, bs, True)
+    system = workloads.token_ids(sys_len, seed=21)
+    bm.allocate(0, system + [1])               # registers the shared prompt's blocks
+    tables_l, cached = [], []
+    for b in range(1, B + 1):
+        toks = system + workloads.token_ids(sfx, seed=300 + b)
+        bm.allocate(b, toks)
+        cached.append(bm.num_cached_tokens(b))
+    bm.free(0)
+    seqs = list(range(1, B + 1))
+    qlens = [n - c for c in cached]
+    tables, lens = bm.export_batch(seqs, n // bs, pad_block=0)
+    k = workloads.normal_torch((NB, bs, H, D), 80, torch.float16, dev)
+    v = workloads.normal_torch((NB, bs, H, D), 81, torch.float16, dev)
+    T = sum(qlens)
+    q = workloads.normal_torch((T, H, D), 82, torch.float16, dev)
+    qs = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32, device=dev)
+    d_tab = torch.from_numpy(tables).to(dev)
+    d_len = torch.from_numpy(lens).to(dev)
+    out = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    mq = max(qlens)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        pkv.pa_prefill(q, k, v, d_tab, qs, d_len, mq, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        pkv.pa_prefill(q, k, v, d_tab, qs, d_len, mq, out=out)
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    pairs = sum(sum(c + i + 1 for i in range(ql)) for c, ql in zip(cached, qlens))
+    flops = 4.0 * D * H * pairs
+    kv_bytes = 2.0 * H * D * 2 * sum(lens)         # each sequence's K/V once
+    tflops = flops / (ms.mean() * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        kh = k.float().cpu().numpy()
+        vh = v.float().cpu().numpy()
+        qh = q[:64].float().cpu().numpy()
+        rows, t1 = 0, time.perf_counter()
+        with threadpool_limits(limits=1):
+            while True:
+                oracle.ref_prefill(qh, kh, vh, tables[:1], [64], [cached[0] + 64])
+                rows += 64
+                if time.perf_counter() - t1 > min(args.cpu_seconds, 10):
+                    break
+        sec = time.perf_counter() - t1
+        sample_pairs = rows // 64 * sum(cached[0] + i + 1 for i in range(64))
+        cpu = {"value": round(4.0 * D * H * sample_pairs / sec / 1e12, 6), "unit": "TFLOP/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"the first 64 suffix rows of sequence 1 (after its {cached[0]} cached "
+                         f"tokens), {rows // 64} repetitions in {sec:.1f} s, float64 NumPy, BLAS 1 thread"}
+    return {
+        "metric": "prefill of uncached suffixes: attention TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "prefill", "sequences": B, "cached_prefix": sys_len, "suffix": sfx,
+                   "context": n, "q_heads": H, "kv_heads": H, "head_dim": D, "block_size": bs,
+                   "cached_tokens": cached[:1], "timing": "GPU events per pa_prefill launch"},
+        "kv_gbs": round(kv_bytes / (ms.mean() * 1e-3) / 1e9, 2),
+        "roofline": {"kernel": "pa_prefill", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_MFMA_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_MFMA_F16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(float(ms.mean()), 5), "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": cpu, "wall_s": round(wall, 3),
+    }
+
+
 LENGTH_NOTES = {
     "mixed_7b": "log-uniform [50, 4096], PCG64 seed 0, +1 token per step",
     "13b_layer": "10 x 4096, +1 token per step",
@@ -737,6 +828,8 @@ def main():
         result = run_serve(args, torch, pkv, workloads)
     elif args.workload == "beam":
         result = run_beam(args, torch, pkv, workloads)
+    elif args.workload == "prefill":
+        result = run_prefill(args, torch, pkv, workloads)
     else:
         wb = DecodeBench(args.workload, args, torch, pkv, workloads)
         result = wb.run()

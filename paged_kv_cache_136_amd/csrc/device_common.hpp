@@ -109,6 +109,13 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// c ? a : b for 16-byte chunks, component by component: a ternary on the
+// uint4 struct itself is lowered as a select between two stack copies,
+// which puts both in scratch memory.
+__device__ __forceinline__ uint4 select4(bool c, const uint4& a, const uint4& b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 // ---- 16-byte chunk arithmetic ------------------------------------------
 // A lane holds one 16-byte chunk of a K/V row (4 floats or 8 halves) and the
 // matching chunk of q in the same raw form.

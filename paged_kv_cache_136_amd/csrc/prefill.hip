@@ -11,24 +11,26 @@
 // * bs + pos % bs), its own K/V already written.  Scale 1/sqrt(head_dim)
 // and float output as in the article's kernel listing.
 //
-// Design.  One workgroup of 4 waves per (query head, 64-query tile,
-// sequence); wave w owns 16 query rows.  The tile's K/V blocks are streamed
-// through LDS once for all four waves (double-buffered, one barrier per
-// block; the next block's loads are in flight while the current one is
-// used), with block ids read by scalar loads and range-checked.  Per block
-// and wave, on the matrix cores:
+// Design.  One workgroup of 4 waves per (query head, 128-row query tile,
+// sequence); wave w owns two 16-row query tiles.  The tile's K/V blocks are
+// streamed through LDS once for all four waves, two blocks (32 keys) per
+// stage (double-buffered, one barrier per stage; the next stage's loads are
+// in flight while the current one is used), with block ids read by scalar
+// loads and range-checked.  Per stage and wave, on the matrix cores (every
+// K and V^T operand read from LDS feeds both query tiles):
 //   S^T = K Q^T  v_mfma_f32_16x16x32, A = 16 keys from LDS, B = Q^T of the
 //                wave's 16 query rows (registers); lane (qa, t) gets the
 //                scores of keys 4qa .. 4qa+3 for query row t;
 //   causal mask  key position <= query position, element by element;
-//   softmax      online, exp2 domain, the running max moving only when a
-//                block max exceeds it by more than 2^8 (one wave-uniform
-//                test); per query row, the block max is a 2-step butterfly
-//                over the four qa lanes;
+//   softmax      online, exp2 domain, one update per stage; the running max
+//                moves only when a stage max exceeds it by more than 2^8
+//                (one wave-uniform test); per query row the stage max is a
+//                2-step butterfly over the four qa lanes;
 //   O^T += V^T P^T  v_mfma_f32_16x16x16, A = V^T via transposed LDS reads,
-//                B = the lane's own four p values, split into a high and a
-//                low 16-bit part so P's rounding does not reach the output.
-// A wave skips blocks past its last query row but keeps loading and
+//                B = the lane's own four p values; for bfloat16 p is split
+//                into a high and a low part (two MFMAs) so its 8-bit
+//                rounding does not reach the output.
+// A wave skips stages past its last query row but keeps loading and
 // synchronizing with the others.
 #include <hip/hip_runtime.h>
 
@@ -46,9 +48,20 @@ namespace {
 constexpr int kPWaves = 4;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPBlock = 16;                 // tokens per KV block
-constexpr int kQTile = 16 * kPWaves;        // query rows per workgroup
 constexpr float kPMinusBig = -1e30f;
 constexpr float kPRescaleLog2 = 8.f;
+#ifndef PKV_PF_QW
+#define PKV_PF_QW 2        // 16-row query tiles per wave
+#endif
+#ifndef PKV_PF_KB
+#define PKV_PF_KB 2        // KV blocks per LDS stage (one barrier each)
+#endif
+#ifndef PKV_PF_SPLIT_F16
+#define PKV_PF_SPLIT_F16 0 // also split P into two halves for float16 inputs
+#endif
+constexpr int kQW = PKV_PF_QW;
+constexpr int kKB = PKV_PF_KB;
+constexpr int kQTile = 16 * kQW * kPWaves;  // query rows per workgroup
 
 struct PrefillArgs {
   float* out;
@@ -69,13 +82,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
   constexpr int ELEM = 2;
   constexpr int KSTEPS = D / 32;
   constexpr int NT = D / 16;
-  constexpr int VROW = D * ELEM + 32;           // padded LDS row (bytes)
-  constexpr int CHUNKS = kPBlock * D * ELEM / 16;   // 16-byte chunks per block (K or V)
-  constexpr int CPR = D * ELEM / 16;            // chunks per row
-  static_assert(CHUNKS <= kPThreads, "one chunk per thread");
+  constexpr int VROW = D * ELEM + 32;              // padded LDS row (bytes)
+  constexpr int SROWS = kKB * kPBlock;             // key rows per stage
+  constexpr int CPR = D * ELEM / 16;               // 16-byte chunks per row
+  constexpr int CHUNKS = SROWS * CPR;              // chunks per stage (K or V)
+  constexpr int LPT = (CHUNKS + kPThreads - 1) / kPThreads;   // chunks per thread
+  // bfloat16 keeps 8 bits of p: p goes through the MFMA as a high and a
+  // low part.  float16 keeps 11, enough on its own unless asked otherwise.
+  constexpr bool SPLIT = DT == PA_DTYPE_BF16 || PKV_PF_SPLIT_F16;
 
-  __shared__ __attribute__((aligned(16))) char s_k[2][kPBlock * VROW];
-  __shared__ __attribute__((aligned(16))) char s_v[2][kPBlock * VROW];
+  __shared__ __attribute__((aligned(16))) char s_k[2][SROWS * VROW];
+  __shared__ __attribute__((aligned(16))) char s_v[2][SROWS * VROW];
 
   const int h = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -97,103 +114,168 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
   if (row0 >= ql) return;
   const int cached = n - ql;
   const int rows_here = min(kQTile, ql - row0);
-  const int last_pos_wg = cached + row0 + rows_here - 1;        // last query position of the tile
+  const int last_pos_wg = cached + row0 + rows_here - 1;   // last query position of the tile
   const int nblk = last_pos_wg / kPBlock + 1;
-  // This wave's query rows and the lane's query row t.
-  const int wrow0 = row0 + 16 * w;
-  const int wrows = max(0, min(16, ql - wrow0));
-  const int my_row = wrow0 + t;
-  const bool row_ok = t < wrows;
-  const int my_pos = row_ok ? cached + my_row : -1;
+  const int nstage = (nblk + kKB - 1) / kKB;
+  // This wave's rows: kQW tiles of 16; lane t is row t of each tile.
+  const int wrow0 = row0 + 16 * kQW * w;
+  const int wrows = max(0, min(16 * kQW, ql - wrow0));
   const int wave_last_pos = wrows > 0 ? cached + wrow0 + wrows - 1 : -1;
-
-  uint4 qb[KSTEPS];
+  int my_pos[kQW];
+  uint4 qb[kQW][KSTEPS];
 #pragma unroll
-  for (int j = 0; j < KSTEPS; ++j)
-    qb[j] = row_ok ? *reinterpret_cast<const uint4*>(
-                         a.q + ((static_cast<size_t>(q0 + my_row) * a.hq + h) * D + 32 * j + 8 * qa) * ELEM)
-                   : make_uint4(0u, 0u, 0u, 0u);
-
-  f32x4_t acc[NT];
+  for (int u = 0; u < kQW; ++u) {
+    const int row = wrow0 + 16 * u + t;
+    const bool ok = 16 * u + t < wrows;
+    my_pos[u] = ok ? cached + row : -1;
 #pragma unroll
-  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = kPMinusBig, lsum = 0.f;
+    for (int j = 0; j < KSTEPS; ++j)
+      qb[u][j] = ok ? *reinterpret_cast<const uint4*>(
+                          a.q + ((static_cast<size_t>(q0 + row) * a.hq + h) * D + 32 * j + 8 * qa) * ELEM)
+                    : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  f32x4_t acc[kQW][NT];
+#pragma unroll
+  for (int u = 0; u < kQW; ++u)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[u][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m[kQW], lsum[kQW];
+#pragma unroll
+  for (int u = 0; u < kQW; ++u) { m[u] = kPMinusBig; lsum[u] = 0.f; }
 
   const size_t row_bytes = static_cast<size_t>(a.hkv) * D * ELEM;
   const size_t block_bytes = row_bytes * kPBlock;
   const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
-  // Cooperative load mapping: thread tid < CHUNKS moves chunk (row, col).
-  const int c_row = tid / CPR, c_col = tid % CPR;
-  const bool loader = tid < CHUNKS;
-  const size_t c_off = c_row * row_bytes + static_cast<size_t>(g) * D * ELEM + c_col * 16;
-  const int lds_off = c_row * VROW + c_col * 16;
   bool bad = false;
-  auto load = [&](int j, uint4& kr, uint4& vr) {
-    const int32_t e = trow[j];
-    const bool ok = e >= 0 && e < a.num_blocks;
-    bad |= !ok;
-    const size_t base = static_cast<size_t>(ok ? e : 0) * block_bytes + c_off;
-    if (loader) {
-      kr = *reinterpret_cast<const uint4*>(a.k + base);
-      vr = *reinterpret_cast<const uint4*>(a.v + base);
-      // Rows past the sequence's length stay out of the MFMAs as zeros
-      // (a zero weight times NaN poison would still be NaN).
-      if (j * kPBlock + c_row >= n) kr = vr = make_uint4(0u, 0u, 0u, 0u);
+  // Stage s holds blocks kKB*s .. +kKB-1; thread tid moves chunks tid,
+  // tid + 256, ... (row = chunk / CPR within the stage).  Branch-free, so
+  // the in-flight chunks stay in registers: the address of a key past the
+  // tile's last query position is clamped to the cache start and its value
+  // replaced by zeros (neither NaN poison nor a block outside the tile's
+  // range can reach the MFMAs).
+  static_assert(CHUNKS % kPThreads == 0, "whole chunks per thread");
+  uint4 kr[LPT], vr[LPT];
+  auto load = [&](int stage) {
+    int32_t ids[kKB];
+#pragma unroll
+    for (int bb = 0; bb < kKB; ++bb) {
+      const int j = stage * kKB + bb;
+      const int32_t e = j < nblk ? trow[j] : 0;
+      const bool ok = e >= 0 && e < a.num_blocks;
+      bad |= !ok;
+      ids[bb] = ok ? e : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + i * kPThreads;
+      const int row = c / CPR, col = c % CPR, bb = row / kPBlock;
+      // Keys past the tile's last query position are never attended (and
+      // past the last block they have no valid id): zeros.
+      const bool live = stage * SROWS + row <= last_pos_wg;
+      int32_t id = ids[0];          // select, not an indexed (scratch) array
+#pragma unroll
+      for (int q = 1; q < kKB; ++q) id = bb == q ? ids[q] : id;
+      const size_t off = live ? static_cast<size_t>(id) * block_bytes + (row % kPBlock) * row_bytes +
+                                    static_cast<size_t>(g) * D * ELEM + col * 16
+                              : 0;
+      const uint4 kx = *reinterpret_cast<const uint4*>(a.k + off);
+      const uint4 vx = *reinterpret_cast<const uint4*>(a.v + off);
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+      kr[i] = select4(live, kx, zero);
+      vr[i] = select4(live, vx, zero);
     }
   };
-  auto stash = [&](int buf, const uint4& kr, const uint4& vr) {
-    if (loader) {
-      *reinterpret_cast<uint4*>(s_k[buf] + lds_off) = kr;
-      *reinterpret_cast<uint4*>(s_v[buf] + lds_off) = vr;
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = tid + i * kPThreads;
+      const int off = (c / CPR) * VROW + (c % CPR) * 16;
+      *reinterpret_cast<uint4*>(s_k[buf] + off) = kr[i];
+      *reinterpret_cast<uint4*>(s_v[buf] + off) = vr[i];
     }
   };
   typedef typename M::lds_x4 lds_x4;
 
-  uint4 kr = make_uint4(0u, 0u, 0u, 0u), vr = kr;
-  load(0, kr, vr);
-  stash(0, kr, vr);
+  load(0);
+  stash(0);
   __syncthreads();
-  for (int j = 0; j < nblk; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nblk) load(j + 1, kr, vr);
-    const int key0 = j * kPBlock;
-    if (key0 <= wave_last_pos) {
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nstage) load(st + 1);
+    const int key_base = st * SROWS;
+    if (key_base <= wave_last_pos) {
+      // Scores of every (block, query tile) of the stage first.
+      f32x4_t sacc[kKB][kQW];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(s_k[buf] + t * VROW + (32 * s + 8 * qa) * ELEM);
-        sacc = M::qk(kk, qb[s], sacc);
+      for (int bb = 0; bb < kKB; ++bb) {
+#pragma unroll
+        for (int u = 0; u < kQW; ++u) sacc[bb][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const uint4 kk = *reinterpret_cast<const uint4*>(
+              s_k[buf] + (bb * kPBlock + t) * VROW + (32 * s + 8 * qa) * ELEM);
+#pragma unroll
+          for (int u = 0; u < kQW; ++u) sacc[bb][u] = M::qk(kk, qb[u][s], sacc[bb][u]);
+        }
       }
-      float sc[4];
+      // One softmax update over the stage's keys, per query tile.
+      float sc[kKB][kQW][4];
+      float bm[kQW];
+      bool grow = false;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sc[r] = (key0 + 4 * qa + r <= my_pos) ? sacc[r] * a.scale_log2 : -INFINITY;
-      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      bm = group_max<16, 64>(bm);
-      if (__any(bm > m + kPRescaleLog2)) {
-        const float mn = fmaxf(m, bm);
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        lsum *= alpha;
+      for (int u = 0; u < kQW; ++u) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+        for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = key_base + bb * kPBlock + 4 * qa + r;
+            sc[bb][u][r] = key <= my_pos[u] ? sacc[bb][u][r] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sc[bb][u][r]);
+          }
+        bm[u] = group_max<16, 64>(mx);
+        grow |= bm[u] > m[u] + kPRescaleLog2;
       }
-      float p[4];
+      if (__any(grow)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[r] - m);
-      lsum += (p[0] + p[1]) + (p[2] + p[3]);
-      uint2 ph, pl;
-      M::split(p, ph, pl);
-      lds_x4* tr = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[buf]) +
-                             (4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
+        for (int u = 0; u < kQW; ++u) {
+          const float mn = fmaxf(m[u], bm[u]);
+          const float alpha = fast_exp2(m[u] - mn);
+          m[u] = mn;
+          lsum[u] *= alpha;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const uint2 vt = M::read_tr(tr + 4 * nt);
-        acc[nt] = M::pv(vt, ph, acc[nt]);
-        acc[nt] = M::pv(vt, pl, acc[nt]);
+          for (int nt = 0; nt < NT; ++nt) acc[u][nt] *= alpha;
+        }
+      }
+      uint2 ph[kKB][kQW], pl[kKB][kQW];
+#pragma unroll
+      for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+        for (int u = 0; u < kQW; ++u) {
+          float p[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[bb][u][r] - m[u]);
+          lsum[u] += (p[0] + p[1]) + (p[2] + p[3]);
+          M::split(p, ph[bb][u], pl[bb][u]);
+        }
+      // O^T += V^T P^T: each transposed V read feeds every query tile.
+#pragma unroll
+      for (int bb = 0; bb < kKB; ++bb) {
+        lds_x4* tr = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[buf]) +
+                               (bb * kPBlock + 4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint2 vt = M::read_tr(tr + 4 * nt);
+#pragma unroll
+          for (int u = 0; u < kQW; ++u) {
+            acc[u][nt] = M::pv(vt, ph[bb][u], acc[u][nt]);
+            if constexpr (SPLIT) acc[u][nt] = M::pv(vt, pl[bb][u], acc[u][nt]);
+          }
+        }
       }
     }
-    if (j + 1 < nblk) stash(buf ^ 1, kr, vr);
+    if (st + 1 < nstage) stash(buf ^ 1);
     __syncthreads();
   }
   // The rest of the sequence's table too, so a bad entry anywhere in it
@@ -203,20 +285,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
     const int32_t e = trow[j];
     bad |= !(e >= 0 && e < a.num_blocks);
   }
-  const bool any_bad = bad;
 
-  lsum = group_sum<16, 64>(lsum);
-  if (row_ok) {
-    const float inv = 1.f / lsum;
-    float* orow = a.out + (static_cast<size_t>(q0 + my_row) * a.hq + h) * D;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float4 o;
-      o.x = any_bad ? __builtin_nanf("") : acc[nt][0] * inv;
-      o.y = any_bad ? __builtin_nanf("") : acc[nt][1] * inv;
-      o.z = any_bad ? __builtin_nanf("") : acc[nt][2] * inv;
-      o.w = any_bad ? __builtin_nanf("") : acc[nt][3] * inv;
-      *reinterpret_cast<float4*>(orow + 16 * nt + 4 * qa) = o;
+  for (int u = 0; u < kQW; ++u) {
+    const float l = group_sum<16, 64>(lsum[u]);
+    if (16 * u + t < wrows) {
+      const float inv = 1.f / l;
+      float* orow = a.out + (static_cast<size_t>(q0 + wrow0 + 16 * u + t) * a.hq + h) * D;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float4 o;
+        o.x = bad ? __builtin_nanf("") : acc[u][nt][0] * inv;
+        o.y = bad ? __builtin_nanf("") : acc[u][nt][1] * inv;
+        o.z = bad ? __builtin_nanf("") : acc[u][nt][2] * inv;
+        o.w = bad ? __builtin_nanf("") : acc[u][nt][3] * inv;
+        *reinterpret_cast<float4*>(orow + 16 * nt + 4 * qa) = o;
+      }
     }
   }
 }
