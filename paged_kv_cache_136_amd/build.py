@@ -20,9 +20,12 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# Packed-FP32 instructions are disabled for all device code.
+# Packed-FP32 instructions are disabled for all device code.  MFMA results
+# are kept in ordinary VGPRs: the softmax rescales the accumulators with VALU
+# instructions, and with the accumulation registers chosen instead every
+# prefill stage spent ~200 extra register moves shuttling them back and forth.
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
-                "-packed-fp32-ops"]
+                "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 

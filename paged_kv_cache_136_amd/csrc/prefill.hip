@@ -26,10 +26,10 @@
 //                moves only when a stage max exceeds it by more than 2^8
 //                (one wave-uniform test); per query row the stage max is a
 //                2-step butterfly over the four qa lanes;
-//   O^T += V^T P^T  v_mfma_f32_16x16x16, A = V^T via transposed LDS reads,
-//                B = the lane's own four p values; for bfloat16 p is split
-//                into a high and a low part (two MFMAs) so its 8-bit
-//                rounding does not reach the output.
+//   O^T += V^T P^T  v_mfma_f32_16x16x32 over the stage's two blocks, A = V^T
+//                via transposed LDS reads, B = the lane's own p values; for
+//                bfloat16 p is split into a high and a low part (two MFMAs)
+//                so its 8-bit rounding does not reach the output.
 // A wave skips stages past its last query row but keeps loading and
 // synchronizing with the others.
 #include <hip/hip_runtime.h>
@@ -259,18 +259,32 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
           lsum[u] += (p[0] + p[1]) + (p[2] + p[3]);
           M::split(p, ph[bb][u], pl[bb][u]);
         }
-      // O^T += V^T P^T: each transposed V read feeds every query tile.
+      // O^T += V^T P^T with the K=32 MFMA over two blocks at once (the
+      // K=16 form runs at half the rate on gfx950): the reduction index k =
+      // 8qa + e stands for key 4qa + e of the pair's first block (e < 4) and
+      // of its second block (e >= 4), in both operands -- two transposed V
+      // reads side by side as A, the lane's p values of both blocks as B.
+      // Each V read feeds every query tile.
+      static_assert(kKB % 2 == 0, "blocks are taken in pairs");
 #pragma unroll
-      for (int bb = 0; bb < kKB; ++bb) {
-        lds_x4* tr = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[buf]) +
-                               (bb * kPBlock + 4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
+      for (int bp = 0; bp < kKB; bp += 2) {
+        lds_x4* tr0 = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[buf]) +
+                                (bp * kPBlock + 4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
+        lds_x4* tr1 = (lds_x4*)((__attribute__((address_space(3))) char*)tr0 + kPBlock * VROW);
+        uint4 pb[kQW], pbl[kQW];
+#pragma unroll
+        for (int u = 0; u < kQW; ++u) {
+          pb[u] = make_uint4(ph[bp][u].x, ph[bp][u].y, ph[bp + 1][u].x, ph[bp + 1][u].y);
+          pbl[u] = make_uint4(pl[bp][u].x, pl[bp][u].y, pl[bp + 1][u].x, pl[bp + 1][u].y);
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const uint2 vt = M::read_tr(tr + 4 * nt);
+          const uint2 v0 = M::read_tr(tr0 + 4 * nt), v1 = M::read_tr(tr1 + 4 * nt);
+          const uint4 vt = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
           for (int u = 0; u < kQW; ++u) {
-            acc[u][nt] = M::pv(vt, ph[bb][u], acc[u][nt]);
-            if constexpr (SPLIT) acc[u][nt] = M::pv(vt, pl[bb][u], acc[u][nt]);
+            acc[u][nt] = M::qk(vt, pb[u], acc[u][nt]);
+            if constexpr (SPLIT) acc[u][nt] = M::qk(vt, pbl[u], acc[u][nt]);
           }
         }
       }
