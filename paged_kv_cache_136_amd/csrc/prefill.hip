@@ -56,6 +56,9 @@ constexpr float kPRescaleLog2 = 8.f;
 #ifndef PKV_PF_KB
 #define PKV_PF_KB 2        // KV blocks per LDS stage (one barrier each)
 #endif
+#ifndef PKV_PF_WAVES_PER_EU
+#define PKV_PF_WAVES_PER_EU 3  // waves per SIMD the register budget is fitted to
+#endif
 #ifndef PKV_PF_SPLIT_F16
 #define PKV_PF_SPLIT_F16 0 // also split P into two halves for float16 inputs
 #endif
@@ -77,7 +80,7 @@ struct PrefillArgs {
 };
 
 template <int DT, int D>
-__global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_PF_WAVES_PER_EU, PKV_PF_WAVES_PER_EU))) void prefill_mfma(PrefillArgs a) {
   using M = MfmaOps<DT>;
   constexpr int ELEM = 2;
   constexpr int KSTEPS = D / 32;
@@ -219,7 +222,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
           for (int u = 0; u < kQW; ++u) sacc[bb][u] = M::qk(kk, qb[u][s], sacc[bb][u]);
         }
       }
-      // One softmax update over the stage's keys, per query tile.
+      // One softmax update over the stage's keys, per query tile.  Scores
+      // stay unscaled (scale > 0, so the max commutes with it) and the
+      // causal mask is only applied where the stage reaches past a row's
+      // position: a full wave whose first row is at or after the stage's
+      // last key needs none.
+      const bool no_mask = wrows == 16 * kQW && cached + wrow0 >= key_base + SROWS - 1;
       float sc[kKB][kQW][4];
       float bm[kQW];
       bool grow = false;
@@ -231,10 +239,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = key_base + bb * kPBlock + 4 * qa + r;
-            sc[bb][u][r] = key <= my_pos[u] ? sacc[bb][u][r] * a.scale_log2 : -INFINITY;
+            sc[bb][u][r] = (no_mask || key <= my_pos[u]) ? sacc[bb][u][r] : -INFINITY;
             mx = fmaxf(mx, sc[bb][u][r]);
           }
-        bm[u] = group_max<16, 64>(mx);
+        bm[u] = group_max<16, 64>(mx) * a.scale_log2;
         grow |= bm[u] > m[u] + kPRescaleLog2;
       }
       if (__any(grow)) {
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma(PrefillArgs a) {
         for (int u = 0; u < kQW; ++u) {
           float p[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(sc[bb][u][r] - m[u]);
+          for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(sc[bb][u][r], a.scale_log2, -m[u]));
           lsum[u] += (p[0] + p[1]) + (p[2] + p[3]);
           M::split(p, ph[bb][u], pl[bb][u]);
         }
