@@ -312,8 +312,12 @@ def run_fork_cow(args, torch, pkv, workloads):
     round after the fork copies 7 shared, partly filled blocks per prompt
     (448 pa_copy_blocks pairs); rounds 2..255 are run untimed; the timed
     steps are then rounds of append + write + decode over 512 sequences of
-    2305+ tokens.  Reported: logical KV GB/s (every sequence's tokens) and
-    GB/s over the unique blocks read, plus the COW round's copy kernel."""
+    2305+ tokens.  Decode is pa_decode_shared with a plan from
+    pa_shared_plan made on the host every step (the 128 prompt blocks of a
+    family are read once per family); plain pa_decode on the final batch is
+    timed after the steps for comparison.  Reported: logical KV GB/s (every
+    sequence's tokens) and GB/s over the unique blocks read, plus the COW
+    round's copy kernel."""
     cfg = workloads.CONFIGS["fork_cow"]
     bs, NB, H, D = cfg["bs"], cfg["num_blocks"], cfg["hkv"], cfg["d"]
     P, F, L0, X = cfg["prompts"], cfg["forks"], cfg["prompt_len"], cfg["extra"]
@@ -345,15 +349,29 @@ def run_fork_cow(args, torch, pkv, workloads):
         d_pairs = torch.from_numpy(pairs).to(dev) if len(pairs) else None
         return d_slot, d_pairs, len(pairs)
 
-    def decode(max_len, ev=None):
+    plan_s = []
+
+    def decode(max_len, ev=None, shared=True):
         bm.export_batch(seqs, max_blocks, 0, tables_out=tab_h.numpy(), lens_out=len_h.numpy())
         d_tab.copy_(tab_h)
         d_len.copy_(len_h)
+        if shared:
+            h0 = time.perf_counter()
+            sg, groups, mx, mp = pkv.pa_shared_plan(tab_h.numpy(), len_h.numpy(), bs, 512, 1)
+            plan_s.append(time.perf_counter() - h0)
+            d_sg = torch.from_numpy(sg).to(dev)
+            d_groups = torch.from_numpy(groups).to(dev)
         if ev is not None:
             ev[0].record()
-        pkv.pa_decode(q, k, v, d_tab, d_len, max_len, partition_tokens=512, out=out, workspace=ws)
+        if shared:
+            pkv.pa_decode_shared(q, k, v, d_tab, d_len, max_len, d_sg, d_groups, mx, mp,
+                                 partition_tokens=512, out=out, workspace=ws)
+        else:
+            pkv.pa_decode(q, k, v, d_tab, d_len, max_len, partition_tokens=512, out=out,
+                          workspace=ws)
         if ev is not None:
             ev[1].record()
+        return len(groups) if shared else 0
 
     T = torch.cuda.Event
     # Parent token, then the forks.
@@ -389,13 +407,14 @@ def run_fork_cow(args, torch, pkv, workloads):
     evs = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
     dec = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
     lens, uniq = [], []
+    plan_s.clear()
     t0 = time.perf_counter()
     for i in range(args.steps):
         n = L0 + 1 + X + args.warmup + i + 1
         d_slot, _, _ = append(seqs, toks)
         evs[i][0].record()
         pkv.pa_write_kv(k, v, kn, vn, d_slot)
-        decode(n, dec[i])
+        n_groups = decode(n, dec[i])
         evs[i][1].record()
         lens.append(n)
         # unique blocks read: the shared prefix once per prompt plus every
@@ -405,6 +424,13 @@ def run_fork_cow(args, torch, pkv, workloads):
     wall = time.perf_counter() - t0
     step_ms = np.array([a.elapsed_time(b) for a, b in evs])
     dec_ms = np.array([a.elapsed_time(b) for a, b in dec])
+    # plain pa_decode over the final batch, same tables, for comparison
+    n_last = lens[-1]
+    plain = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        decode(n_last, plain[i], shared=False)
+    torch.cuda.synchronize()
+    plain_ms = np.array([a.elapsed_time(b) for a, b in plain])
     per_tok = 2 * H * D * 2
     logical = np.array(lens, dtype=np.float64) * B * per_tok
     unique = np.array(uniq, dtype=np.float64) * per_tok
@@ -421,7 +447,8 @@ def run_fork_cow(args, torch, pkv, workloads):
                    "appended": X, "q_heads": cfg["hq"], "kv_heads": H, "head_dim": D,
                    "block_size": bs, "num_blocks": NB, "partition_tokens": 512,
                    "timing": "GPU events per step (write + decode); value counts logical "
-                             "KV bytes (shared prefix blocks once per sequence)"},
+                             "KV bytes (shared prefix blocks once per sequence)",
+                   "decode": "pa_decode_shared with a per-step host plan"},
         "seqs_per_s": round(B * args.steps / (step_ms.sum() * 1e-3), 1),
         "gpu_step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(step_ms, [10, 50, 90])],
         "unique_kv_gbs": round(float(unique.sum() / (step_ms.sum() * 1e-3) / 1e9), 2),
@@ -429,7 +456,11 @@ def run_fork_cow(args, torch, pkv, workloads):
         "cow_round": {"pairs": npairs, "copy_ms": round(cow_ms, 4),
                       "copy_gbs": round(cow_bytes / (cow_ms * 1e-3) / 1e9, 2),
                       "round_ms": round(round_ms, 4)},
-        "roofline": {"kernel": "pa_decode (split-KV phase 1 + reduce), unique bytes",
+        "shared_prefix": {"groups": n_groups, "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
+                          "decode_ms": round(float(dec_ms.mean()), 5),
+                          "plain_pa_decode_ms": round(float(plain_ms.mean()), 5),
+                          "plain_unique_gbs": round(float(unique[-1] / (plain_ms.mean() * 1e-3) / 1e9), 2)},
+        "roofline": {"kernel": "pa_decode_shared (shared phase + private phase + reduce), unique bytes",
                      "bound": "hbm", "achieved": round(achieved_u, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved_u / PEAK_HBM_GBS, 4),
                      "traffic": None, "avg_launch_ms": round(float(dec_ms.mean()), 5),

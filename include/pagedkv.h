@@ -12,7 +12,8 @@
  *     pinned host memory when a sequence is preempted and resumed;
  *   - pa_decode: attention of one query token per sequence over K/V that
  *     live in fixed-size blocks scattered through HBM, found through the
- *     sequence's block table, with split-KV partitions and a final reduce.
+ *     sequence's block table, with split-KV partitions and a final reduce;
+ *     pa_decode_shared reads blocks shared by several sequences once.
  *
  * Pages cited:
  *   [A130]  "qaqbuyan.com article 130" (vLLM PagedAttention walk-through):
@@ -434,6 +435,80 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- shared-prefix decode ------------------------------------------------
+ * Sequences forked from one parent share the parent's blocks ([D31] fork
+ * and copy-on-write) and prefix-cache hits share full blocks ([P06] spec
+ * overview), so in a batch several block tables can start with the same
+ * physical blocks.  pa_decode reads such a block once per sequence;
+ * pa_decode_shared reads the shared leading partitions of a group of
+ * sequences once for the whole group, then each member's own partitions.
+ * The output is the attention pa_decode defines (same formula, same
+ * float32 accumulation; partial results are merged in a different order).
+ *
+ * A plan is two int32 arrays:
+ *   seq_group [B]: the group of sequence b, or -1;
+ *   groups [n_groups][PA_SHARED_ROW]: row = {P, m_0, ..., m_15}: P shared
+ *     split-KV partitions (P * partition_tokens leading tokens), then the
+ *     batch indices of the members, -1 in unused slots.  At most
+ *     PA_SHARED_MAX_MEMBERS / (num_q_heads / num_kv_heads) slots are used.
+ * Sequence b is a member of group g when seq_group[b] == g, b is listed in
+ * row g, 1 <= P <= max_shared_parts, and b's blocks before its last one
+ * cover at least the P partitions (P * partition_tokens / block_size <
+ * number of blocks of b).  A member's first P partitions are computed from
+ * the table row of m_0 (which need not be a member itself); the rest of
+ * its partitions, and every sequence that is not a member, as in
+ * pa_decode.  A member whose table differs from row m_0 inside those
+ * partitions, or a group whose m_0 is outside [0, B), gives NaN output
+ * rows for those members (nothing is read out of range). */
+#define PA_SHARED_MAX_MEMBERS 16
+#define PA_SHARED_ROW (1 + PA_SHARED_MAX_MEMBERS)
+
+/* A plan for pa_decode_shared from the host copies of the batch's tables
+ * and lengths.  Candidates are sequences with at least one whole partition
+ * of full blocks before their last block.  They are bucketed by first
+ * block id and sorted by table row; a bucket is cut greedily into groups of
+ * at most PA_SHARED_MAX_MEMBERS / query_group sequences, a sequence joining
+ * the open group while (members - 1) x shared partitions does not drop; a
+ * group's P is the common leading run of its rows, in whole partitions.
+ *   tables: host int32 [B][max_blocks]; lens: host int32 [B].
+ *   partition_tokens: the value pa_decode_shared will get (> 0, multiple of
+ *     block_size); query_group: num_q_heads / num_kv_heads (1, 2, 4, 8).
+ *   seq_group_out: host int32 [B].
+ *   groups_out: host int32 [B / 2][PA_SHARED_ROW] (unused if B < 2).
+ *   *n_groups_out: groups written; *max_parts_out: largest P (0 if none);
+ *   *max_private_parts_out: the most partitions any sequence has outside
+ *     its group's P (a sequence in no group: all of its partitions).
+ * Every group it writes satisfies the membership rule above for all its
+ * members. */
+int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t B,
+                   int32_t block_size, int32_t partition_tokens, int32_t query_group,
+                   int32_t* seq_group_out, int32_t* groups_out, int32_t* n_groups_out,
+                   int32_t* max_parts_out, int32_t* max_private_parts_out);
+
+/* pa_decode with a shared-prefix plan (above).  Arguments as pa_decode,
+ * plus:
+ *   seq_group: device int32 [B]; groups: device int32
+ *     [n_groups][PA_SHARED_ROW]; both may be NULL when n_groups == 0, which
+ *     makes the call exactly pa_decode.
+ *   max_shared_parts: host-side bound on every group's P (sizes the grid;
+ *     a group with a larger P has no members).
+ *   max_private_parts: host-side bound on the partitions any sequence has
+ *     outside its group's P (sizes the private grid; 0 = no bound, the
+ *     grid then covers max_context_len).  A sequence with more gets NaN
+ *     output rows.
+ * With n_groups > 0: dtype F16 or BF16 (the shared partitions run on the
+ * matrix cores with up to 16 query columns: members x query group), and
+ * partition_tokens > 0.  The workspace is the one pa_decode needs. */
+int pa_decode_shared(float* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, float scale,
+                     int32_t partition_tokens, int32_t dtype, const int32_t* seq_group,
+                     const int32_t* groups, int32_t n_groups, int32_t max_shared_parts,
+                     int32_t max_private_parts, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,9 +73,14 @@ SIGNATURES = {
                                   c_i32, c_vp, c_vp, c_i32, c_vp, c_i64, c_vp]),
     "pa_prefill": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
+    "pa_shared_plan": (ctypes.c_int, [P_i32, c_i32, P_i32, c_i32, c_i32, c_i32, c_i32, P_i32,
+                                      P_i32, P_i32, P_i32, P_i32]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_vp]),
+    "pa_decode_shared": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                        c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32,
+                                        c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
 }
 
 

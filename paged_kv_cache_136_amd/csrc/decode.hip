@@ -33,6 +33,7 @@
 // under 1% of that at the supported shapes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <string>
 
@@ -84,6 +85,14 @@ struct DecodeArgs {
   int32_t part_blocks;   // blocks per partition
   int32_t num_parts;     // P = partitions of max_len
   float scale_log2;      // scale * log2(e)
+  // Shared-prefix plan (seq_group == nullptr: none).
+  const int32_t* seq_group;  // [B]
+  const int32_t* groups;     // [n_groups][PA_SHARED_ROW]
+  int32_t n_groups;
+  int32_t max_shared_parts;
+  int32_t batch;             // B
+  int32_t qgroup;            // query heads per KV head
+  int32_t grid_parts;        // z extent of the private grid (<= num_parts)
 };
 
 __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
@@ -93,6 +102,30 @@ __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
 __device__ __forceinline__ int num_parts_of(int n, int part_blocks) {
   int nb = (n + kBlock - 1) / kBlock;
   return nb == 0 ? 1 : (nb + part_blocks - 1) / part_blocks;
+}
+
+// Shared partitions P of a group row when P is in range and leaves at least
+// one private block to a sequence of nblk blocks, else 0.  Both the shared
+// and the private kernels decide membership through this one rule, so every
+// partition of every sequence is computed by exactly one of them.
+__device__ __forceinline__ int shared_parts_for(const DecodeArgs& a, const int32_t* row, int nblk) {
+  const int P = row[0];
+  const bool ok = P >= 1 && P <= a.max_shared_parts &&
+                  static_cast<int64_t>(P) * a.part_blocks < nblk;
+  return ok ? P : 0;
+}
+
+// Partitions of sequence b computed by the shared kernel (0: not a member).
+// nblk is b's block count, 0 for an invalid length.
+__device__ __forceinline__ int shared_start(const DecodeArgs& a, int b, int nblk) {
+  if (a.seq_group == nullptr) return 0;
+  const int gi = a.seq_group[b];
+  if (gi < 0 || gi >= a.n_groups) return 0;
+  const int32_t* row = a.groups + static_cast<size_t>(gi) * PA_SHARED_ROW;
+  const int slots = PA_SHARED_MAX_MEMBERS / a.qgroup;
+  bool listed = false;
+  for (int sl = 0; sl < slots; ++sl) listed |= row[1 + sl] == b;
+  return listed ? shared_parts_for(a, row, nblk) : 0;
 }
 
 // Running softmax state of one lane: every lane of a row group (the LPR
@@ -175,13 +208,17 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   // correlate with work size: heads of one (sequence, partition) cost the
   // same, and partitions that a sequence does not have (the cheap exits)
   // collect at the end of the grid.
-  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  // With a shared-prefix plan, a member's first partitions belong to the
+  // shared kernel and z counts from the first private one.
+  const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
   const int n = a.lens[b];
   const bool valid = len_valid(n, a);
   const int nblk = valid ? (n + kBlock - 1) / kBlock : 0;
   const int nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
+  const int start = shared_start(a, b, nblk);
+  const int part = static_cast<int>(blockIdx.z) + start;
   if (part >= nparts) return;
   const int h0 = g * G;
 
@@ -226,7 +263,9 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   // outside the pool is replaced by block 0 (never read out of range) and
   // flags the sequence; its output becomes NaN after the merge.
   const int wv = __builtin_amdgcn_readfirstlane(w);
-  bool bad_ids = false;
+  // A grid sized below this sequence's private partitions (a host bound
+  // that was too small) leaves some uncomputed: flag it like a bad id.
+  bool bad_ids = nparts - start > static_cast<int>(gridDim.z);
   auto block_id = [&](int j) -> int {
     const int32_t e = trow[j];
     const bool ok = e >= 0 && e < a.num_blocks;
@@ -348,9 +387,21 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 //       (2^-9 for bf16) does not reach the output (2^-18 after the split).
 //       C: lane (qa, t), reg r holds O[head t][dim 16n + 4qa + r], so the
 //       rescale by alpha is lane-local.
-template <int DT, int D, int G, int NBUF>
+// SHARED: one workgroup per (KV head, plan group, shared partition).  The
+//       16 query columns are (member slot t / qgroup, query head t % qgroup)
+//       of the group's members, the blocks come from the table row of the
+//       group's first slot, and each column's (m, l, o) goes to its
+//       member's workspace row.  Every member checks that its own table
+//       holds the same ids over the partition (NaN output otherwise).
+// The per-wave output rows overlay the K/V staging buffers after a barrier
+// (PKV_MFMA_O_UNION), which keeps LDS at 36 KB for 16 columns.
+#ifndef PKV_MFMA_O_UNION
+#define PKV_MFMA_O_UNION 1
+#endif
+template <int DT, int D, int G, int NBUF, bool SHARED>
 __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
-  static_assert(DT != PA_DTYPE_F32 && (D == 64 || D == 128) && (G == 4 || G == 8), "shape");
+  static_assert(DT != PA_DTYPE_F32 && (D == 64 || D == 128), "shape");
+  static_assert(SHARED ? G == 16 : (G == 4 || G == 8), "query columns");
   using M = MfmaOps<DT>;
   constexpr int ELEM = 2;
   constexpr int KSTEPS = D / 32;          // QK MFMAs per block
@@ -360,36 +411,92 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   constexpr int VLOADS = kBlock / RPI;    // V loads per block
   constexpr int VROW = D * ELEM + 32;     // padded LDS row (bytes)
 
+  constexpr int KVBUF = kWaves * kBlock * VROW;
+  constexpr int KBUFS = PKV_MFMA_K_LDS ? 2 : 1;
+  constexpr bool O_UNION = PKV_MFMA_O_UNION && kWaves * G * D * 4 <= KBUFS * KVBUF;
   __shared__ int32_t s_bad[kWaves];
-  __shared__ __attribute__((aligned(16))) char s_v[kWaves][kBlock * VROW];
-  __shared__ __attribute__((aligned(16))) char s_k[PKV_MFMA_K_LDS ? kWaves : 1][kBlock * VROW];
+  __shared__ __attribute__((aligned(16))) char s_kv[KBUFS * KVBUF + (O_UNION ? 0 : kWaves * G * D * 4)];
   __shared__ float s_m[kWaves][G], s_l[kWaves][G];
-  __shared__ float s_o[kWaves][G][D];
+  __shared__ int32_t s_col[SHARED ? G : 1];          // member of each column, -1 if none
+  __shared__ int32_t s_mis[SHARED ? kWaves : 1][SHARED ? 16 : 1];
+  char (*s_v)[kBlock * VROW] = reinterpret_cast<char (*)[kBlock * VROW]>(s_kv);
+  char (*s_k)[kBlock * VROW] =
+      reinterpret_cast<char (*)[kBlock * VROW]>(s_kv + (PKV_MFMA_K_LDS ? KVBUF : 0));
+  float (*s_o)[G][D] = reinterpret_cast<float (*)[G][D]>(s_kv + (O_UNION ? 0 : KBUFS * KVBUF));
 
-  const int g = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+  const int g = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t = lane & 15, qa = lane >> 4;
-  const int n = a.lens[b];
-  const bool valid = len_valid(n, a);
-  const int nblk = valid ? (n + kBlock - 1) / kBlock : 0;
-  const int nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
-  if (part >= nparts) return;
-  const int h0 = g * G;
-
-  if (!valid || n == 0) {
-    const float fill = valid ? 0.f : __builtin_nanf("");
-    for (int i = tid; i < G * D; i += kThreads)
-      a.out[(static_cast<size_t>(b) * a.hq + h0 + i / D) * D + i % D] = fill;
-    return;
+  const int h0 = g * (SHARED ? a.qgroup : G);
+  // b: sequence (private) or plan group (shared).  n: tokens the blocks
+  // [first, last) are cut from; trow: the table row they are read from.
+  int b = blockIdx.y, part, n, nblk, nparts, first, last;
+  bool short_grid = false;
+  const int32_t* trow;
+  // SHARED: column t's member (-1 if none) and its query head; the member
+  // slot this lane checks (slot t), and whether the group's source row is
+  // usable.
+  int col_seq = -1, chk_seq = -1;
+  bool src_ok = true;
+  if constexpr (SHARED) {
+    const int32_t* row = a.groups + static_cast<size_t>(b) * PA_SHARED_ROW;
+    const int P = row[0];
+    part = blockIdx.z;
+    if (P < 1 || P > a.max_shared_parts || part >= P) return;
+    const int slots = PA_SHARED_MAX_MEMBERS / a.qgroup;
+    // Membership as the private kernels decide it.
+    auto member = [&](int sl) -> int {
+      if (sl >= slots) return -1;
+      const int m = row[1 + sl];
+      if (m < 0 || m >= a.batch || a.seq_group[m] != b) return -1;
+      const int nm = a.lens[m];
+      if (!len_valid(nm, a)) return -1;
+      return shared_parts_for(a, row, (nm + kBlock - 1) / kBlock) > 0 ? m : -1;
+    };
+    col_seq = member(t / a.qgroup);
+    chk_seq = member(t);
+    // Nothing to do unless some column has a member (wave-uniform: every
+    // wave holds the same 16 columns).
+    if (!__any(col_seq >= 0)) return;
+    const int lead = row[1];
+    src_ok = lead >= 0 && lead < a.batch;
+    trow = a.tables + static_cast<size_t>(src_ok ? lead : 0) * a.max_blocks;
+    first = part * a.part_blocks;
+    last = src_ok ? first + a.part_blocks : first;   // within max_blocks: a member exists
+    n = last * kBlock;                               // shared blocks are full
+    nblk = last;
+    nparts = 0;
+  } else {
+    const int nn = a.lens[b];
+    const bool valid = len_valid(nn, a);
+    n = nn;
+    nblk = valid ? (n + kBlock - 1) / kBlock : 0;
+    nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
+    const int start = shared_start(a, b, nblk);
+    part = static_cast<int>(blockIdx.z) + start;
+    if (part >= nparts) return;
+    short_grid = nparts - start > static_cast<int>(gridDim.z);
+    if (!valid || n == 0) {
+      const float fill = valid ? 0.f : __builtin_nanf("");
+      for (int i = tid; i < G * D; i += kThreads)
+        a.out[(static_cast<size_t>(b) * a.hq + h0 + i / D) * D + i % D] = fill;
+      return;
+    }
+    trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
+    first = part * a.part_blocks;
+    last = min(nblk, first + a.part_blocks);
   }
 
-  // Q^T as the QK B operand: head t, dims 32j + 8qa .. +8 (zero past G).
+  // Q^T as the QK B operand: column t, dims 32j + 8qa .. +8 (zero for a
+  // column without a query head).
+  const int qhead = SHARED ? h0 + t % a.qgroup : h0 + t;
+  const int qseq = SHARED ? col_seq : (t < G ? b : -1);
   uint4 qb[KSTEPS];
 #pragma unroll
   for (int j = 0; j < KSTEPS; ++j)
-    qb[j] = t < G ? *reinterpret_cast<const uint4*>(
-                        a.q + ((static_cast<size_t>(b) * a.hq + h0 + t) * D + 32 * j + 8 * qa) * ELEM)
-                  : make_uint4(0u, 0u, 0u, 0u);
+    qb[j] = qseq >= 0 ? *reinterpret_cast<const uint4*>(
+                            a.q + ((static_cast<size_t>(qseq) * a.hq + qhead) * D + 32 * j + 8 * qa) * ELEM)
+                      : make_uint4(0u, 0u, 0u, 0u);
 
   f32x4_t acc[NT];
 #pragma unroll
@@ -411,16 +518,13 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   lds_x4* tr_base = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[w]) +
                               (4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
 
-  const int first = part * a.part_blocks;
-  const int last = min(nblk, first + a.part_blocks);
-  const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
   // Block ids come straight from the table with scalar loads (uniform
   // addresses, served by the scalar cache; tables are tiny and stay in L2),
   // so a wave starts streaming without any LDS staging or barrier.  An id
   // outside the pool is replaced by block 0 (never read out of range) and
   // flags the sequence; its output becomes NaN after the merge.
   const int wv = __builtin_amdgcn_readfirstlane(w);
-  bool bad_ids = false;
+  bool bad_ids = short_grid;
   auto block_id = [&](int j) -> int {
     const int32_t e = trow[j];
     const bool ok = e >= 0 && e < a.num_blocks;
@@ -520,9 +624,24 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     }
   }
 
-  // Wave result per head t: m is already uniform over the four qa lanes;
+  // SHARED: member slot t's own table must hold the source row's ids over
+  // [first, last); lane (w, qa) of column t compares blocks first + 4w + qa,
+  // +16, ...  (after the main loop, so the first K/V loads are not held up).
+  if constexpr (SHARED) {
+    bool mismatch = false;
+    if (chk_seq >= 0 && src_ok) {
+      const int32_t* mrow = a.tables + static_cast<size_t>(chk_seq) * a.max_blocks;
+      for (int j = first + 4 * w + qa; j < last; j += 16) mismatch |= mrow[j] != trow[j];
+    }
+    mismatch = group_max<16, 64>(mismatch ? 1.f : 0.f) != 0.f;   // over the qa lanes
+    if (qa == 0) s_mis[w][t] = mismatch;
+    if (w == 0 && qa == 0) s_col[t] = col_seq;
+  }
+
+  // Wave result per column t: m is already uniform over the four qa lanes;
   // the partial sums of the four token quarters add up.
   lsum = group_sum<16, 64>(lsum);
+  if constexpr (O_UNION) __syncthreads();   // every wave is done with the K/V staging
   if (t < G) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -539,6 +658,31 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   const bool bad = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
   for (int i = tid; i < G * D; i += kThreads) {
     const int hh = i / D, d = i % D;
+    if constexpr (SHARED) {
+      // Column hh -> (member slot hh / qgroup, query head h0 + hh % qgroup).
+      const int mseq = s_col[hh];
+      if (mseq < 0) continue;
+      const int sl = hh / a.qgroup;
+      const bool badc = bad || !src_ok ||
+                        (s_mis[0][sl] | s_mis[1][sl] | s_mis[2][sl] | s_mis[3][sl]) != 0;
+      float Mx = s_m[0][hh];
+#pragma unroll
+      for (int ww = 1; ww < kWaves; ++ww) Mx = fmaxf(Mx, s_m[ww][hh]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = fast_exp2(s_m[ww][hh] - Mx);
+        L = fmaf(s_l[ww][hh], f, L);
+        O = fmaf(s_o[ww][hh][d], f, O);
+      }
+      const size_t bhp = (static_cast<size_t>(mseq) * a.hq + h0 + hh % a.qgroup) * a.num_parts + part;
+      a.ws_o[bhp * D + d] = badc ? __builtin_nanf("") : O / L;
+      if (d == 0) {
+        a.ws_m[bhp] = badc ? 0.f : Mx;
+        a.ws_l[bhp] = badc ? __builtin_nanf("") : L;
+      }
+      continue;
+    }
     float Mx = s_m[0][hh];
 #pragma unroll
     for (int ww = 1; ww < kWaves; ++ww) Mx = fmaxf(Mx, s_m[ww][hh]);
@@ -610,16 +754,23 @@ __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
 
 template <int DT, int D>
 hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
-  dim3 grid(a.hkv, B, a.num_parts);
+  // Shared partitions first (they fill workspace rows the private pass
+  // skips), then every sequence's private partitions, then the reduce.
+  if constexpr (DT != PA_DTYPE_F32) {
+    if (a.n_groups > 0)
+      decode_phase1_mfma<DT, D, 16, PKV_NBUF_MFMA, true>
+          <<<dim3(a.hkv, a.n_groups, a.max_shared_parts), kThreads, 0, st>>>(a);
+  }
+  dim3 grid(a.hkv, B, a.grid_parts);
   switch (group) {
     case 1: decode_phase1<DT, D, 1, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
     case 2: decode_phase1<DT, D, 2, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
     case 4:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, PKV_NBUF_MFMA><<<grid, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, PKV_NBUF_MFMA, false><<<grid, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 4, PKV_NBUF_G4><<<grid, kThreads, 0, st>>>(a);
       break;
     case 8:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, PKV_NBUF_MFMA><<<grid, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, PKV_NBUF_MFMA, false><<<grid, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a);
       break;
     default: return hipErrorInvalidValue;
@@ -672,54 +823,61 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int3
   return ws_layout(B, num_q_heads, head_dim, P).total;
 }
 
-extern "C" int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_tables, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, int32_t max_context_len, int32_t B,
-                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                         int32_t block_size, int32_t num_blocks, float scale,
-                         int32_t partition_tokens, int32_t dtype, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
+                const int32_t* seq_group, const int32_t* groups, int32_t n_groups,
+                int32_t max_shared_parts, int32_t max_private_parts, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const std::string name(fn);
+  auto err_ = [&](int code, const std::string& msg) { return fail(code, name + ": " + msg); };
   if (B < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
-    return fail(PA_ERR_INVALID, "pa_decode: negative size or empty pool");
+    return err_(PA_ERR_INVALID, "negative size or empty pool");
+  if (n_groups < 0 || max_shared_parts < 0 || max_private_parts < 0)
+    return err_(PA_ERR_INVALID, "negative n_groups, max_shared_parts or max_private_parts");
   if (B == 0) { clear_error(); return PA_OK; }
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PA_ERR_INVALID, "pa_decode: null pointer");
+    return err_(PA_ERR_INVALID, "null pointer");
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID, "pa_decode: num_q_heads must be a positive multiple of num_kv_heads");
+    return err_(PA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
   const int group = num_q_heads / num_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: query group size must be 1, 2, 4 or 8");
-  if (block_size != kBlock) return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size must be 16");
+    return err_(PA_ERR_UNSUPPORTED, "query group size must be 1, 2, 4 or 8");
+  if (block_size != kBlock) return err_(PA_ERR_UNSUPPORTED, "block_size must be 16");
   if (head_dim != 64 && head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim must be 64 or 128");
+    return err_(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (dtype != PA_DTYPE_F32 && dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: unknown dtype");
+    return err_(PA_ERR_UNSUPPORTED, "unknown dtype");
   if (partition_tokens < 0 || partition_tokens % kBlock != 0)
-    return fail(PA_ERR_INVALID, "pa_decode: partition_tokens must be 0 or a multiple of 16");
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_decode: scale must be finite");
+    return err_(PA_ERR_INVALID, "partition_tokens must be 0 or a multiple of 16");
+  if (!std::isfinite(scale)) return err_(PA_ERR_INVALID, "scale must be finite");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache)) & 15)
-    return fail(PA_ERR_INVALID, "pa_decode: q and caches must be 16-byte aligned");
+    return err_(PA_ERR_INVALID, "q and caches must be 16-byte aligned");
   const size_t block_bytes = static_cast<size_t>(num_kv_heads) * head_dim * kBlock *
                              (dtype == PA_DTYPE_F32 ? 4 : 2);
   if (block_bytes >= (static_cast<size_t>(1) << 31))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: one block of one layer must be under 2 GiB");
+    return err_(PA_ERR_UNSUPPORTED, "one block of one layer must be under 2 GiB");
   // Grid limits: KV heads on x, sequences on y (<= 65535), partitions on z.
-  if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 sequences");
+  if (B > 65535) return err_(PA_ERR_UNSUPPORTED, "more than 65535 sequences");
 
   DecodeArgs a{};
   a.part_blocks = part_blocks_for(max_context_len, partition_tokens);
   const int32_t nb = (max_context_len + kBlock - 1) / kBlock;
   a.num_parts = nb == 0 ? 1 : (nb + a.part_blocks - 1) / a.part_blocks;
   if (a.num_parts > 65535)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 partitions; use larger partitions");
+    return err_(PA_ERR_UNSUPPORTED, "more than 65535 partitions; use larger partitions");
   const WsLayout wl = ws_layout(B, num_q_heads, head_dim, a.num_parts);
   if (wl.total > 0) {
     if (!workspace || workspace_bytes < wl.total)
-      return fail(PA_ERR_INVALID, "pa_decode: workspace too small (need " +
+      return err_(PA_ERR_INVALID, "workspace too small (need " +
                                       std::to_string(wl.total) + " bytes)");
     if (reinterpret_cast<uintptr_t>(workspace) & 15)
-      return fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
+      return err_(PA_ERR_INVALID, "workspace must be 16-byte aligned");
     char* ws = static_cast<char*>(workspace);
     a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
     a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
@@ -737,6 +895,25 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_cache, const v
   a.hkv = num_kv_heads;
   a.num_blocks = num_blocks;
   a.scale_log2 = scale * kLog2e;
+  a.batch = B;
+  a.qgroup = group;
+  a.grid_parts = a.num_parts;
+  if (n_groups > 0) {
+    if (!seq_group || !groups) return err_(PA_ERR_INVALID, "null plan pointer");
+    if (dtype == PA_DTYPE_F32)
+      return err_(PA_ERR_UNSUPPORTED, "a shared-prefix plan needs F16 or BF16 K/V");
+    if (partition_tokens == 0)
+      return err_(PA_ERR_INVALID, "a shared-prefix plan needs partition_tokens > 0");
+    if (n_groups > 65535 || max_shared_parts > 65535)
+      return err_(PA_ERR_UNSUPPORTED, "more than 65535 plan groups or shared partitions");
+    if (max_shared_parts > 0) {
+      a.seq_group = seq_group;
+      a.groups = groups;
+      a.n_groups = n_groups;
+      a.max_shared_parts = max_shared_parts;
+      if (max_private_parts > 0) a.grid_parts = std::min(a.num_parts, max_private_parts);
+    }
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
@@ -746,7 +923,39 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_cache, const v
     default: err = launch_dt<PA_DTYPE_BF16>(a, B, head_dim, group, st); break;
   }
   if (err != hipSuccess)
-    return fail(PA_ERR_DEVICE, std::string("pa_decode: launch failed: ") + hipGetErrorString(err));
+    return err_(PA_ERR_DEVICE, std::string("launch failed: ") + hipGetErrorString(err));
   clear_error();
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, float scale,
+                         int32_t partition_tokens, int32_t dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, B, num_q_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, scale, partition_tokens, dtype, nullptr, nullptr, 0,
+                     0, 0, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_decode_shared(float* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, int32_t B, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, float scale, int32_t partition_tokens,
+                                int32_t dtype, const int32_t* seq_group, const int32_t* groups,
+                                int32_t n_groups, int32_t max_shared_parts,
+                                int32_t max_private_parts, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return decode_impl("pa_decode_shared", out, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, B, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
+                     dtype, seq_group, groups, n_groups, max_shared_parts, max_private_parts,
+                     workspace, workspace_bytes, stream);
 }

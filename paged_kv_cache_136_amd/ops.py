@@ -8,9 +8,12 @@ runs in the library's kernels; nothing here computes.
 import ctypes
 import math
 
+import numpy as np
 import torch
 
 from ._lib import (PA_DTYPE_BF16, PA_DTYPE_F16, PA_DTYPE_F32, c_vp, check, lib)
+
+SHARED_ROW = 17          # PA_SHARED_ROW: shared partitions, then 16 member slots
 
 _DTYPES = {torch.float32: PA_DTYPE_F32, torch.float16: PA_DTYPE_F16, torch.bfloat16: PA_DTYPE_BF16}
 
@@ -135,13 +138,8 @@ def pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partiti
                                            partition_tokens)
 
 
-def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
-              partition_tokens=512, out=None, workspace=None, stream=None):
-    """Paged decode attention; returns float32 out [B, Hq, D].
-
-    q [B, Hq, D] and caches [num_blocks, 16, Hkv, D] share a dtype;
-    block_tables int32 [B, max_blocks]; context_lens int32 [B];
-    max_context_len is a host int bounding context_lens."""
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                 partition_tokens, out, workspace):
     _dev(q, k_cache, v_cache, block_tables, context_lens)
     B, hq, d = q.shape
     nb, bs, hkv, d2 = k_cache.shape
@@ -164,11 +162,65 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
     ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
-    check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                          block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
-                          int(max_context_len), B, hq, hkv, d, bs, nb, float(scale),
-                          int(partition_tokens), _dtype_code(q), ws_ptr, ws_bytes,
-                          _stream(stream)))
+    head = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+            int(max_context_len), B, hq, hkv, d, bs, nb, float(scale), int(partition_tokens),
+            _dtype_code(q))
+    return out, head, (ws_ptr, ws_bytes)
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale=None,
+              partition_tokens=512, out=None, workspace=None, stream=None):
+    """Paged decode attention; returns float32 out [B, Hq, D].
+
+    q [B, Hq, D] and caches [num_blocks, 16, Hkv, D] share a dtype;
+    block_tables int32 [B, max_blocks]; context_lens int32 [B];
+    max_context_len is a host int bounding context_lens."""
+    out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                 max_context_len, scale, partition_tokens, out, workspace)
+    check(lib().pa_decode(*head, *ws, _stream(stream)))
+    return out
+
+
+def pa_shared_plan(block_tables, context_lens, block_size, partition_tokens, query_group):
+    """Shared-prefix plan from host int32 arrays tables [B, max_blocks] and
+    lens [B].  Returns (seq_group int32 [B], groups int32 [n, 17],
+    max_shared_parts, max_private_parts)."""
+    tab = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if tab.ndim != 2 or lens.shape != (tab.shape[0],):
+        raise ValueError("tables must be [B, max_blocks] and lens [B]")
+    B = tab.shape[0]
+    seq_group = np.empty(B, dtype=np.int32)
+    groups = np.empty((max(B // 2, 1), SHARED_ROW), dtype=np.int32)
+    n, mx, mp = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    p = ctypes.POINTER(ctypes.c_int32)
+    check(lib().pa_shared_plan(tab.ctypes.data_as(p), tab.shape[1], lens.ctypes.data_as(p), B,
+                               int(block_size), int(partition_tokens), int(query_group),
+                               seq_group.ctypes.data_as(p), groups.ctypes.data_as(p),
+                               ctypes.byref(n), ctypes.byref(mx), ctypes.byref(mp)))
+    return seq_group, groups[:n.value].copy(), mx.value, mp.value
+
+
+def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, max_context_len, seq_group,
+                     groups, max_shared_parts, max_private_parts=0, scale=None,
+                     partition_tokens=512, out=None, workspace=None, stream=None):
+    """pa_decode with a shared-prefix plan: seq_group int32 [B] and groups
+    int32 [n, 17] on the GPU (from pa_shared_plan); max_shared_parts and
+    max_private_parts are the plan's host-side grid bounds (0 for the
+    latter: no bound)."""
+    out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                 max_context_len, scale, partition_tokens, out, workspace)
+    n = 0 if groups is None else groups.shape[0]
+    if n:
+        _dev(seq_group, groups)
+        if (seq_group.dtype != torch.int32 or seq_group.shape != (q.shape[0],)
+                or groups.dtype != torch.int32 or groups.shape != (n, SHARED_ROW)
+                or not groups.is_contiguous()):
+            raise ValueError("seq_group must be int32 [B] and groups int32 [n, 17]")
+    check(lib().pa_decode_shared(*head, seq_group.data_ptr() if n else None,
+                                 groups.data_ptr() if n else None, n, int(max_shared_parts),
+                                 int(max_private_parts), *ws, _stream(stream)))
     return out
 
 

@@ -362,3 +362,19 @@ def test_fork_cow_full_flow():
     want = oracle.ref_decode(host_f32(q)[rows], kf, vf, ref_tables, clens[rows])
     err = np.abs(out.cpu().numpy()[rows] - want).max()
     assert err <= TOL["f16"], err
+    # The same batch through the shared-prefix path: one group per prompt,
+    # the 128 prompt blocks (4 partitions) read once per group.
+    sg, groups, mx, mp = pkv.pa_shared_plan(tables, clens, bs, cfg["partition_tokens"], 1)
+    assert len(groups) == P and mx == 4 and mp == 1
+    assert sorted(int(m) for m in groups[:, 1:].ravel() if m >= 0) == list(range(P * F))
+    say("fork_cow: shared-prefix decode 512 forks")
+    out_s = pkv.pa_decode_shared(q, k, v, torch.from_numpy(tables).cuda(),
+                                 torch.from_numpy(clens).cuda(), L0 + 1 + X,
+                                 torch.from_numpy(sg).cuda(), torch.from_numpy(groups).cuda(), mx,
+                                 mp, partition_tokens=cfg["partition_tokens"])
+    torch.cuda.synchronize()
+    got_s = out_s.cpu().numpy()
+    assert np.isfinite(got_s).all()
+    err = np.abs(got_s[rows] - want).max()
+    assert err <= TOL["f16"], err
+    assert np.abs(got_s - out.cpu().numpy()).max() <= TOL["f16"]

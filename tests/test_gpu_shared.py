@@ -1,0 +1,256 @@
+"""GPU parity of pa_decode_shared: decode that reads the blocks a group of
+forked sequences shares ("day31" fork and copy-on-write; "P06 ·
+BlockManager" prefix sharing) once for the whole group.
+
+The result is the attention pa_decode computes, so every case is checked
+against the oracle's fp64 paged attention on the same seeded inputs (slots
+no sequence attends hold NaN), with plans from the library's planner and
+with hand-corrupted plans: a member whose own table disagrees with the
+group's source row must come out NaN, and every other way a plan can be
+wrong (a member not pointing at its group, too many partitions, too few
+blocks, duplicates) must fall back to the private path with correct output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.families import beam_family, fork_family
+from tests.gpu_util import TOL, TORCH_DTYPES, host_f32, make_cache, poison_mask, say
+
+pytestmark = pytest.mark.gpu
+
+pkv = pytest.importorskip("paged_kv_cache_136_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+BS = 16
+
+
+class Case:
+    """Seeded device inputs for a batch given by host tables and lengths."""
+
+    def __init__(self, tables, lens, hq, hkv, d, dtype, seed, num_blocks=None):
+        self.tables, self.lens = tables, lens
+        self.hq, self.hkv, self.d, self.dtype = hq, hkv, d, dtype
+        nb = num_blocks or int(tables.max()) + 1
+        self.k, self.v = make_cache(nb, BS, hkv, d, dtype, seed,
+                                    poison=poison_mask(tables, lens, nb, BS))
+        self.q = workloads.normal_torch((len(lens), hq, d), seed + 7, TORCH_DTYPES[dtype], "cuda")
+        self.max_len = int(lens.max())
+
+    def dev(self, a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    def plan(self, pt):
+        return pkv.pa_shared_plan(self.tables, self.lens, BS, pt, self.hq // self.hkv)
+
+    def shared(self, plan, pt, tables=None, lens=None):
+        """plan: (seq_group, groups, max_shared_parts[, max_private_parts])."""
+        sg, groups, mx = plan[:3]
+        mp = plan[3] if len(plan) > 3 else 0
+        t = self.tables if tables is None else tables
+        n = self.lens if lens is None else lens
+        out = pkv.pa_decode_shared(self.q, self.k, self.v, self.dev(t), self.dev(n),
+                                   self.max_len, self.dev(sg), self.dev(groups.reshape(-1, 17)),
+                                   mx, mp, partition_tokens=pt)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    def private(self, pt):
+        out = pkv.pa_decode(self.q, self.k, self.v, self.dev(self.tables), self.dev(self.lens),
+                            self.max_len, partition_tokens=pt)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    def want(self, tables=None, lens=None):
+        t = self.tables if tables is None else tables
+        n = self.lens if lens is None else lens
+        return oracle.ref_decode(host_f32(self.q), host_f32(self.k), host_f32(self.v), t, n)
+
+
+def _extra(n, seed, hi=60):
+    return np.random.default_rng(seed).integers(1, hi, size=n)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_shared_fork_families(dtype, d, group):
+    """Four fork families (prompts 700, 1100, 530 and 95 tokens; 16/group
+    members, at most 4), ragged appends, two unforked sequences; 128-token
+    partitions."""
+    hkv, forks = 2, min(4, 16 // group)
+    prompts = [700, 1100, 530, 95]
+    tables, lens = fork_family(prompts, forks, _extra(len(prompts) * forks, d + group),
+                               singles=[300, 17], seed=group)
+    say("shared forks", dtype, d, group)
+    c = Case(tables, lens, hkv * group, hkv, d, dtype, seed=31 + d + group)
+    plan = c.plan(128)
+    assert len(plan[1]) == len(prompts) - 1      # the 95-token family shares no partition
+    got, want = c.shared(plan, 128), c.want()
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max()
+    assert err <= TOL[dtype], err
+    assert np.abs(got - c.private(128)).max() <= TOL[dtype]
+
+
+@pytest.mark.parametrize("pt", [16, 64, 512])
+def test_shared_partition_sizes(pt):
+    tables, lens = fork_family([1500, 640], 8, _extra(16, pt, 200), seed=5)
+    say("shared partitions", pt)
+    c = Case(tables, lens, 8, 8, 128, "f16", seed=pt)
+    plan = c.plan(pt)
+    assert len(plan[1]) == 2
+    err = np.abs(c.shared(plan, pt) - c.want()).max()
+    assert err <= TOL["f16"], err
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("f16", 4, 4), ("bf16", 16, 4)])
+def test_shared_beam_tree(dtype, hq, hkv):
+    """Beam-search trees: sharing at arbitrary depths, groups cut from
+    sorted rows."""
+    tables, lens = beam_family([300, 700, 150, 1200], 4, 60, seed=8)
+    say("shared beam", dtype, hq, hkv)
+    c = Case(tables, lens, hq, hkv, 128, dtype, seed=77)
+    plan = c.plan(64)
+    assert len(plan[1]) > 0
+    err = np.abs(c.shared(plan, 64) - c.want()).max()
+    assert err <= TOL[dtype], err
+
+
+def _family_case(seed=3):
+    """Two families of 4 forks (1000 and 700 tokens) and one single; f16,
+    4 heads x 128; 128-token partitions."""
+    tables, lens = fork_family([1000, 700], 4, _extra(8, seed, 40), singles=[333], seed=seed)
+    return Case(tables, lens, 4, 4, 128, "f16", seed=seed)
+
+
+def _members(groups, gi):
+    return [int(m) for m in groups[gi, 1:] if m >= 0]
+
+
+def test_shared_table_mismatch_gives_nan():
+    """A member whose own table differs from the group's source row inside
+    the shared partitions gets NaN rows; everyone else stays exact."""
+    c = _family_case()
+    sg, groups, mx, _ = c.plan(128)
+    mem = _members(groups, 0)
+    victim = mem[2]
+    bad = c.tables.copy()
+    bad[victim, 3] = bad[mem[0], 40]                # another block that row also holds
+    say("shared mismatch")
+    got = c.shared((sg, groups, mx), 128, tables=bad)
+    want = c.want(tables=bad)
+    assert np.isnan(got[victim]).all()
+    others = [b for b in range(len(c.lens)) if b != victim]
+    assert np.abs(got[others] - want[others]).max() <= TOL["f16"]
+
+
+def test_shared_source_out_of_range_gives_nan():
+    c = _family_case()
+    sg, groups, mx, _ = c.plan(128)
+    g = groups.copy()
+    mem = _members(g, 1)
+    g[1, 1] = len(c.lens) + 3                          # source slot outside the batch
+    say("shared bad source")
+    got = c.shared((sg, g, mx), 128)
+    want = c.want()
+    assert np.isnan(got[mem[1:]]).all()
+    rest = [b for b in range(len(c.lens)) if b not in mem[1:]]
+    assert np.abs(got[rest] - want[rest]).max() <= TOL["f16"]
+
+
+def test_shared_plan_mistakes_fall_back_to_private():
+    """Members that the rule excludes are computed privately: not pointing
+    at their group, listed twice, too few blocks, P beyond
+    max_shared_parts, P = 0, a group index past n_groups."""
+    c = _family_case()
+    sg, groups, mx, _ = c.plan(128)
+    want = c.want()
+    B = len(c.lens)
+    cases = {}
+    s1 = sg.copy(); s1[_members(groups, 0)[1]] = -1
+    cases["not pointing at its group"] = (s1, groups, mx)
+    s2 = sg.copy(); s2[_members(groups, 0)[2]] = 1
+    cases["pointing at another group"] = (s2, groups, mx)
+    g3 = groups.copy(); g3[0, 4] = g3[0, 2]
+    cases["listed twice"] = (sg, g3, mx)
+    cases["P beyond max_shared_parts"] = (sg, groups, int(groups[:, 0].min()) - 1)
+    g5 = groups.copy(); g5[1, 0] = 0
+    cases["P = 0"] = (sg, g5, mx)
+    s6 = sg.copy(); s6[B - 1] = len(groups) + 4
+    cases["group past n_groups"] = (s6, groups, mx)
+    g7 = groups.copy(); g7[0, 0] = 50
+    cases["P past every member's blocks"] = (sg, g7, 64)
+    for name, plan in cases.items():
+        say("shared fallback", name)
+        got = c.shared(plan, 128)
+        assert np.isfinite(got).all(), name
+        assert np.abs(got - want).max() <= TOL["f16"], name
+    # a member whose length leaves no private block past P partitions
+    lens = c.lens.copy()
+    m = _members(groups, 0)[3]
+    lens[m] = int(groups[0, 0]) * 128
+    say("shared fallback short member")
+    got = c.shared((sg, groups, mx), 128, lens=lens)
+    assert np.abs(got - c.want(lens=lens)).max() <= TOL["f16"]
+
+
+def test_shared_private_grid_bound():
+    """The planner's private bound runs every sequence; one below it turns
+    exactly the sequences with more private partitions into NaN rows."""
+    c = _family_case()
+    sg, groups, mx, mp = c.plan(128)
+    pb = 128 // BS
+    priv = []
+    for b, n in enumerate(c.lens):
+        nparts = -(-(-(-int(n) // BS)) // pb)
+        priv.append(nparts - (int(groups[sg[b], 0]) if sg[b] >= 0 else 0))
+    assert mp == max(priv) and mp > 1
+    want = c.want()
+    say("shared private bound", mp)
+    got = c.shared((sg, groups, mx, mp), 128)
+    assert np.abs(got - want).max() <= TOL["f16"]
+    say("shared private bound short", mp - 1)
+    got = c.shared((sg, groups, mx, mp - 1), 128)
+    over = [b for b in range(len(priv)) if priv[b] > mp - 1]
+    ok = [b for b in range(len(priv)) if priv[b] <= mp - 1]
+    assert over and ok
+    assert np.isnan(got[over]).all()
+    assert np.abs(got[ok] - want[ok]).max() <= TOL["f16"]
+
+
+def test_shared_empty_plan_is_pa_decode():
+    """n_groups == 0 launches exactly pa_decode's kernels: bit-identical."""
+    c = _family_case()
+    say("shared empty plan")
+    empty = (np.full(len(c.lens), -1, np.int32), np.zeros((0, 17), np.int32), 0)
+    assert np.array_equal(c.shared(empty, 128), c.private(128))
+
+
+def test_shared_rejects_unsupported():
+    c = _family_case()
+    plan = c.plan(128)
+    sg, groups = c.dev(plan[0]), c.dev(plan[1])
+    tab, lens = c.dev(c.tables), c.dev(c.lens)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.pa_decode_shared(c.q, c.k, c.v, tab, lens, c.max_len, sg, groups, plan[2],
+                             partition_tokens=0)
+    with pytest.raises(pkv.PagedKVError):
+        pkv.pa_decode_shared(c.q, c.k, c.v, tab, lens, c.max_len, sg, groups, plan[2], -1,
+                             partition_tokens=128)
+    k32, v32, q32 = c.k.float(), c.v.float(), c.q.float()
+    with pytest.raises(pkv.PagedKVError):
+        pkv.pa_decode_shared(q32, k32, v32, tab, lens, c.max_len, sg, groups, plan[2],
+                             partition_tokens=128)
