@@ -64,6 +64,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 #ifndef PKV_MFMA_K_LDS
 #define PKV_MFMA_K_LDS 1           // K rows staged through LDS (row-layout loads) on the MFMA path
 #endif
+#ifndef PKV_WG_MAP
+#define PKV_WG_MAP 1               // 0: head = x; 1: head = (x + y + z) mod Hkv; 2: XCD tiles
+#endif
 #ifndef PKV_NBUF_G4
 #define PKV_NBUF_G4 1              // same, query group of 4 (VGPR-limited)
 #endif
@@ -97,6 +100,60 @@ struct DecodeArgs {
 
 __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
   return n >= 0 && n <= a.max_len && (n + kBlock - 1) / kBlock <= a.max_blocks;
+}
+
+// Workgroup -> (KV head, y, z).  The hardware deals workgroups to the 8
+// XCDs round-robin by linear id, and x (the head) is the fastest index, so
+// with head = x every XCD would read the same head columns of every block
+// (with 32 heads, XCD k gets heads k, k+8, ...: fixed 256-byte columns of
+// each 8 KB row).  Map 1 (default) rotates the head by rot: every XCD still
+// gets a share of every (y, z) tile, which keeps the XCDs balanced when
+// tiles differ in cost (mixed lengths), while its reads spread over all
+// head columns; measured 3-5% more bandwidth than map 0.  The caller picks
+// rot so that sequences sharing blocks (forks, beams: same first block)
+// keep one head -> XCD assignment and meet their shared blocks in that
+// XCD's L2.  Map 2 gives each XCD whole tiles (linear id
+// L = 8 * (Hkv * q + head) + xcd serves tile 8q + xcd, a last partial group
+// of tiles dealt head-fastest): as fast or slightly faster when all tiles
+// cost the same, 10% slower on mixed lengths, where XCD k always gets the
+// sequences b = k mod 8.
+struct WgCoord {
+  int g, y, z;
+};
+__device__ __forceinline__ WgCoord wg_coord(int hkv, uint32_t rot) {
+  if constexpr (PKV_WG_MAP == 1) {
+    return {static_cast<int>((blockIdx.x + rot) % hkv), static_cast<int>(blockIdx.y),
+            static_cast<int>(blockIdx.z)};
+  } else if constexpr (PKV_WG_MAP == 2) {
+    const uint32_t Y = gridDim.y;
+    const uint32_t L = blockIdx.x + hkv * (blockIdx.y + Y * blockIdx.z);
+    const uint32_t T = Y * gridDim.z;               // tiles
+    const uint32_t full = (T / 8) * 8 * hkv;        // ids in whole groups of 8 tiles
+    uint32_t g, tile;
+    if (L < full) {
+      const uint32_t slot = L >> 3;
+      g = slot % hkv;
+      tile = (slot / hkv) * 8 + (L & 7);
+    } else {
+      const uint32_t loc = L - full;
+      g = loc % hkv;
+      tile = (T / 8) * 8 + loc / hkv;
+    }
+    return {static_cast<int>(g), static_cast<int>(tile % Y), static_cast<int>(tile / Y)};
+  } else {
+    return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
+  }
+}
+
+// Rotation for a sequence's workgroups: a hash of its first block id
+// (sequences sharing a prefix share it; unrelated ones get spread-out
+// values, also when a free list hands out blocks in order) plus the
+// partition.  Only the private grid (y = sequence) uses it.
+__device__ __forceinline__ uint32_t seq_rot(const int32_t* tables, int32_t max_blocks) {
+  if (PKV_WG_MAP != 1) return 0;
+  const uint32_t e0 =
+      max_blocks > 0 ? static_cast<uint32_t>(tables[static_cast<size_t>(blockIdx.y) * max_blocks]) : 0u;
+  return ((e0 * 2654435761u) >> 16) + blockIdx.z;
 }
 
 __device__ __forceinline__ int num_parts_of(int n, int part_blocks) {
@@ -203,14 +260,15 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   __shared__ float s_m[kWaves][G], s_l[kWaves][G];
   __shared__ float s_o[kWaves][G][D];
 
-  // Grid: x = KV head, y = sequence, z = partition.  Workgroups are dealt to
-  // the 8 XCDs round-robin by linear id, so the fastest index must not
-  // correlate with work size: heads of one (sequence, partition) cost the
-  // same, and partitions that a sequence does not have (the cheap exits)
-  // collect at the end of the grid.
+  // Grid: x = KV head (rotated by wg_coord), y = sequence, z = partition.
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id, so the
+  // fastest index must not correlate with work size: heads of one
+  // (sequence, partition) cost the same, and partitions that a sequence
+  // does not have (the cheap exits) collect at the end of the grid.
   // With a shared-prefix plan, a member's first partitions belong to the
   // shared kernel and z counts from the first private one.
-  const int g = blockIdx.x, b = blockIdx.y;
+  const WgCoord wc = wg_coord(a.hkv, seq_rot(a.tables, a.max_blocks));
+  const int g = wc.g, b = wc.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
   const int n = a.lens[b];
@@ -218,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   const int nblk = valid ? (n + kBlock - 1) / kBlock : 0;
   const int nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
   const int start = shared_start(a, b, nblk);
-  const int part = static_cast<int>(blockIdx.z) + start;
+  const int part = wc.z + start;
   if (part >= nparts) return;
   const int h0 = g * G;
 
@@ -424,13 +482,15 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       reinterpret_cast<char (*)[kBlock * VROW]>(s_kv + (PKV_MFMA_K_LDS ? KVBUF : 0));
   float (*s_o)[G][D] = reinterpret_cast<float (*)[G][D]>(s_kv + (O_UNION ? 0 : KBUFS * KVBUF));
 
-  const int g = blockIdx.x;
+  const WgCoord wc = wg_coord(a.hkv, SHARED ? blockIdx.y + blockIdx.z
+                                            : seq_rot(a.tables, a.max_blocks));
+  const int g = wc.g;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t = lane & 15, qa = lane >> 4;
   const int h0 = g * (SHARED ? a.qgroup : G);
   // b: sequence (private) or plan group (shared).  n: tokens the blocks
   // [first, last) are cut from; trow: the table row they are read from.
-  int b = blockIdx.y, part, n, nblk, nparts, first, last;
+  int b = wc.y, part, n, nblk, nparts, first, last;
   bool short_grid = false;
   const int32_t* trow;
   // SHARED: column t's member (-1 if none) and its query head; the member
@@ -441,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   if constexpr (SHARED) {
     const int32_t* row = a.groups + static_cast<size_t>(b) * PA_SHARED_ROW;
     const int P = row[0];
-    part = blockIdx.z;
+    part = wc.z;
     if (P < 1 || P > a.max_shared_parts || part >= P) return;
     const int slots = PA_SHARED_MAX_MEMBERS / a.qgroup;
     // Membership as the private kernels decide it.
@@ -473,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     nblk = valid ? (n + kBlock - 1) / kBlock : 0;
     nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
     const int start = shared_start(a, b, nblk);
-    part = static_cast<int>(blockIdx.z) + start;
+    part = wc.z + start;
     if (part >= nparts) return;
     short_grid = nparts - start > static_cast<int>(gridDim.z);
     if (!valid || n == 0) {
