@@ -46,6 +46,8 @@ def parse_args():
                    choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap", "serve", "beam",
                             "prefill"],
                    help="mixed_7b is the headline workload; the others are reported lines")
+    p.add_argument("--shared-prefix", choices=["on", "off"], default=None,
+                   help="serve: decode with pa_decode_shared (default: the workload's choice)")
     p.add_argument("--partition-tokens", type=int, default=-1,
                    help="split-KV partition size (default: the workload's, 512)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -552,8 +554,10 @@ def run_serve(args, torch, pkv, workloads):
     from paged_kv_cache_136_amd.engine import DecodeEngine
     L, H, D, bs, NB, batch, host_slots, n_req = 32, 32, 128, 16, 16384, 128, 256, 1024
     dev = torch.device("cuda:0")
+    pt = args.partition_tokens if args.partition_tokens >= 0 else 512
+    shared = args.shared_prefix == "on"
     eng = DecodeEngine(L, NB, bs, H, H, D, torch.float16, batch, host_slots, True,
-                       partition_tokens=512)
+                       partition_tokens=pt, shared_prefix=shared)
     rng = np.random.Generator(np.random.PCG64(11))
     system = workloads.token_ids(256, seed=12)
     lo, hi = math.log(50), math.log(2048)
@@ -609,7 +613,9 @@ def run_serve(args, torch, pkv, workloads):
                    "requests": n_req, "prompts": "log-uniform [50, 2048], half after a shared "
                    "256-token system prompt", "budgets": "log-uniform [16, 512]",
                    "timing": "wall clock over whole engine steps (host scheduling, copies, "
-                             "writes, 32 decode launches, one sync per step)"},
+                             "writes, 32 decode launches, one sync per step)",
+                   "partition_tokens": pt, "shared_prefix_decode": shared},
+        "shared_groups_per_step": round(eng.shared_groups / max(eng.step_no, 1), 2),
         "kv_gbs": round(kv_bytes / wall / 1e9, 2),
         "pct_hbm_peak": round(100 * kv_bytes / wall / 1e9 / PEAK_HBM_GBS, 2),
         "host_sched_ms_per_step": round((eng.host_seconds - host0) / args.steps * 1e3, 4),
@@ -626,9 +632,11 @@ def run_beam(args, torch, pkv, workloads):
     step each group's 8 beams are re-forked from seeded parents at their
     current (arbitrary) positions, the old beams freed, and all 512 beams
     append a token: beams sharing a partly filled last block copy it
-    (pa_copy_blocks with many small pairs), then pa_write_kv and pa_decode
-    over the 512 beams.  Reported: step rate, copy pairs per step and the
-    copy kernel's rate, decode KV GB/s (logical and over unique blocks)."""
+    (pa_copy_blocks with many small pairs), then pa_write_kv and
+    pa_decode_shared (host plan every step) over the 512 beams.  Reported:
+    step rate, copy pairs per step and the copy kernel's rate, decode KV
+    GB/s (logical and over unique blocks), and plain pa_decode against
+    pa_decode_shared on the final batch."""
     cfg = workloads.CONFIGS["beam"]
     bs, NB, H, D, G, W = cfg["bs"], cfg["num_blocks"], cfg["hkv"], cfg["d"], cfg["groups"], cfg["beams"]
     dev = torch.device("cuda:0")
@@ -672,11 +680,13 @@ def run_beam(args, torch, pkv, workloads):
         flat = np.array([s for g in beams for s in g], dtype=np.int64)
         slots, pairs = bm.append_slots(flat, np.arange(B, dtype=np.int32))
         tables, lens = bm.export_batch(flat, width, pad_block=0)
+        sg, groups, mx, mp = pkv.pa_shared_plan(tables, lens, bs, 512, cfg["hq"] // H)
         host = time.perf_counter() - h0
         d_slot = torch.from_numpy(slots).to(dev)
         d_pairs = torch.from_numpy(pairs).to(dev) if len(pairs) else None
         d_tab = torch.from_numpy(tables).to(dev)
         d_len = torch.from_numpy(lens).to(dev)
+        d_sg, d_gr = torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev)
         if ev is not None:
             ev[0].record()
         if d_pairs is not None:
@@ -686,12 +696,15 @@ def run_beam(args, torch, pkv, workloads):
         pkv.pa_write_kv(k, v, kn, vn, d_slot)
         if ev is not None:
             ev[2].record()
-        pkv.pa_decode(q, k, v, d_tab, d_len, int(lens.max()), partition_tokens=512, out=out,
-                      workspace=ws)
+        pkv.pa_decode_shared(q, k, v, d_tab, d_len, int(lens.max()), d_sg, d_gr, mx, mp,
+                             partition_tokens=512, out=out, workspace=ws)
         if ev is not None:
             ev[3].record()
         uniq = len(np.unique(np.concatenate([tables[i, :-(-int(n) // bs)] for i, n in enumerate(lens)])))
+        last[:] = [d_tab, d_len, tables, lens]
         return len(pairs), int(lens.sum()), uniq, host
+
+    last = [None] * 4
 
     for _ in range(args.warmup):
         step()
@@ -706,6 +719,31 @@ def run_beam(args, torch, pkv, workloads):
     copy_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    # The final batch again: plain pa_decode against pa_decode_shared with a
+    # host plan (beams of a group share their prefix up to the last fork).
+    d_tab, d_len, tables, lens = last
+    mlen = int(lens.max())
+
+    def timed(fn, reps=10):
+        ev = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    cmp = {"plain_pa_decode_ms": timed(lambda: pkv.pa_decode(
+        q, k, v, d_tab, d_len, mlen, partition_tokens=512, out=out, workspace=ws))}
+    for pt in (512, 128):
+        sg, groups, mx, mp = pkv.pa_shared_plan(tables, lens, bs, pt, cfg["hq"] // H)
+        d_sg, d_gr = torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev)
+        ws2 = torch.empty(max(pkv.pa_decode_workspace_bytes(B, cfg["hq"], D, mlen, pt), 1),
+                          dtype=torch.uint8, device=dev)
+        cmp[f"shared_pt{pt}"] = {"groups": len(groups), "shared_partitions": int(groups[:, 0].sum()),
+                                 "ms": timed(lambda: pkv.pa_decode_shared(
+                                     q, k, v, d_tab, d_len, mlen, d_sg, d_gr, mx, mp,
+                                     partition_tokens=pt, out=out, workspace=ws2))}
     npairs = np.array([x[0] for x in info])
     toks = np.array([x[1] for x in info], dtype=np.float64)
     uniq = np.array([x[2] for x in info], dtype=np.float64)
@@ -723,7 +761,8 @@ def run_beam(args, torch, pkv, workloads):
                    "kv_heads": H, "q_heads": cfg["hq"], "head_dim": D, "block_size": bs, "num_blocks": NB,
                    "partition_tokens": 512,
                    "timing": "GPU events per step (COW copies + write + decode); value counts every "
-                             "beam's tokens (shared blocks once per beam)"},
+                             "beam's tokens (shared blocks once per beam)",
+                   "decode": "pa_decode_shared with a per-step host plan"},
         "beams_per_s": round(B * args.steps / (step_ms.sum() * 1e-3), 1),
         "unique_kv_gbs": round(float(uniq.sum() * bs * per_tok / (dec_ms.sum() * 1e-3) / 1e9), 2),
         "cow_pairs_per_step": round(float(npairs.mean()), 1),
@@ -732,6 +771,7 @@ def run_beam(args, torch, pkv, workloads):
         if with_pairs.any() else None,
         "decode_ms_per_step": round(float(dec_ms.mean()), 4),
         "host_ms_per_step": round(float(np.mean([x[3] for x in info]) * 1e3), 4),
+        "final_batch_decode": cmp,
         "roofline": None, "cpu_baseline": None, "wall_s": round(wall, 3),
     }
 

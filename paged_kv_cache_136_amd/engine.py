@@ -8,7 +8,10 @@ work through the library's calls, in the order the plan requires:
   3. swap-out copies (pa_swap_out) of preempted requests;
   4. copy-on-write copies (pa_copy_blocks);
   5. the batch's K/V writes (pa_write_kv) at the appended slots;
-  6. decode (pa_decode) of the batch, every layer.
+  6. decode (pa_decode) of the batch, every layer; with ``shared_prefix``
+     the host plans shared-prefix groups once per step (pa_shared_plan) and
+     every layer decodes with pa_decode_shared, reading blocks that several
+     sequences share (a common system prompt, forks) once per group.
 
 There is no model here: the caller supplies the K/V rows to write, the
 queries and the sampled tokens through functions, so every value the
@@ -22,8 +25,8 @@ import numpy as np
 import torch
 
 from .block_manager import BlockManager
-from .ops import (pa_copy_blocks, pa_decode, pa_decode_workspace_bytes, pa_swap_in, pa_swap_out,
-                  pa_write_kv, swap_record_bytes)
+from .ops import (pa_copy_blocks, pa_decode, pa_decode_shared, pa_decode_workspace_bytes,
+                  pa_shared_plan, pa_swap_in, pa_swap_out, pa_write_kv, swap_record_bytes)
 from .scheduler import Scheduler
 
 
@@ -34,11 +37,15 @@ class DecodeEngine:
 
     def __init__(self, num_layers, num_blocks, block_size, num_kv_heads, num_q_heads, head_dim,
                  dtype, max_batch, host_slots, enable_prefix_cache=True, partition_tokens=512,
-                 device="cuda", caches=None):
+                 device="cuda", caches=None, shared_prefix=False):
         self.L, self.nb, self.bs = num_layers, num_blocks, block_size
         self.hkv, self.hq, self.d, self.dtype = num_kv_heads, num_q_heads, head_dim, dtype
         self.dev = torch.device(device)
         self.partition_tokens = partition_tokens
+        if shared_prefix and (dtype == torch.float32 or partition_tokens <= 0):
+            raise ValueError("shared_prefix needs 16-bit caches and partition_tokens > 0")
+        self.shared_prefix = shared_prefix
+        self.shared_groups = 0           # groups planned, summed over steps
         self.bm = BlockManager(num_blocks, block_size, enable_prefix_cache)
         self.sched = Scheduler(self.bm, max_batch, host_slots)
         if caches is None:
@@ -98,6 +105,14 @@ class DecodeEngine:
             slots = torch.from_numpy(plan["slots"].copy()).to(self.dev)
             h0 = time.perf_counter()
             tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
+            splan = None
+            if self.shared_prefix:
+                sg, groups, mx, mp = pa_shared_plan(tables, lens, self.bs, self.partition_tokens,
+                                                    self.hq // self.hkv)
+                self.shared_groups += len(groups)
+                if len(groups):
+                    splan = (torch.from_numpy(sg).to(self.dev),
+                             torch.from_numpy(groups).to(self.dev), mx, mp)
             self.host_seconds += time.perf_counter() - h0
             max_len = int(lens.max())
             d_tab = torch.from_numpy(tables).to(self.dev)
@@ -108,9 +123,15 @@ class DecodeEngine:
             for layer in range(self.L):
                 k, v = kv_rows(layer, "decode", plan)
                 pa_write_kv(self.k[layer], self.v[layer], k, v, slots)
-                outs.append(pa_decode(q_rows(layer, plan), self.k[layer], self.v[layer], d_tab,
-                                      d_len, max_len, partition_tokens=self.partition_tokens,
-                                      workspace=self.ws))
+                if splan is None:
+                    outs.append(pa_decode(q_rows(layer, plan), self.k[layer], self.v[layer], d_tab,
+                                          d_len, max_len, partition_tokens=self.partition_tokens,
+                                          workspace=self.ws))
+                else:
+                    outs.append(pa_decode_shared(q_rows(layer, plan), self.k[layer], self.v[layer],
+                                                 d_tab, d_len, max_len, *splan,
+                                                 partition_tokens=self.partition_tokens,
+                                                 workspace=self.ws))
         torch.cuda.current_stream().synchronize()
         owed = ids.tolist() + plan["admitted"].tolist()
         toks = sample(owed, outs)
