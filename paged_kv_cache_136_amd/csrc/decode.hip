@@ -73,9 +73,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 
 struct DecodeArgs {
   float* out;            // [B][Hq][D]
-  float* ws_o;           // [B][Hq][P][D]  partition output, normalized
-  float* ws_m;           // [B][Hq][P]     partition max (exp2 domain)
-  float* ws_l;           // [B][Hq][P]     partition sum
+  float* ws_o;           // [B][Hkv][P][G][D]  partition output, normalized
+  float* ws_m;           // [B][Hkv][P][G]     partition max (exp2 domain)
+  float* ws_l;           // [B][Hkv][P][G]     partition sum
   const char* q;         // [B][Hq][D]
   const char* k;         // [num_blocks][16][Hkv][D]
   const char* v;
@@ -120,11 +120,8 @@ __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
 struct WgCoord {
   int g, y, z;
 };
-__device__ __forceinline__ WgCoord wg_coord(int hkv, uint32_t rot) {
-  if constexpr (PKV_WG_MAP == 1) {
-    return {static_cast<int>((blockIdx.x + rot) % hkv), static_cast<int>(blockIdx.y),
-            static_cast<int>(blockIdx.z)};
-  } else if constexpr (PKV_WG_MAP == 2) {
+__device__ __forceinline__ WgCoord wg_coord(int hkv) {
+  if constexpr (PKV_WG_MAP == 2) {
     const uint32_t Y = gridDim.y;
     const uint32_t L = blockIdx.x + hkv * (blockIdx.y + Y * blockIdx.z);
     const uint32_t T = Y * gridDim.z;               // tiles
@@ -145,15 +142,55 @@ __device__ __forceinline__ WgCoord wg_coord(int hkv, uint32_t rot) {
   }
 }
 
-// Rotation for a sequence's workgroups: a hash of its first block id
-// (sequences sharing a prefix share it; unrelated ones get spread-out
-// values, also when a free list hands out blocks in order) plus the
-// partition.  Only the private grid (y = sequence) uses it.
-__device__ __forceinline__ uint32_t seq_rot(const int32_t* tables, int32_t max_blocks) {
-  if (PKV_WG_MAP != 1) return 0;
-  const uint32_t e0 =
-      max_blocks > 0 ? static_cast<uint32_t>(tables[static_cast<size_t>(blockIdx.y) * max_blocks]) : 0u;
-  return ((e0 * 2654435761u) >> 16) + blockIdx.z;
+__device__ __forceinline__ int rotate_head(int g, int hkv, uint32_t rot) {
+  return PKV_WG_MAP == 1 ? static_cast<int>((g + rot) % hkv) : g;
+}
+
+// The scalar reads a private-grid workgroup starts with, issued together
+// so the first K/V loads wait for one round trip: the sequence's length,
+// its first table entry (for the head rotation) and the table entries of
+// the wave's first NBUF blocks of partition z (used when there is no
+// shared-prefix plan, whose partitions start elsewhere).  Every index is
+// clamped into the row and no read sits behind a branch; a table of width
+// 0 is replaced by the length array (B >= 1 entries), whose values then
+// serve only as a rotation, since such a table has no block to read.
+template <int NBUF>
+struct Prologue {
+  const int32_t* trow;
+  int32_t n;
+  int32_t spec[NBUF];
+  uint32_t rot;
+};
+
+// z: the partition the ids are read for; rot_z: the one the rotation adds
+// (the workgroup's, so every wave of a workgroup takes the same head).
+template <int NBUF, int WAVES = kWaves>
+__device__ __forceinline__ Prologue<NBUF> prologue(const DecodeArgs& a, int b, int z, int wv,
+                                                   int rot_z) {
+  Prologue<NBUF> p;
+  p.trow = a.max_blocks > 0 ? a.tables + static_cast<size_t>(b) * a.max_blocks : a.lens;
+  const int last_idx = max(a.max_blocks, 1) - 1;
+  const uint32_t e0 = static_cast<uint32_t>(p.trow[0]);
+  p.n = a.lens[b];
+#pragma unroll
+  for (int sl = 0; sl < NBUF; ++sl)
+    p.spec[sl] = p.trow[min(z * a.part_blocks + wv + sl * WAVES, last_idx)];
+  // Rotation: a hash of the first block id (sequences sharing a prefix
+  // share it; unrelated ones get spread-out values, also when a free list
+  // hands out blocks in order) plus the partition.
+  p.rot = ((e0 * 2654435761u) >> 16) + static_cast<uint32_t>(rot_z);
+  return p;
+}
+
+// Workspace row of the partial result of (sequence b, query head h,
+// partition part): rows are [B][Hkv][P][G], so the G query heads of one KV
+// head and partition are adjacent and a wave writes its partial (G rows of
+// D floats, and G values of m and l) as one contiguous piece.  Scattered
+// rows (query heads P rows apart) cost the long GQA batch ~10% of its read
+// bandwidth.
+__device__ __forceinline__ size_t ws_row(const DecodeArgs& a, int b, int h, int part) {
+  const int g = h / a.qgroup, c = h - g * a.qgroup;
+  return ((static_cast<size_t>(b) * a.hkv + g) * a.num_parts + part) * a.qgroup + c;
 }
 
 __device__ __forceinline__ int num_parts_of(int n, int part_blocks) {
@@ -267,11 +304,15 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   // does not have (the cheap exits) collect at the end of the grid.
   // With a shared-prefix plan, a member's first partitions belong to the
   // shared kernel and z counts from the first private one.
-  const WgCoord wc = wg_coord(a.hkv, seq_rot(a.tables, a.max_blocks));
-  const int g = wc.g, b = wc.y;
+  const WgCoord wc = wg_coord(a.hkv);
+  const int b = wc.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
-  const int n = a.lens[b];
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  const Prologue<NBUF> pro = prologue<NBUF>(a, b, wc.z, wv, wc.z);
+  const int g = rotate_head(wc.g, a.hkv, pro.rot);
+  const int32_t* trow = pro.trow;
+  const int n = pro.n;
   const bool valid = len_valid(n, a);
   const int nblk = valid ? (n + kBlock - 1) / kBlock : 0;
   const int nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
@@ -314,22 +355,20 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 
   const int first = part * a.part_blocks;
   const int last = min(nblk, first + a.part_blocks);   // exclusive
-  const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
   // Block ids come straight from the table with scalar loads (uniform
   // addresses, served by the scalar cache; tables are tiny and stay in L2),
   // so a wave starts streaming without any LDS staging or barrier.  An id
   // outside the pool is replaced by block 0 (never read out of range) and
   // flags the sequence; its output becomes NaN after the merge.
-  const int wv = __builtin_amdgcn_readfirstlane(w);
   // A grid sized below this sequence's private partitions (a host bound
   // that was too small) leaves some uncomputed: flag it like a bad id.
   bool bad_ids = nparts - start > static_cast<int>(gridDim.z);
-  auto block_id = [&](int j) -> int {
-    const int32_t e = trow[j];
+  auto check_id = [&](int32_t e) -> int {
     const bool ok = e >= 0 && e < a.num_blocks;
     bad_ids |= !ok;
     return ok ? e : 0;
   };
+  auto block_id = [&](int j) -> int { return check_id(trow[j]); };
 
   auto load_block = [&](int blk, uint4 (&kw)[LPB], uint4 (&vw)[LPB]) {
     const size_t boff = static_cast<size_t>(blk) * block_bytes;
@@ -361,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 #pragma unroll
   for (int sl = 0; sl < NBUF; ++sl) {
     const int jj = first + wv + sl * kWaves;
-    if (jj < last) load_block(block_id(jj), kr[sl], vr[sl]);
+    if (jj < last) load_block(check_id(a.seq_group == nullptr ? pro.spec[sl] : trow[jj]), kr[sl], vr[sl]);
   }
   for (int j = first + wv; j < last; j += NBUF * kWaves) {
 #pragma unroll
@@ -419,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     if (nparts == 1) {
       a.out[bh * D + d] = res;
     } else {
-      const size_t bhp = bh * a.num_parts + part;
+      const size_t bhp = ws_row(a, b, h0 + hh, part);
       a.ws_o[bhp * D + d] = res;
       if (d == 0) {
         a.ws_m[bhp] = bad ? 0.f : M;
@@ -445,17 +484,23 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 //       (2^-9 for bf16) does not reach the output (2^-18 after the split).
 //       C: lane (qa, t), reg r holds O[head t][dim 16n + 4qa + r], so the
 //       rescale by alpha is lane-local.
-// SHARED: one workgroup per (KV head, plan group, shared partition).  The
-//       16 query columns are (member slot t / qgroup, query head t % qgroup)
-//       of the group's members, the blocks come from the table row of the
-//       group's first slot, and each column's (m, l, o) goes to its
-//       member's workspace row.  Every member checks that its own table
+// Work split: wave-owned partitions, merged per workgroup.  A workgroup of
+//       4 waves takes 4 consecutive partitions (grid z = partitions / 4);
+//       wave w streams every block of partition 4z + w, with no barrier
+//       until its partition is done.  The four results are then merged
+//       through LDS (each wave's staging space is free by then) and written
+//       once, at the group's first partition; the other three partitions
+//       get only m = -big, l = 0, which the reduce skips.  Writing every
+//       partition's G output rows instead cost the long GQA batch ~12% of
+//       its read bandwidth for 0.8% more bytes; with four waves splitting
+//       each partition the cost is per workgroup as well, and this form has
+//       a quarter as many.
+// SHARED: the workgroups run over (KV head, plan group, shared partitions).
+//       The 16 query columns are (member slot t / qgroup, query head
+//       t % qgroup) of the group's members, the blocks come from the table
+//       row of the group's first slot, and each column's (m, l, o) goes to
+//       its member's workspace row.  Every member checks that its own table
 //       holds the same ids over the partition (NaN output otherwise).
-// The per-wave output rows overlay the K/V staging buffers after a barrier
-// (PKV_MFMA_O_UNION), which keeps LDS at 36 KB for 16 columns.
-#ifndef PKV_MFMA_O_UNION
-#define PKV_MFMA_O_UNION 1
-#endif
 template <int DT, int D, int G, int NBUF, bool SHARED>
 __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   static_assert(DT != PA_DTYPE_F32 && (D == 64 || D == 128), "shape");
@@ -469,40 +514,49 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   constexpr int VLOADS = kBlock / RPI;    // V loads per block
   constexpr int VROW = D * ELEM + 32;     // padded LDS row (bytes)
 
-  constexpr int KVBUF = kWaves * kBlock * VROW;
-  constexpr int KBUFS = PKV_MFMA_K_LDS ? 2 : 1;
-  constexpr bool O_UNION = PKV_MFMA_O_UNION && kWaves * G * D * 4 <= KBUFS * KVBUF;
-  __shared__ int32_t s_bad[kWaves];
-  __shared__ __attribute__((aligned(16))) char s_kv[KBUFS * KVBUF + (O_UNION ? 0 : kWaves * G * D * 4)];
-  __shared__ float s_m[kWaves][G], s_l[kWaves][G];
-  __shared__ int32_t s_col[SHARED ? G : 1];          // member of each column, -1 if none
-  __shared__ int32_t s_mis[SHARED ? kWaves : 1][SHARED ? 16 : 1];
-  char (*s_v)[kBlock * VROW] = reinterpret_cast<char (*)[kBlock * VROW]>(s_kv);
-  char (*s_k)[kBlock * VROW] =
-      reinterpret_cast<char (*)[kBlock * VROW]>(s_kv + (PKV_MFMA_K_LDS ? KVBUF : 0));
-  float (*s_o)[G][D] = reinterpret_cast<float (*)[G][D]>(s_kv + (O_UNION ? 0 : KBUFS * KVBUF));
+  // Per wave: V rows, then K rows, while streaming; the wave's unnormalized
+  // result (16 columns x D, padded rows) plus m, l and a bad flag per
+  // column once its partition is done.
+  constexpr int WBYTES = 2 * kBlock * VROW;
+  constexpr int OROW = D + 4;             // floats per staged output row (bank stagger)
+  static_assert(16 * OROW * 4 + 3 * 16 * 4 <= WBYTES, "merge staging fits the K/V staging");
+  __shared__ __attribute__((aligned(16))) char s_wave[kWaves][WBYTES];
+  __shared__ int32_t s_colseq[16];
 
-  const WgCoord wc = wg_coord(a.hkv, SHARED ? blockIdx.y + blockIdx.z
-                                            : seq_rot(a.tables, a.max_blocks));
-  const int g = wc.g;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const WgCoord wc = wg_coord(a.hkv);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int t = lane & 15, qa = lane >> 4;
+  const int zp = wc.z * kWaves + w;       // this wave's partition, counted in the grid
+  // Private grid: the prologue's reads (length, rotation, first ids).  The
+  // shared grid reads each block once, so it rotates by (group, z).  The
+  // rotation is the workgroup's: its four waves take the same head, which
+  // the merge below relies on.
+  Prologue<NBUF> pro{};
+  if constexpr (!SHARED) pro = prologue<NBUF, 1>(a, wc.y, zp, 0, wc.z);
+  const int g = rotate_head(wc.g, a.hkv, SHARED ? wc.y + wc.z : pro.rot);
   const int h0 = g * (SHARED ? a.qgroup : G);
   // b: sequence (private) or plan group (shared).  n: tokens the blocks
   // [first, last) are cut from; trow: the table row they are read from.
   int b = wc.y, part, n, nblk, nparts, first, last;
   bool short_grid = false;
   const int32_t* trow;
-  // SHARED: column t's member (-1 if none) and its query head; the member
-  // slot this lane checks (slot t), and whether the group's source row is
-  // usable.
+  // SHARED: column t's member (-1 if none); the member slot this lane
+  // checks (slot t); whether the group's source row is usable.
   int col_seq = -1, chk_seq = -1;
   bool src_ok = true;
+  // Waves whose partition does not exist stream nothing but still take
+  // part in the merge (the barrier needs every wave).
+  bool active;
+  int p0, pend;                           // the group's partitions: [p0, pend)
   if constexpr (SHARED) {
     const int32_t* row = a.groups + static_cast<size_t>(b) * PA_SHARED_ROW;
     const int P = row[0];
-    part = wc.z;
-    if (P < 1 || P > a.max_shared_parts || part >= P) return;
+    part = zp;
+    p0 = wc.z * kWaves;
+    if (P < 1 || P > a.max_shared_parts || p0 >= P) return;   // uniform over the workgroup
+    pend = min(P, p0 + kWaves);
+    active = part < P;
     const int slots = PA_SHARED_MAX_MEMBERS / a.qgroup;
     // Membership as the private kernels decide it.
     auto member = [&](int sl) -> int {
@@ -515,36 +569,38 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     };
     col_seq = member(t / a.qgroup);
     chk_seq = member(t);
-    // Nothing to do unless some column has a member (wave-uniform: every
-    // wave holds the same 16 columns).
-    if (!__any(col_seq >= 0)) return;
+    if (!__any(col_seq >= 0)) return;     // no column has a member (uniform)
     const int lead = row[1];
     src_ok = lead >= 0 && lead < a.batch;
     trow = a.tables + static_cast<size_t>(src_ok ? lead : 0) * a.max_blocks;
     first = part * a.part_blocks;
-    last = src_ok ? first + a.part_blocks : first;   // within max_blocks: a member exists
+    // within max_blocks: a member exists
+    last = src_ok && active ? first + a.part_blocks : first;
     n = last * kBlock;                               // shared blocks are full
     nblk = last;
     nparts = 0;
   } else {
-    const int nn = a.lens[b];
+    const int nn = pro.n;
     const bool valid = len_valid(nn, a);
     n = nn;
     nblk = valid ? (n + kBlock - 1) / kBlock : 0;
     nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
     const int start = shared_start(a, b, nblk);
-    part = wc.z + start;
-    if (part >= nparts) return;
-    short_grid = nparts - start > static_cast<int>(gridDim.z);
-    if (!valid || n == 0) {
+    part = zp + start;
+    p0 = wc.z * kWaves + start;
+    if (p0 >= nparts) return;             // uniform over the workgroup
+    pend = min(nparts, p0 + kWaves);
+    active = part < nparts;
+    short_grid = nparts - start > static_cast<int>(gridDim.z) * kWaves;
+    if (!valid || n == 0) {               // uniform: nparts == 1, p0 == 0
       const float fill = valid ? 0.f : __builtin_nanf("");
-      for (int i = tid; i < G * D; i += kThreads)
+      for (int i = threadIdx.x; i < G * D; i += kThreads)
         a.out[(static_cast<size_t>(b) * a.hq + h0 + i / D) * D + i % D] = fill;
       return;
     }
-    trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
+    trow = pro.trow;
     first = part * a.part_blocks;
-    last = min(nblk, first + a.part_blocks);
+    last = active ? min(nblk, first + a.part_blocks) : first;
   }
 
   // Q^T as the QK B operand: column t, dims 32j + 8qa .. +8 (zero for a
@@ -570,27 +626,26 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   const uint32_t k_off = t * row_bytes + static_cast<uint32_t>(g * D + 8 * qa) * ELEM;
   const int vr = lane / LPR, vc = lane % LPR;
   const uint32_t v_off = vr * row_bytes + static_cast<uint32_t>(g * D + 8 * vc) * ELEM;
-  char* lds_v = s_v[w];
+  char* lds_v = s_wave[w];
+  char* lds_k = s_wave[w] + kBlock * VROW;
   typedef typename M::lds_x4 lds_x4;
   // Transpose-read address: lane 16qa + 4e + q points at the 4 dims
   // 16n + 4q .. +3 of token 4qa + e; the instruction then hands lane
   // 16qa + j the four tokens 4qa .. 4qa+3 of dim 16n + j.
-  lds_x4* tr_base = (lds_x4*)((__attribute__((address_space(3))) char*)(s_v[w]) +
+  lds_x4* tr_base = (lds_x4*)((__attribute__((address_space(3))) char*)(s_wave[w]) +
                               (4 * qa + (t >> 2)) * VROW + 8 * (t & 3));
 
   // Block ids come straight from the table with scalar loads (uniform
-  // addresses, served by the scalar cache; tables are tiny and stay in L2),
-  // so a wave starts streaming without any LDS staging or barrier.  An id
-  // outside the pool is replaced by block 0 (never read out of range) and
-  // flags the sequence; its output becomes NaN after the merge.
-  const int wv = __builtin_amdgcn_readfirstlane(w);
+  // addresses, served by the scalar cache; tables are tiny and stay in L2).
+  // An id outside the pool is replaced by block 0 (never read out of range)
+  // and flags the partition; its output becomes NaN.
   bool bad_ids = short_grid;
-  auto block_id = [&](int j) -> int {
-    const int32_t e = trow[j];
+  auto check_id = [&](int32_t e) -> int {
     const bool ok = e >= 0 && e < a.num_blocks;
     bad_ids |= !ok;
     return ok ? e : 0;
   };
+  auto block_id = [&](int j) -> int { return check_id(trow[j]); };
 
   auto load_block = [&](int blk, uint4 (&kw)[KSTEPS], uint4 (&vw)[VLOADS]) {
     const size_t boff = static_cast<size_t>(blk) * block_bytes;
@@ -625,10 +680,10 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       static_assert(KSTEPS == VLOADS, "K row loads reuse the V row mapping");
 #pragma unroll
       for (int i = 0; i < VLOADS; ++i)
-        *reinterpret_cast<uint4*>(s_k[w] + (i * RPI + vr) * VROW + 16 * vc) = kw[i];
+        *reinterpret_cast<uint4*>(lds_k + (i * RPI + vr) * VROW + 16 * vc) = kw[i];
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(s_k[w] + t * VROW + (32 * j + 8 * qa) * ELEM);
+        const uint4 kk = *reinterpret_cast<const uint4*>(lds_k + t * VROW + (32 * j + 8 * qa) * ELEM);
         sacc = M::qk(kk, qb[j], sacc);
       }
     } else {
@@ -666,104 +721,100 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     }
   };
 
+  // The partition's blocks in order, NBUF of them in flight.
   uint4 kr[NBUF][KSTEPS], vrg[NBUF][VLOADS];
 #pragma unroll
   for (int sl = 0; sl < NBUF; ++sl) {
-    const int jj = first + wv + sl * kWaves;
-    if (jj < last) load_block(block_id(jj), kr[sl], vrg[sl]);
+    const int jj = first + sl;
+    if (jj < last)
+      load_block(check_id(!SHARED && a.seq_group == nullptr ? pro.spec[sl] : trow[jj]), kr[sl],
+                 vrg[sl]);
   }
-  for (int j = first + wv; j < last; j += NBUF * kWaves) {
+  for (int j = first; j < last; j += NBUF) {
 #pragma unroll
     for (int sl = 0; sl < NBUF; ++sl) {
-      const int jj = j + sl * kWaves;
+      const int jj = j + sl;
       if (jj < last) {
         consume(kr[sl], vrg[sl], jj);
-        const int jn = jj + NBUF * kWaves;
+        const int jn = jj + NBUF;
         if (jn < last) load_block(block_id(jn), kr[sl], vrg[sl]);
       }
     }
   }
 
-  // SHARED: member slot t's own table must hold the source row's ids over
-  // [first, last); lane (w, qa) of column t compares blocks first + 4w + qa,
-  // +16, ...  (after the main loop, so the first K/V loads are not held up).
+  // Result of column t: m is uniform over the four qa lanes, and their
+  // partial sums add up.
+  lsum = group_sum<16, 64>(lsum);
+  bool bad = bad_ids || !src_ok;
   if constexpr (SHARED) {
+    // Member slot t's own table must hold the source row's ids over
+    // [first, last): lane qa of slot t compares blocks first + qa, +4, ...
     bool mismatch = false;
     if (chk_seq >= 0 && src_ok) {
       const int32_t* mrow = a.tables + static_cast<size_t>(chk_seq) * a.max_blocks;
-      for (int j = first + 4 * w + qa; j < last; j += 16) mismatch |= mrow[j] != trow[j];
+      for (int j = first + qa; j < last; j += 4) mismatch |= mrow[j] != trow[j];
     }
-    mismatch = group_max<16, 64>(mismatch ? 1.f : 0.f) != 0.f;   // over the qa lanes
-    if (qa == 0) s_mis[w][t] = mismatch;
-    if (w == 0 && qa == 0) s_col[t] = col_seq;
+    const float mis = group_max<16, 64>(mismatch ? 1.f : 0.f);   // slot t's flag, every qa lane
+    bad |= __shfl(mis, t / a.qgroup) != 0.f;                      // the flag of column t's slot
   }
-
-  // Wave result per column t: m is already uniform over the four qa lanes;
-  // the partial sums of the four token quarters add up.
-  lsum = group_sum<16, 64>(lsum);
-  if constexpr (O_UNION) __syncthreads();   // every wave is done with the K/V staging
-  if (t < G) {
+  // Stage this wave's result in its own staging space (its streaming is
+  // over; the other waves use only theirs), then merge the four.
+  float* st = reinterpret_cast<float*>(s_wave[w]);
+  float* st_m = st + 16 * OROW;
+  float* st_l = st_m + 16;
+  int32_t* st_bad = reinterpret_cast<int32_t*>(st_l + 16);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s_o[w][t][16 * nt + 4 * qa + r] = acc[nt][r];
-    if (qa == 0) {
-      s_m[w][t] = m;
-      s_l[w][t] = lsum;
-    }
+  for (int nt = 0; nt < NT; ++nt)
+    *reinterpret_cast<float4*>(st + t * OROW + 16 * nt + 4 * qa) =
+        make_float4(acc[nt][0], acc[nt][1], acc[nt][2], acc[nt][3]);
+  if (qa == 0) {
+    st_m[t] = active ? m : kMinusBig;
+    st_l[t] = active ? lsum : 0.f;
+    st_bad[t] = active && bad;
+    if (w == 0) s_colseq[t] = SHARED ? col_seq : (t < G ? b : -1);
   }
-  if (lane == 0) s_bad[w] = bad_ids;
   __syncthreads();
 
-  const bool bad = (s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3]) != 0;
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int hh = i / D, d = i % D;
-    if constexpr (SHARED) {
-      // Column hh -> (member slot hh / qgroup, query head h0 + hh % qgroup).
-      const int mseq = s_col[hh];
-      if (mseq < 0) continue;
-      const int sl = hh / a.qgroup;
-      const bool badc = bad || !src_ok ||
-                        (s_mis[0][sl] | s_mis[1][sl] | s_mis[2][sl] | s_mis[3][sl]) != 0;
-      float Mx = s_m[0][hh];
+  // Merged result of column c: M = max m_w, L = sum l_w 2^(m_w - M),
+  // O = sum o_w 2^(m_w - M) (o_w unnormalized), written as O / L at the
+  // group's first partition p0.
+  constexpr int C = SHARED ? 16 : G;     // columns that can carry a row
+  for (int i = threadIdx.x; i < C * D; i += kThreads) {
+    const int c = i / D, d = i % D;
+    const int oseq = s_colseq[c];
+    if (oseq < 0) continue;
+    const int oh = SHARED ? h0 + c % a.qgroup : h0 + c;
+    float Mx = kMinusBig;
+    bool badc = false;
 #pragma unroll
-      for (int ww = 1; ww < kWaves; ++ww) Mx = fmaxf(Mx, s_m[ww][hh]);
-      float L = 0.f, O = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float f = fast_exp2(s_m[ww][hh] - Mx);
-        L = fmaf(s_l[ww][hh], f, L);
-        O = fmaf(s_o[ww][hh][d], f, O);
-      }
-      const size_t bhp = (static_cast<size_t>(mseq) * a.hq + h0 + hh % a.qgroup) * a.num_parts + part;
-      a.ws_o[bhp * D + d] = badc ? __builtin_nanf("") : O / L;
-      if (d == 0) {
-        a.ws_m[bhp] = badc ? 0.f : Mx;
-        a.ws_l[bhp] = badc ? __builtin_nanf("") : L;
-      }
-      continue;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float* sw = reinterpret_cast<const float*>(s_wave[ww]);
+      Mx = fmaxf(Mx, sw[16 * OROW + c]);
+      badc |= reinterpret_cast<const int32_t*>(sw + 16 * OROW + 32)[c] != 0;
     }
-    float Mx = s_m[0][hh];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) Mx = fmaxf(Mx, s_m[ww][hh]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(s_m[ww][hh] - Mx);
-      L = fmaf(s_l[ww][hh], f, L);
-      O = fmaf(s_o[ww][hh][d], f, O);
+      const float* sw = reinterpret_cast<const float*>(s_wave[ww]);
+      const float f = fast_exp2(sw[16 * OROW + c] - Mx);   // 0 for a wave without a partition
+      L = fmaf(sw[16 * OROW + 16 + c], f, L);
+      O = fmaf(sw[c * OROW + d], f, O);
     }
-    const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
-    const float res = bad ? __builtin_nanf("") : O / L;
-    if (nparts == 1) {
-      a.out[bh * D + d] = res;
-    } else {
-      const size_t bhp = bh * a.num_parts + part;
-      a.ws_o[bhp * D + d] = res;
-      if (d == 0) {
-        a.ws_m[bhp] = bad ? 0.f : Mx;
-        a.ws_l[bhp] = bad ? __builtin_nanf("") : L;
-      }
+    const float res = badc ? __builtin_nanf("") : O / L;
+    if (!SHARED && nparts == 1) {
+      a.out[(static_cast<size_t>(oseq) * a.hq + oh) * D + d] = res;
+      continue;
+    }
+    const size_t row = ws_row(a, oseq, oh, p0);
+    a.ws_o[row * D + d] = res;
+    if (d == 0) {
+      a.ws_m[row] = badc ? 0.f : Mx;
+      a.ws_l[row] = badc ? __builtin_nanf("") : L;
+    } else if (d < pend - p0) {
+      // the group's other partitions: empty (the reduce reads no row there)
+      const size_t er = ws_row(a, oseq, oh, p0 + d);
+      a.ws_m[er] = kMinusBig;
+      a.ws_l[er] = 0.f;
     }
   }
 }
@@ -783,26 +834,32 @@ __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
   const int nparts = num_parts_of(n, a.part_blocks);
   if (nparts <= 1) return;                 // phase 1 wrote the output
   const size_t bh = static_cast<size_t>(b) * a.hq + h;
-  const float* pm = a.ws_m + bh * a.num_parts;
-  const float* pl = a.ws_l + bh * a.num_parts;
+  // Partition p's row is row0 + p * G (rows are [B][Hkv][P][G]).
+  const size_t row0 = ws_row(a, b, h, 0);
+  const int G = a.qgroup;
+  const float* pm = a.ws_m + row0;
+  const float* pl = a.ws_l + row0;
   float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, pm[p]);
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, pm[static_cast<size_t>(p) * G]);
   M = group_max<1, 64>(M);
   float L = 0.f;
-  for (int p = lane; p < nparts; p += 64) L += pl[p] * fast_exp2(pm[p] - M);
+  for (int p = lane; p < nparts; p += 64)
+    L += pl[static_cast<size_t>(p) * G] * fast_exp2(pm[static_cast<size_t>(p) * G] - M);
   L = group_sum<1, 64>(L);
   const float inv = 1.f / L;
   float acc[PER] = {};
-  const float* po = a.ws_o + bh * a.num_parts * D + PER * lane;
+  const float* po = a.ws_o + row0 * D + PER * lane;
 #pragma unroll 4
   for (int p = __builtin_amdgcn_readfirstlane(w); p < nparts; p += kWaves) {
-    const float wgt = pl[p] * fast_exp2(pm[p] - M) * inv;
+    const size_t pr = static_cast<size_t>(p) * G;
+    const float wgt = pl[pr] * fast_exp2(pm[pr] - M) * inv;
+    if (wgt == 0.f) continue;            // an empty partition (merged into another); NaN passes
     if constexpr (PER == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(po + static_cast<size_t>(p) * D);
+      const float2 v = *reinterpret_cast<const float2*>(po + pr * D);
       acc[0] = fmaf(wgt, v.x, acc[0]);
       acc[1] = fmaf(wgt, v.y, acc[1]);
     } else {
-      acc[0] = fmaf(wgt, po[static_cast<size_t>(p) * D], acc[0]);
+      acc[0] = fmaf(wgt, po[pr * D], acc[0]);
     }
   }
 #pragma unroll
@@ -819,18 +876,20 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
   if constexpr (DT != PA_DTYPE_F32) {
     if (a.n_groups > 0)
       decode_phase1_mfma<DT, D, 16, PKV_NBUF_MFMA, true>
-          <<<dim3(a.hkv, a.n_groups, a.max_shared_parts), kThreads, 0, st>>>(a);
+          <<<dim3(a.hkv, a.n_groups, (a.max_shared_parts + kWaves - 1) / kWaves), kThreads, 0, st>>>(a);
   }
   dim3 grid(a.hkv, B, a.grid_parts);
+  // The matrix-core kernel gives each wave a whole partition.
+  dim3 grid_w(a.hkv, B, (a.grid_parts + kWaves - 1) / kWaves);
   switch (group) {
     case 1: decode_phase1<DT, D, 1, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
     case 2: decode_phase1<DT, D, 2, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
     case 4:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, PKV_NBUF_MFMA, false><<<grid, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, PKV_NBUF_MFMA, false><<<grid_w, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 4, PKV_NBUF_G4><<<grid, kThreads, 0, st>>>(a);
       break;
     case 8:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, PKV_NBUF_MFMA, false><<<grid, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, PKV_NBUF_MFMA, false><<<grid_w, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a);
       break;
     default: return hipErrorInvalidValue;
