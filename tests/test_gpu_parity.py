@@ -119,6 +119,22 @@ def test_decode_partition_sizes(partition):
     assert np.abs(got - want).max() <= TOL["f16"]
 
 
+@pytest.mark.parametrize("partition", [16, 32, 48, 64, 512])
+@pytest.mark.parametrize("dtype,group", [("bf16", 4), ("f16", 8)])
+def test_decode_mfma_partition_groups(partition, dtype, group):
+    """The matrix-core path merges each workgroup's four partitions: lengths
+    whose partition counts leave 1, 2 or 3 partitions in the last group (and
+    single-partition rows) against the oracle."""
+    bs = 16
+    pb = partition // bs
+    lens = [1, 17, pb * bs, pb * bs + 1, 2 * pb * bs + 5, 3 * pb * bs, 5 * pb * bs + 7,
+            6 * pb * bs + 16, 9 * pb * bs + 3]
+    say("decode_mfma_groups", partition, dtype, group)
+    got, want = _run_decode(lens, 2 * group, 2, 128, dtype, partition, seed=11 + partition)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]
+
+
 def test_decode_tiny_workload():
     """Lengths [7,16,31,48,63], 4 heads x 64, fp32, scale 1/8, 64-block pool;
     tables built by the library's block manager with the prefix cache on
