@@ -11,13 +11,14 @@
 // stored, and long sequences are split into partitions whose partial
 // results a second kernel combines.
 //
-// Phase 1 -- one workgroup of 4 waves per (KV head, sequence, partition):
+// Phase 1, vector ALU (query groups of 1 and 2, and fp32 K/V) -- one
+// workgroup of 4 waves per (KV head, sequence, partition):
 //   * wave w takes the partition's blocks w, w+4, w+8, ..., reading their ids
 //     from the block table with scalar loads (range-checked);
 //   * a token row of one KV head (head_dim elements) is read by
 //     LPR = head_dim*elem/16 lanes with one 16-byte load each, so one load
 //     instruction covers 64/LPR rows and a 16-token block takes 16*LPR/64
-//     loads for K and as many for V; the next block's loads are issued
+//     loads for K and as many for V; the next blocks' loads are issued
 //     before the current block is consumed;
 //   * QK partial dots are summed over the LPR lanes of a row with DPP;
 //     every query head of the GQA group reuses the same K/V registers;
@@ -26,7 +27,13 @@
 //   * the four waves' (m, l, o) are merged through LDS; a sequence with one
 //     partition writes out[] directly, otherwise (m, l, o/l) go to the
 //     workspace.
-// Phase 2 -- one wave per (query head, sequence) merges the partitions.
+// Phase 1, matrix cores (query groups of 4 and 8, 16-bit K/V): QK^T and PV
+//   as MFMAs; each wave streams a whole partition and a workgroup merges
+//   its four partitions before writing (decode_phase1_mfma).
+// Shared-prefix plans add a matrix-core pass over each group's shared
+//   partitions, read once for all members, before the private pass.
+// Phase 2 -- one workgroup of 4 waves per (query head, sequence) merges the
+//   partitions.
 //
 // Memory traffic is dominated by K and V: 2*len*Hkv*head_dim*elem bytes per
 // sequence and layer; every byte is read once.  Q, tables and partials are
@@ -184,10 +191,8 @@ __device__ __forceinline__ Prologue<NBUF> prologue(const DecodeArgs& a, int b, i
 
 // Workspace row of the partial result of (sequence b, query head h,
 // partition part): rows are [B][Hkv][P][G], so the G query heads of one KV
-// head and partition are adjacent and a wave writes its partial (G rows of
-// D floats, and G values of m and l) as one contiguous piece.  Scattered
-// rows (query heads P rows apart) cost the long GQA batch ~10% of its read
-// bandwidth.
+// head and partition are adjacent and a workgroup writes its partial (G
+// rows of D floats, and G values of m and l) as one contiguous piece.
 __device__ __forceinline__ size_t ws_row(const DecodeArgs& a, int b, int h, int part) {
   const int g = h / a.qgroup, c = h - g * a.qgroup;
   return ((static_cast<size_t>(b) * a.hkv + g) * a.num_parts + part) * a.qgroup + c;
