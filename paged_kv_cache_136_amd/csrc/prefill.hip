@@ -50,6 +50,7 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPBlock = 16;                 // tokens per KV block
 constexpr float kPMinusBig = -1e30f;
 constexpr float kPRescaleLog2 = 8.f;
+constexpr int kPRsrcWord3 = 0x00020000;     // buffer descriptor word 3: 32-bit raw access
 #ifndef PKV_PF_QW
 #define PKV_PF_QW 2        // 16-row query tiles per wave
 #endif
@@ -98,7 +99,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
   __shared__ __attribute__((aligned(16))) char s_v[2][SROWS * VROW];
 
   const int h = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar
   const int t = lane & 15, qa = lane >> 4;
   const int g = h / (a.hq / a.hkv);
   const int q0 = a.qstart[b], q1 = a.qstart[b + 1], total = a.num_tokens;
@@ -143,21 +145,38 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
   for (int u = 0; u < kQW; ++u)
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[u][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m[kQW], lsum[kQW];
+  // Row sums of p accumulate on the matrix cores (A = ones): the sum lands
+  // in every register of the query row's lanes, already reduced over keys,
+  // and it uses the same rounded p as the P V product.
+  float m[kQW];
+  f32x4_t lsum[kQW];
 #pragma unroll
-  for (int u = 0; u < kQW; ++u) { m[u] = kPMinusBig; lsum[u] = 0.f; }
+  for (int u = 0; u < kQW; ++u) { m[u] = kPMinusBig; lsum[u] = f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
-  const size_t row_bytes = static_cast<size_t>(a.hkv) * D * ELEM;
-  const size_t block_bytes = row_bytes * kPBlock;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.hkv) * D * ELEM;
+  const uint32_t block_bytes = row_bytes * kPBlock;
   const int32_t* trow = a.tables + static_cast<size_t>(b) * a.max_blocks;
   bool bad = false;
   // Stage s holds blocks kKB*s .. +kKB-1; thread tid moves chunks tid,
-  // tid + 256, ... (row = chunk / CPR within the stage).  Branch-free, so
-  // the in-flight chunks stay in registers: the address of a key past the
-  // tile's last query position is clamped to the cache start and its value
-  // replaced by zeros (neither NaN poison nor a block outside the tile's
-  // range can reach the MFMAs).
+  // tid + 256, ... (row = chunk / CPR within the stage).  K/V are read with
+  // buffer loads: a scalar descriptor per block (base = block start, range
+  // = one block) and a lane offset that does not change from stage to
+  // stage.  A key past the tile's last query position gets the offset just
+  // past the block, which the hardware's range check turns into zeros, so
+  // neither NaN poison nor a block outside the tile's range reaches the
+  // MFMAs and nothing waits on the loads before the stage's compute.  The
+  // chunks of one load index all lie in one block (a row of chunks spans
+  // 2*D bytes of 16-byte chunks), so the block is wave-uniform.
   static_assert(CHUNKS % kPThreads == 0, "whole chunks per thread");
+  uint32_t coff[LPT];
+  int crow[LPT], cblk[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + i * kPThreads;
+    crow[i] = c / CPR;
+    cblk[i] = __builtin_amdgcn_readfirstlane(crow[i] / kPBlock);
+    coff[i] = (crow[i] % kPBlock) * row_bytes + static_cast<uint32_t>(g * D * ELEM) + (c % CPR) * 16;
+  }
   uint4 kr[LPT], vr[LPT];
   auto load = [&](int stage) {
     int32_t ids[kKB];
@@ -171,22 +190,17 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
     }
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int c = tid + i * kPThreads;
-      const int row = c / CPR, col = c % CPR, bb = row / kPBlock;
-      // Keys past the tile's last query position are never attended (and
-      // past the last block they have no valid id): zeros.
-      const bool live = stage * SROWS + row <= last_pos_wg;
       int32_t id = ids[0];          // select, not an indexed (scratch) array
 #pragma unroll
-      for (int q = 1; q < kKB; ++q) id = bb == q ? ids[q] : id;
-      const size_t off = live ? static_cast<size_t>(id) * block_bytes + (row % kPBlock) * row_bytes +
-                                    static_cast<size_t>(g) * D * ELEM + col * 16
-                              : 0;
-      const uint4 kx = *reinterpret_cast<const uint4*>(a.k + off);
-      const uint4 vx = *reinterpret_cast<const uint4*>(a.v + off);
-      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-      kr[i] = select4(live, kx, zero);
-      vr[i] = select4(live, vx, zero);
+      for (int q = 1; q < kKB; ++q) id = cblk[i] == q ? ids[q] : id;
+      const size_t boff = static_cast<size_t>(id) * block_bytes;
+      const auto kd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.k + boff), 0,
+                                                        static_cast<int>(block_bytes), kPRsrcWord3);
+      const auto vd = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(a.v + boff), 0,
+                                                        static_cast<int>(block_bytes), kPRsrcWord3);
+      const uint32_t off = stage * SROWS + crow[i] <= last_pos_wg ? coff[i] : block_bytes;
+      kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kd, off, 0, 0));
+      vr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vd, off, 0, 0));
     }
   };
   auto stash = [&](int buf) {
@@ -199,6 +213,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
     }
   };
   typedef typename M::lds_x4 lds_x4;
+  constexpr uint32_t kOne2 = DT == PA_DTYPE_F16 ? 0x3C003C00u : 0x3F803F80u;   // two 1.0s
+  const uint4 kOnes = make_uint4(kOne2, kOne2, kOne2, kOne2);
 
   load(0);
   stash(0);
@@ -229,6 +245,23 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
       // last key needs none.
       const bool no_mask = wrows == 16 * kQW && cached + wrow0 >= key_base + SROWS - 1;
       float sc[kKB][kQW][4];
+#pragma unroll
+      for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+        for (int u = 0; u < kQW; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[bb][u][r] = sacc[bb][u][r];
+      if (!no_mask) {
+#pragma unroll
+        for (int bb = 0; bb < kKB; ++bb)
+#pragma unroll
+          for (int u = 0; u < kQW; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = key_base + bb * kPBlock + 4 * qa + r;
+              sc[bb][u][r] = key <= my_pos[u] ? sc[bb][u][r] : -INFINITY;
+            }
+      }
       float bm[kQW];
       bool grow = false;
 #pragma unroll
@@ -237,11 +270,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
 #pragma unroll
         for (int bb = 0; bb < kKB; ++bb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = key_base + bb * kPBlock + 4 * qa + r;
-            sc[bb][u][r] = (no_mask || key <= my_pos[u]) ? sacc[bb][u][r] : -INFINITY;
-            mx = fmaxf(mx, sc[bb][u][r]);
-          }
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[bb][u][r]);
         bm[u] = group_max<16, 64>(mx) * a.scale_log2;
         grow |= bm[u] > m[u] + kPRescaleLog2;
       }
@@ -264,7 +293,6 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
           float p[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(sc[bb][u][r], a.scale_log2, -m[u]));
-          lsum[u] += (p[0] + p[1]) + (p[2] + p[3]);
           M::split(p, ph[bb][u], pl[bb][u]);
         }
       // O^T += V^T P^T with the K=32 MFMA over two blocks at once (the
@@ -284,6 +312,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
         for (int u = 0; u < kQW; ++u) {
           pb[u] = make_uint4(ph[bp][u].x, ph[bp][u].y, ph[bp + 1][u].x, ph[bp + 1][u].y);
           pbl[u] = make_uint4(pl[bp][u].x, pl[bp][u].y, pl[bp + 1][u].x, pl[bp + 1][u].y);
+          lsum[u] = M::qk(kOnes, pb[u], lsum[u]);
+          if constexpr (SPLIT) lsum[u] = M::qk(kOnes, pbl[u], lsum[u]);
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -310,7 +340,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
 
 #pragma unroll
   for (int u = 0; u < kQW; ++u) {
-    const float l = group_sum<16, 64>(lsum[u]);
+    const float l = lsum[u][0];
     if (16 * u + t < wrows) {
       const float inv = 1.f / l;
       float* orow = a.out + (static_cast<size_t>(q0 + wrow0 + 16 * u + t) * a.hq + h) * D;
@@ -366,6 +396,8 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
   if (static_cast<size_t>(num_kv_heads) * head_dim * 2 * kPBlock * static_cast<size_t>(num_blocks) >
       (static_cast<size_t>(1) << 47))
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: cache too large");
+  if (static_cast<size_t>(num_kv_heads) * head_dim * 2 * kPBlock >= (static_cast<size_t>(1) << 31))
+    return fail(PA_ERR_UNSUPPORTED, "pa_prefill: KV block larger than 2 GiB");
   if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(q) |
        reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15)
     return fail(PA_ERR_INVALID, "pa_prefill: buffers must be 16-byte aligned");
