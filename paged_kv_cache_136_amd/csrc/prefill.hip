@@ -80,6 +80,19 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+// Max over the lanes t, t + 16, t + 32 and t + 48 of a wave (every lane gets
+// it), with the gfx950 lane-swap instructions: swapping a value with itself
+// across rows of 16 (then halves of 32) puts each lane's partner beside it,
+// an exact xor-16 then xor-32 butterfly without a round trip through LDS.
+__device__ __forceinline__ float max_across_rows(float x) {
+  const int xi = __float_as_int(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  const float y = fmaxf(__int_as_float(a[0]), __int_as_float(a[1]));
+  const int yi = __float_as_int(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  return fmaxf(__int_as_float(b[0]), __int_as_float(b[1]));
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_PF_WAVES_PER_EU, PKV_PF_WAVES_PER_EU))) void prefill_mfma(PrefillArgs a) {
   using M = MfmaOps<DT>;
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
         for (int bb = 0; bb < kKB; ++bb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[bb][u][r]);
-        bm[u] = group_max<16, 64>(mx) * a.scale_log2;
+        bm[u] = max_across_rows(mx) * a.scale_log2;
         grow |= bm[u] > m[u] + kPRescaleLog2;
       }
       if (__any(grow)) {

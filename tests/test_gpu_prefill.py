@@ -31,7 +31,7 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def run_case(qlens, lens, hq, hkv, d, dtype, seed, nb=None, poison=True):
+def run_case(qlens, lens, hq, hkv, d, dtype, seed, nb=None, poison=True, q_scale=1.0):
     bs = 16
     need = sum(-(-n // bs) for n in lens)
     nb = nb or need + 5
@@ -40,6 +40,8 @@ def run_case(qlens, lens, hq, hkv, d, dtype, seed, nb=None, poison=True):
     k, v = make_cache(nb, bs, hkv, d, dtype, seed=seed + 10, poison=pm)
     T = int(sum(qlens))
     q = workloads.normal_torch((max(T, 1), hq, d), seed + 20, TORCH_DTYPES[dtype], "cuda")[:T]
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(TORCH_DTYPES[dtype])
     qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
     out = pkv.pa_prefill(q, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(qs).cuda(),
                          torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max(qlens + [1]))
@@ -62,6 +64,20 @@ CASES = [
 def test_prefill_matches_oracle(qlens, lens, hq, hkv, d, dtype):
     say("prefill", dtype, qlens, lens, hq, hkv, d)
     got, want = run_case(qlens, lens, hq, hkv, d, dtype, seed=sum(lens) % 97)
+    assert np.isfinite(got).all()
+    err = np.abs(got - want).max()
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_large_scores(dtype):
+    """Scores with a spread of hundreds in the exponent (q scaled by 64):
+    exp of a score minus anything but the true running max of its row
+    overflows or underflows, so this pins the stage max and its lane
+    exchange, which ordinary scores cannot (softmax does not depend on the
+    subtracted value)."""
+    say("prefill large scores", dtype)
+    got, want = run_case([150, 40], [400, 40], 8, 2, 128, dtype, seed=5, q_scale=64.0)
     assert np.isfinite(got).all()
     err = np.abs(got - want).max()
     assert err <= TOL[dtype], err
