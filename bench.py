@@ -16,7 +16,7 @@ Sequences grow by one token per step, as in real decoding; the KV bytes of
 every step are counted exactly.  The metric is achieved KV GB/s (valid
 tokens' K and V bytes read per second, whole job) with seqs/s beside it.
 
-Prints one JSON line.  --gpus N with N > 1 exits: this build runs on one GPU.
+Prints one JSON line.  --gpus N with N > 1 exits: the library runs on one GPU.
 """
 
 import argparse
@@ -383,7 +383,7 @@ def run_fork_cow(args, torch, pkv, workloads):
         for c in range(1, F):
             bm.fork(int(p), int(p) + c)
     torch.cuda.synchronize()
-    # Round 1: the copy-on-write round, timed.
+    # First append pass after the forks: the one with the copy-on-write copies, timed.
     toks = np.arange(B, dtype=np.int32)
     cow_ev, round_ev = (T(enable_timing=True), T(enable_timing=True)), (T(enable_timing=True), T(enable_timing=True))
     d_slot, d_pairs, npairs = append(seqs, toks)
@@ -880,8 +880,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(decode shards by sequence or KV head with no exchange; see the design notes).",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(decode would shard by sequence or by KV head, with no exchange inside attention).",
               file=sys.stderr)
         sys.exit(2)
 
