@@ -80,7 +80,8 @@ def test_copy_blocks_bitexact():
 
 # ---------------------------------------------------------------- decode
 
-def _run_decode(lens, hq, hkv, d, dtype, partition, seed, poison=True, num_blocks=None):
+def _run_decode(lens, hq, hkv, d, dtype, partition, seed, poison=True, num_blocks=None,
+                q_scale=1.0):
     bs = 16
     need = sum(-(-int(n) // bs) for n in lens)
     num_blocks = num_blocks or need + 5
@@ -88,6 +89,8 @@ def _run_decode(lens, hq, hkv, d, dtype, partition, seed, poison=True, num_block
     mask = poison_mask(tables, lens, num_blocks, bs) if poison else None
     k, v = make_cache(num_blocks, bs, hkv, d, dtype, seed, poison=mask)
     q = workloads.normal_torch((len(lens), hq, d), seed + 7, TORCH_DTYPES[dtype], "cuda")
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(TORCH_DTYPES[dtype])
     max_len = int(max(lens)) if len(lens) else 0
     out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(),
                         torch.tensor(lens, dtype=torch.int32, device="cuda"), max_len,
@@ -163,6 +166,22 @@ def test_decode_tiny_workload():
     torch.cuda.synchronize()
     want = oracle.ref_decode(host_f32(q), host_f32(k), host_f32(v), tables, clens, scale=1 / 8)
     assert np.abs(out.cpu().numpy() - want).max() <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("group", [1, 4])
+@pytest.mark.parametrize("partition", [0, 64])
+def test_decode_large_scores(dtype, group, partition):
+    """q scaled by 64, so scores spread over hundreds in the exponent: the
+    online softmax's running max, its per-block and per-partition maxima
+    and the reduce's maximum over partitions must each be the true one, or
+    the exponentials overflow or underflow (ordinary scores cannot show a
+    wrong max: softmax does not depend on the subtracted value)."""
+    say("decode_large_scores", dtype, group, partition)
+    got, want = _run_decode([1, 40, 300, 1000], 2 * group, 2, 128, dtype, partition, seed=23,
+                            q_scale=64.0)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]
 
 
 def test_decode_edge_cases():

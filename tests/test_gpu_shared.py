@@ -140,6 +140,18 @@ def _members(groups, gi):
     return [int(m) for m in groups[gi, 1:] if m >= 0]
 
 
+def test_shared_large_scores():
+    """q scaled by 64 (exponents spread over hundreds): the shared and the
+    private partitions' maxima meet in the reduce."""
+    tables, lens = fork_family([1000, 700], 4, _extra(8, 9, 40), singles=[333], seed=9)
+    c = Case(tables, lens, 8, 2, 128, "bf16", seed=9)
+    c.q = (c.q.float() * 64.0).to(torch.bfloat16)
+    say("shared large scores")
+    got = c.shared(c.plan(128), 128)
+    assert np.isfinite(got).all()
+    assert np.abs(got - c.want()).max() <= TOL["bf16"]
+
+
 def test_shared_table_mismatch_gives_nan():
     """A member whose own table differs from the group's source row inside
     the shared partitions gets NaN rows; everyone else stays exact."""
