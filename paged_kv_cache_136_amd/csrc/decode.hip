@@ -874,6 +874,62 @@ __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
     a.out[bh * D + tid] = (s_acc[0][tid] + s_acc[1][tid]) + (s_acc[2][tid] + s_acc[3][tid]);
 }
 
+// The same reduce with one wave per (query head, sequence) and four heads
+// per workgroup, for batches of at most kReduceWaveParts partitions and
+// enough pairs to give every CU a workgroup: there a pair's few partial rows
+// leave four waves mostly waiting, and the LDS merge and barrier are pure
+// latency.  Each lane owns D/64 adjacent dims and walks
+// the partitions in order; a partition's weight comes from scalar reads of
+// its (m, l), the same in every lane.
+constexpr int kReduceWaveParts = 16;
+constexpr int kReduceWaveMinPairs = kWaves * 256;   // one workgroup per CU
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_reduce_wave(DecodeArgs a) {
+  constexpr int PER = D / 64;
+  static_assert(PER == 1 || PER == 2, "head_dim 64 or 128");
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int b = blockIdx.y;
+  if (h >= a.hq) return;
+  const int n = a.lens[b];
+  if (!len_valid(n, a)) return;
+  const int nparts = num_parts_of(n, a.part_blocks);
+  if (nparts <= 1) return;                 // phase 1 wrote the output
+  const size_t row0 = ws_row(a, b, h, 0);
+  const int G = a.qgroup;
+  const float* pm = a.ws_m + row0;
+  const float* pl = a.ws_l + row0;
+  float M = -INFINITY;
+  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, pm[static_cast<size_t>(p) * G]);
+  M = group_max<1, 64>(M);
+  float L = 0.f;
+  for (int p = lane; p < nparts; p += 64)
+    L += pl[static_cast<size_t>(p) * G] * fast_exp2(pm[static_cast<size_t>(p) * G] - M);
+  L = group_sum<1, 64>(L);
+  const float inv = 1.f / L;
+  float acc[PER] = {};
+  const float* po = a.ws_o + row0 * D + PER * lane;
+#pragma unroll 4
+  for (int p = 0; p < nparts; ++p) {
+    const size_t pr = static_cast<size_t>(p) * G;
+    const float wgt = pl[pr] * fast_exp2(pm[pr] - M) * inv;
+    if (wgt == 0.f) continue;            // an empty partition (merged into another); NaN passes
+    if constexpr (PER == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(po + pr * D);
+      acc[0] = fmaf(wgt, v.x, acc[0]);
+      acc[1] = fmaf(wgt, v.y, acc[1]);
+    } else {
+      acc[0] = fmaf(wgt, po[pr * D], acc[0]);
+    }
+  }
+  float* orow = a.out + (static_cast<size_t>(b) * a.hq + h) * D + PER * lane;
+  if constexpr (PER == 2)
+    *reinterpret_cast<float2*>(orow) = make_float2(acc[0], acc[1]);
+  else
+    orow[0] = acc[0];
+}
+
 template <int DT, int D>
 hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
   // Shared partitions first (they fill workspace rows the private pass
@@ -899,7 +955,14 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
       break;
     default: return hipErrorInvalidValue;
   }
-  if (a.num_parts > 1) decode_reduce<D><<<dim3(a.hq, B), kThreads, 0, st>>>(a);
+  // One wave per pair where that still gives every CU a workgroup (the
+  // 13B layer's 400 pairs do not: there four waves per pair win).
+  const bool wave_reduce = a.num_parts <= kReduceWaveParts &&
+                           static_cast<int64_t>(B) * a.hq >= kReduceWaveMinPairs;
+  if (a.num_parts > 1 && !wave_reduce)
+    decode_reduce<D><<<dim3(a.hq, B), kThreads, 0, st>>>(a);
+  else if (a.num_parts > 1)
+    decode_reduce_wave<D><<<dim3((a.hq + kWaves - 1) / kWaves, B), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

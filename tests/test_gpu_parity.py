@@ -168,6 +168,21 @@ def test_decode_tiny_workload():
     assert np.abs(out.cpu().numpy() - want).max() <= TOL["f32"]
 
 
+@pytest.mark.parametrize("dtype,d,group", [("f16", 128, 1), ("bf16", 64, 4), ("f32", 128, 2),
+                                           ("bf16", 128, 8)])
+def test_decode_many_pairs(dtype, d, group):
+    """64 sequences x 16 query heads = 1024 (head, sequence) pairs and at
+    most 16 partitions of 64 tokens: the reduce takes one wave per pair,
+    four pairs per workgroup.  Lengths ragged from 1 token (no reduce) to
+    all 16 partitions."""
+    lens = [int(x) for x in np.random.default_rng(5).integers(1, 16 * 64 + 1, size=64)]
+    lens[0], lens[1], lens[2] = 1, 64, 16 * 64
+    say("decode_many_pairs", dtype, d, group)
+    got, want = _run_decode(lens, 16, 16 // group, d, dtype, 64, seed=31 + d + group)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("group", [1, 4])
 @pytest.mark.parametrize("partition", [0, 64])
