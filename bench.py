@@ -7,7 +7,7 @@ log-uniform in [50, 4096], a 16384-block pool scattered by a seeded
 permutation).  One step is one pass of the whole hot path:
 
   host   pa_bm_append_slots (one new token per sequence: slot, table growth)
-         pa_bm_export_batch into pinned buffers, async upload
+         pa_bm_export_batch into a pinned staging buffer, one async upload
   device for each layer: pa_write_kv (the new token's K/V), pa_decode
          (split-KV phase 1 + reduce); pa_copy_blocks when appends report
          copy-on-write pairs (none in this workload)
@@ -185,17 +185,20 @@ class DecodeBench:
         self.out = torch.empty((L, B, self.hq, D), dtype=torch.float32, device=dev)
         ws_bytes = pkv.pa_decode_workspace_bytes(B, self.hq, D, self.max_len_final, self.partition)
         self.ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-        self.d_tab = torch.empty((B, self.max_blocks), dtype=torch.int32, device=dev)
-        self.d_len = torch.empty(B, dtype=torch.int32, device=dev)
-        self.d_slot = torch.empty(B, dtype=torch.int64, device=dev)
-        self.d_pairs = torch.empty((B, 2), dtype=torch.int32, device=dev)
-        # Two pinned host buffer sets: the host fills one while the other's
-        # upload may still be queued.
-        self.pin = [dict(tab=torch.empty((B, self.max_blocks), dtype=torch.int32).pin_memory(),
-                         len=torch.empty(B, dtype=torch.int32).pin_memory(),
-                         slot=torch.empty(B, dtype=torch.int64).pin_memory(),
-                         pairs=torch.empty((B, 2), dtype=torch.int32).pin_memory(),
-                         ev=torch.cuda.Event()) for _ in range(2)]
+        # The step's host outputs (slots, tables, lengths, copy-on-write
+        # pairs) share one staging layout, so one copy uploads them all:
+        # [slots int64 B | tables int32 B x max_blocks | lens int32 B |
+        # pairs int32 B x 2].  Two pinned host buffers: the host fills one
+        # while the other's upload may still be queued.
+        self.stage_bytes = B * 8 + B * self.max_blocks * 4 + B * 4 + B * 2 * 4
+        self.d_stage = torch.empty(self.stage_bytes, dtype=torch.uint8, device=dev)
+        self.d_slot, self.d_tab, self.d_len, self.d_pairs = self._views(self.d_stage)
+        self.pin = []
+        for _ in range(2):
+            buf = torch.empty(self.stage_bytes, dtype=torch.uint8).pin_memory()
+            slot, tab, lens, pairs = self._views(buf)
+            self.pin.append(dict(buf=buf, slot=slot, tab=tab, len=lens, pairs=pairs,
+                                 ev=torch.cuda.Event()))
         for p in self.pin:
             p["ev"].record()
         self.new_tok = np.full(B, 7, dtype=np.int32)
@@ -203,6 +206,15 @@ class DecodeBench:
         self.v_layers = [self.pool[layer, 1] for layer in range(L)]
         self.host_s = []
         torch.cuda.synchronize()
+
+    def _views(self, buf):
+        """(slots, tables, lens, pairs) views of one staging buffer."""
+        torch, B, mb = self.torch, self.B, self.max_blocks
+        o1 = B * 8
+        o2 = o1 + B * mb * 4
+        o3 = o2 + B * 4
+        return (buf[:o1].view(torch.int64), buf[o1:o2].view(torch.int32).view(B, mb),
+                buf[o2:o3].view(torch.int32), buf[o3:].view(torch.int32).view(B, 2))
 
     def step(self, s, ev_pairs=None):
         pkv, p = self.pkv, self.pin[s % 2]
@@ -213,12 +225,10 @@ class DecodeBench:
         self.bm.export_batch(self.seqs, self.max_blocks, 0, tables_out=p["tab"].numpy(),
                              lens_out=p["len"].numpy())
         self.host_s.append(time.perf_counter() - h0)
-        self.d_tab.copy_(p["tab"], non_blocking=True)
-        self.d_len.copy_(p["len"], non_blocking=True)
-        self.d_slot.copy_(p["slot"], non_blocking=True)
         if len(pairs):
             p["pairs"].numpy()[:len(pairs)] = pairs
-            self.d_pairs[:len(pairs)].copy_(p["pairs"][:len(pairs)], non_blocking=True)
+        used = self.stage_bytes - (self.B - len(pairs)) * 2 * 4
+        self.d_stage[:used].copy_(p["buf"][:used], non_blocking=True)
         p["ev"].record()
         if len(pairs):
             pkv.pa_copy_blocks(self.k_layers, self.v_layers, self.d_pairs[:len(pairs)])
