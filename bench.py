@@ -367,27 +367,32 @@ def run_fork_cow(args, torch, pkv, workloads):
 
     plan_s = []
 
-    def decode(max_len, ev=None, shared=True):
+    def prepare(shared=True):
+        """Host part of a decode: tables and lengths exported and uploaded,
+        and the shared-prefix plan made and uploaded.  Runs before a step's
+        timed region, which holds GPU work only."""
         bm.export_batch(seqs, max_blocks, 0, tables_out=tab_h.numpy(), lens_out=len_h.numpy())
         d_tab.copy_(tab_h)
         d_len.copy_(len_h)
-        if shared:
-            h0 = time.perf_counter()
-            sg, groups, mx, mp = pkv.pa_shared_plan(tab_h.numpy(), len_h.numpy(), bs, 512, 1)
-            plan_s.append(time.perf_counter() - h0)
-            d_sg = torch.from_numpy(sg).to(dev)
-            d_groups = torch.from_numpy(groups).to(dev)
+        if not shared:
+            return None
+        h0 = time.perf_counter()
+        sg, groups, mx, mp = pkv.pa_shared_plan(tab_h.numpy(), len_h.numpy(), bs, 512, 1)
+        plan_s.append(time.perf_counter() - h0)
+        return torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev), mx, mp
+
+    def decode(max_len, plan, ev=None):
         if ev is not None:
             ev[0].record()
-        if shared:
-            pkv.pa_decode_shared(q, k, v, d_tab, d_len, max_len, d_sg, d_groups, mx, mp,
+        if plan is not None:
+            pkv.pa_decode_shared(q, k, v, d_tab, d_len, max_len, *plan,
                                  partition_tokens=512, out=out, workspace=ws)
         else:
             pkv.pa_decode(q, k, v, d_tab, d_len, max_len, partition_tokens=512, out=out,
                           workspace=ws)
         if ev is not None:
             ev[1].record()
-        return len(groups) if shared else 0
+        return 0 if plan is None else len(plan[1])
 
     T = torch.cuda.Event
     # Parent token, then the forks.
@@ -401,12 +406,13 @@ def run_fork_cow(args, torch, pkv, workloads):
     toks = np.arange(B, dtype=np.int32)
     cow_ev, round_ev = (T(enable_timing=True), T(enable_timing=True)), (T(enable_timing=True), T(enable_timing=True))
     d_slot, d_pairs, npairs = append(seqs, toks)
+    plan = prepare()
     round_ev[0].record()
     cow_ev[0].record()
     pkv.pa_copy_blocks([k], [v], d_pairs)
     cow_ev[1].record()
     pkv.pa_write_kv(k, v, kn, vn, d_slot)
-    decode(L0 + 2)
+    decode(L0 + 2, plan)
     round_ev[1].record()
     torch.cuda.synchronize()
     cow_ms, round_ms = cow_ev[0].elapsed_time(cow_ev[1]), round_ev[0].elapsed_time(round_ev[1])
@@ -417,8 +423,9 @@ def run_fork_cow(args, torch, pkv, workloads):
         pkv.pa_write_kv(k, v, kn, vn, d_slot)
     for w in range(args.warmup):
         d_slot, _, _ = append(seqs, toks)
+        plan = prepare()
         pkv.pa_write_kv(k, v, kn, vn, d_slot)
-        decode(L0 + 1 + X + w + 1)
+        decode(L0 + 1 + X + w + 1, plan)
     torch.cuda.synchronize()
     evs = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
     dec = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
@@ -428,9 +435,10 @@ def run_fork_cow(args, torch, pkv, workloads):
     for i in range(args.steps):
         n = L0 + 1 + X + args.warmup + i + 1
         d_slot, _, _ = append(seqs, toks)
+        plan = prepare()
         evs[i][0].record()
         pkv.pa_write_kv(k, v, kn, vn, d_slot)
-        n_groups = decode(n, dec[i])
+        n_groups = decode(n, plan, dec[i])
         evs[i][1].record()
         lens.append(n)
         # unique blocks read: the shared prefix once per prompt plus every
@@ -443,8 +451,9 @@ def run_fork_cow(args, torch, pkv, workloads):
     # plain pa_decode over the final batch, same tables, for comparison
     n_last = lens[-1]
     plain = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
+    prepare(shared=False)
     for i in range(args.steps):
-        decode(n_last, plain[i], shared=False)
+        decode(n_last, None, plain[i])
     torch.cuda.synchronize()
     plain_ms = np.array([a.elapsed_time(b) for a, b in plain])
     per_tok = 2 * H * D * 2
