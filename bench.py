@@ -44,7 +44,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixed_7b",
                    choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap", "serve", "beam",
-                            "prefill"],
+                            "prefill", "prefill_gqa"],
                    help="mixed_7b is the headline workload; the others are reported lines")
     p.add_argument("--shared-prefix", choices=["on", "off"], default=None,
                    help="serve: decode with pa_decode_shared (default: the workload's choice)")
@@ -807,10 +807,12 @@ def run_prefill(args, torch, pkv, workloads):
     1024-token system prompt (prefix-cache hits) and each adds a 1024-token
     uncached suffix; one layer of 32 heads x 128, fp16, block 16.  The suffix
     K/V are written (pa_write_kv) and pa_prefill computes their causal
-    attention over 2048-token contexts.  Reported: the kernel's rate in
+    attention over 2048-token contexts.  prefill_gqa is the same with 8
+    KV heads for the 32 query heads.  Reported: the kernel's rate in
     TFLOP/s of algorithmic attention work (4 * head_dim flops per (query,
     key, head) with key <= query), and K/V bytes read per second."""
     B, sys_len, sfx, H, D, bs = 16, 1024, 1024, 32, 128, 16
+    HKV = 8 if args.workload == "prefill_gqa" else H
     n = sys_len + sfx
     NB = B * (n // bs) + 64
     dev = torch.device("cuda:0")
@@ -826,8 +828,8 @@ def run_prefill(args, torch, pkv, workloads):
     seqs = list(range(1, B + 1))
     qlens = [n - c for c in cached]
     tables, lens = bm.export_batch(seqs, n // bs, pad_block=0)
-    k = workloads.normal_torch((NB, bs, H, D), 80, torch.float16, dev)
-    v = workloads.normal_torch((NB, bs, H, D), 81, torch.float16, dev)
+    k = workloads.normal_torch((NB, bs, HKV, D), 80, torch.float16, dev)
+    v = workloads.normal_torch((NB, bs, HKV, D), 81, torch.float16, dev)
     T = sum(qlens)
     q = workloads.normal_torch((T, H, D), 82, torch.float16, dev)
     qs = torch.tensor(np.concatenate([[0], np.cumsum(qlens)]), dtype=torch.int32, device=dev)
@@ -850,7 +852,7 @@ def run_prefill(args, torch, pkv, workloads):
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     pairs = sum(sum(c + i + 1 for i in range(ql)) for c, ql in zip(cached, qlens))
     flops = 4.0 * D * H * pairs
-    kv_bytes = 2.0 * H * D * 2 * sum(lens)         # each sequence's K/V once
+    kv_bytes = 2.0 * HKV * D * 2 * sum(lens)       # each sequence's K/V once
     tflops = flops / (ms.mean() * 1e-3) / 1e12
     cpu = None
     if args.cpu_seconds > 0:
@@ -877,8 +879,8 @@ def run_prefill(args, torch, pkv, workloads):
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "prefill", "sequences": B, "cached_prefix": sys_len, "suffix": sfx,
-                   "context": n, "q_heads": H, "kv_heads": H, "head_dim": D, "block_size": bs,
+        "config": {"workload": args.workload, "sequences": B, "cached_prefix": sys_len, "suffix": sfx,
+                   "context": n, "q_heads": H, "kv_heads": HKV, "head_dim": D, "block_size": bs,
                    "cached_tokens": cached[:1], "timing": "GPU events per pa_prefill launch"},
         "kv_gbs": round(kv_bytes / (ms.mean() * 1e-3) / 1e9, 2),
         "roofline": {"kernel": "pa_prefill", "bound": "mfma", "achieved": round(tflops, 2),
@@ -922,7 +924,7 @@ def main():
         result = run_serve(args, torch, pkv, workloads)
     elif args.workload == "beam":
         result = run_beam(args, torch, pkv, workloads)
-    elif args.workload == "prefill":
+    elif args.workload in ("prefill", "prefill_gqa"):
         result = run_prefill(args, torch, pkv, workloads)
     else:
         wb = DecodeBench(args.workload, args, torch, pkv, workloads)

@@ -11,8 +11,10 @@
 // * bs + pos % bs), its own K/V already written.  Scale 1/sqrt(head_dim)
 // and float output as in the article's kernel listing.
 //
-// Design.  One workgroup of 4 waves per (query head, 128-row query tile,
-// sequence); wave w owns two 16-row query tiles.  The tile's K/V blocks are
+// Design.  One workgroup of 4 waves per (query heads, query tile,
+// sequence): hg = 4, 2 or 1 query heads of one KV group (the largest that
+// divides the group) over 128 / hg rows, wave w serving head w % hg and
+// rows 32 (w / hg) .. +31 as two 16-row query tiles.  The tile's K/V blocks are
 // streamed through LDS once for all four waves, two blocks (32 keys) per
 // stage (double-buffered, one barrier per stage; the next stage's loads are
 // in flight while the current one is used), with block ids read by scalar
@@ -65,7 +67,7 @@ constexpr int kPRsrcWord3 = 0x00020000;     // buffer descriptor word 3: 32-bit 
 #endif
 constexpr int kQW = PKV_PF_QW;
 constexpr int kKB = PKV_PF_KB;
-constexpr int kQTile = 16 * kQW * kPWaves;  // query rows per workgroup
+constexpr int kQTile = 16 * kQW * kPWaves;  // query rows per workgroup of one head
 
 struct PrefillArgs {
   float* out;
@@ -77,6 +79,7 @@ struct PrefillArgs {
   const int32_t* lens;         // [B]
   int32_t num_tokens;          // rows of q and out
   int32_t max_blocks, max_query_len, hq, hkv, num_blocks;
+  int32_t hg;                  // query heads per workgroup (1, 2 or 4; divides hq / hkv)
   float scale_log2;
 };
 
@@ -111,11 +114,16 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
   __shared__ __attribute__((aligned(16))) char s_k[2][SROWS * VROW];
   __shared__ __attribute__((aligned(16))) char s_v[2][SROWS * VROW];
 
-  const int h = blockIdx.x, tile = blockIdx.y, b = blockIdx.z;
+  const int tile = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar
   const int t = lane & 15, qa = lane >> 4;
-  const int g = h / (a.hq / a.hkv);
+  // The workgroup takes hg query heads of one KV group over rows_wg rows:
+  // wave w serves head h0 + w % hg and the 32-row block w / hg, so every
+  // K/V stage staged in LDS is read for hg heads.
+  const int hg = a.hg, rows_wg = kQTile / hg;
+  const int h0 = blockIdx.x * hg, h = h0 + w % hg;
+  const int g = h0 / (a.hq / a.hkv);
   const int q0 = a.qstart[b], q1 = a.qstart[b + 1], total = a.num_tokens;
   const int ql = q1 - q0, n = a.lens[b];
   const bool valid = ql >= 0 && ql <= a.max_query_len && ql <= n &&
@@ -124,19 +132,21 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
     // Invalid lengths: NaN rows for this sequence's queries (when the row
     // range itself is sane), written once by tile 0.
     if (tile == 0 && q0 >= 0 && q1 <= total && q0 <= q1)
-      for (int i = tid; i < (q1 - q0) * D; i += kPThreads)
-        a.out[(static_cast<size_t>(q0 + i / D) * a.hq + h) * D + i % D] = __builtin_nanf("");
+      for (int i = tid; i < (q1 - q0) * D * hg; i += kPThreads) {
+        const int r = i / (D * hg), hh = (i / D) % hg;
+        a.out[(static_cast<size_t>(q0 + r) * a.hq + h0 + hh) * D + i % D] = __builtin_nanf("");
+      }
     return;
   }
-  const int row0 = tile * kQTile;
+  const int row0 = tile * rows_wg;
   if (row0 >= ql) return;
   const int cached = n - ql;
-  const int rows_here = min(kQTile, ql - row0);
+  const int rows_here = min(rows_wg, ql - row0);
   const int last_pos_wg = cached + row0 + rows_here - 1;   // last query position of the tile
   const int nblk = last_pos_wg / kPBlock + 1;
   const int nstage = (nblk + kKB - 1) / kKB;
   // This wave's rows: kQW tiles of 16; lane t is row t of each tile.
-  const int wrow0 = row0 + 16 * kQW * w;
+  const int wrow0 = row0 + 16 * kQW * (w / hg);
   const int wrows = max(0, min(16 * kQW, ql - wrow0));
   const int wave_last_pos = wrows > 0 ? cached + wrow0 + wrows - 1 : -1;
   int my_pos[kQW];
@@ -372,8 +382,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
 
 template <int DT>
 hipError_t launch_prefill(const PrefillArgs& a, int B, int D, hipStream_t st) {
-  const int tiles = (a.max_query_len + kQTile - 1) / kQTile;
-  dim3 grid(a.hq, tiles, B);
+  const int rows_wg = kQTile / a.hg;
+  const int tiles = (a.max_query_len + rows_wg - 1) / rows_wg;
+  dim3 grid(a.hq / a.hg, tiles, B);
   if (D == 64)
     prefill_mfma<DT, 64><<<grid, kPThreads, 0, st>>>(a);
   else
@@ -404,7 +415,9 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
   if (B == 0 || num_tokens == 0 || max_query_len == 0) { clear_error(); return PA_OK; }
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
     return fail(PA_ERR_INVALID, "pa_prefill: null pointer");
-  if (B > 65535 || (max_query_len + kQTile - 1) / kQTile > 65535)
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int32_t hg = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
+  if (B > 65535 || (max_query_len + kQTile / hg - 1) / (kQTile / hg) > 65535)
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: grid too large");
   if (static_cast<size_t>(num_kv_heads) * head_dim * 2 * kPBlock * static_cast<size_t>(num_blocks) >
       (static_cast<size_t>(1) << 47))
@@ -428,6 +441,7 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
   a.hq = num_q_heads;
   a.hkv = num_kv_heads;
   a.num_blocks = num_blocks;
+  a.hg = hg;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err = dtype == PA_DTYPE_F16 ? launch_prefill<PA_DTYPE_F16>(a, B, head_dim, st)

@@ -3,8 +3,8 @@ paged cache) against the float64 oracle ref_prefill.
 
 Cases: fully uncached prompts, suffixes after cached prefixes whose length
 is not a multiple of the block size, one-token suffixes, suffixes spanning
-several 64-row tiles with a ragged last tile, GQA groups, head_dim 64 and
-128, float16 and bfloat16, NaN-poisoned unused slots, empty suffixes,
+several 64-row tiles with a ragged last tile, GQA groups of 2, 4, 6 and 8
+(one, two or four query heads per workgroup), head_dim 64 and 128, float16 and bfloat16, NaN-poisoned unused slots, empty suffixes,
 invalid lengths and bad table entries (NaN rows only for that sequence),
 and block placement invariance.
 """
@@ -56,6 +56,9 @@ CASES = [
     ([1, 5, 33, 100], [17, 100, 50, 300], 8, 2, 128),             # cached prefixes (17-1, 95, 17, 200)
     ([200, 3], [333, 3], 4, 1, 64),                                # 4 tiles, MQA
     ([129, 0, 12], [129, 40, 27], 8, 8, 64),                       # empty suffix in the middle
+    ([70, 33, 1], [300, 33, 90], 16, 2, 128),                      # group 8: 4 heads per workgroup
+    ([65, 129], [65, 500], 12, 2, 64),                             # group 6: 2 heads per workgroup
+    ([40, 97], [200, 97], 8, 4, 128),                              # group 2
 ]
 
 
@@ -101,11 +104,13 @@ def test_prefill_last_row_equals_decode():
     assert np.abs(out[last].cpu().numpy() - dec.cpu().numpy()).max() <= 2 * TOL["bf16"]
 
 
-def test_prefill_invalid_sequences_get_nan_rows_only():
-    """q_b > n, and a table entry outside the pool: NaN rows for that
-    sequence, the others exact."""
-    bs, nb, hq, hkv, d = 16, 24, 4, 4, 64
-    say("prefill invalid")
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (12, 2)])
+def test_prefill_invalid_sequences_get_nan_rows_only(hq, hkv):
+    """q_b > n, and a table entry outside the pool: NaN rows (every head)
+    for that sequence, the others exact; one and several query heads per
+    workgroup."""
+    bs, nb, d = 16, 24, 64
+    say("prefill invalid", hq, hkv)
     lens = [20, 30, 18]
     qlens = [5, 31, 18]                  # sequence 1: suffix longer than the sequence
     tables = random_tables(lens, bs, nb, 4, pad=0)
