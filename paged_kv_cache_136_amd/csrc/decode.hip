@@ -32,8 +32,9 @@
 //   its four partitions before writing (decode_phase1_mfma).
 // Shared-prefix plans add a matrix-core pass over each group's shared
 //   partitions, read once for all members, before the private pass.
-// Phase 2 -- one workgroup of 4 waves per (query head, sequence) merges the
-//   partitions.
+// Phase 2 merges the partitions: one workgroup of 4 waves per (query head,
+//   sequence), or, with at most 16 partitions and at least 1024 such pairs,
+//   one wave per pair and four pairs per workgroup (decode_reduce_wave).
 //
 // Memory traffic is dominated by K and V: 2*len*Hkv*head_dim*elem bytes per
 // sequence and layer; every byte is read once.  Q, tables and partials are
