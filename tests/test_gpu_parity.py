@@ -183,6 +183,17 @@ def test_decode_many_pairs(dtype, d, group):
     assert np.abs(got - want).max() <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,group", [("f16", 1), ("bf16", 4)])
+def test_decode_many_sequences(dtype, group):
+    """3000 short sequences (1-48 tokens, 16-token partitions): a 3000-row
+    grid and 24,000 (head, sequence) pairs through the one-wave reduce."""
+    lens = [int(x) for x in np.random.default_rng(17).integers(1, 49, size=3000)]
+    say("decode_many_sequences", dtype, group)
+    got, want = _run_decode(lens, 8, 8 // group, 64, dtype, 16, seed=41 + group)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("group", [1, 4])
 @pytest.mark.parametrize("partition", [0, 64])

@@ -86,6 +86,18 @@ def test_prefill_large_scores(dtype):
     assert err <= TOL[dtype], err
 
 
+def test_prefill_many_sequences():
+    """300 sequences with 1-20 uncached tokens after 0-40 cached ones:
+    a 300-deep grid of single-tile suffixes, GQA group 2."""
+    rng = np.random.default_rng(23)
+    qlens = [int(x) for x in rng.integers(1, 21, size=300)]
+    lens = [q + int(c) for q, c in zip(qlens, rng.integers(0, 41, size=300))]
+    say("prefill many sequences")
+    got, want = run_case(qlens, lens, 4, 2, 64, "f16", seed=7)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL["f16"]
+
+
 def test_prefill_last_row_equals_decode():
     """The last suffix row's output is the decode of that token."""
     qlens, lens, hq, hkv, d = [40, 9], [300, 9], 8, 4, 128
