@@ -51,7 +51,14 @@ struct CopyArgs {
   int32_t num_blocks;
 };
 
-// grid: x = chunk groups of a block, y = pair, z = 2 * layer + {0: K, 1: V}.
+// grid: x = groups of kCopyGroup chunks of a block, y = pair,
+// z = 2 * layer + {0: K, 1: V}.  A thread moves kCopyPerThread chunks per
+// group, all loads issued before the stores, so they are in flight
+// together.  Plain (cached) loads and stores: the decode that follows a
+// copy-on-write reads both blocks again.
+constexpr int kCopyPerThread = 4;
+constexpr int kCopyGroup = 256 * kCopyPerThread;   // chunks per workgroup pass
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
   const int pair = blockIdx.y;
   const int layer = blockIdx.z >> 1;
@@ -60,9 +67,31 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
   uint4* base = (blockIdx.z & 1) ? a.v[layer] : a.k[layer];
   const uint4* s = base + static_cast<int64_t>(src) * a.chunks_per_block;
   uint4* d = base + static_cast<int64_t>(dst) * a.chunks_per_block;
-  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < a.chunks_per_block;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-    d[i] = s[i];
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* sv = reinterpret_cast<const u32x4*>(s);
+  u32x4* dv = reinterpret_cast<u32x4*>(d);
+  for (int64_t g = blockIdx.x * static_cast<int64_t>(kCopyGroup); g < a.chunks_per_block;
+       g += static_cast<int64_t>(gridDim.x) * kCopyGroup) {
+    u32x4 r[kCopyPerThread];
+    if (g + kCopyGroup <= a.chunks_per_block) {
+      // A whole group: no per-chunk test, so the loads issue back to back.
+#pragma unroll
+      for (int u = 0; u < kCopyPerThread; ++u) r[u] = sv[g + u * 256 + threadIdx.x];
+#pragma unroll
+      for (int u = 0; u < kCopyPerThread; ++u) dv[g + u * 256 + threadIdx.x] = r[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCopyPerThread; ++u) {
+        const int64_t i = g + u * 256 + threadIdx.x;
+        if (i < a.chunks_per_block) r[u] = sv[i];
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyPerThread; ++u) {
+        const int64_t i = g + u * 256 + threadIdx.x;
+        if (i < a.chunks_per_block) dv[i] = r[u];
+      }
+    }
+  }
 }
 
 int elem_bytes(int32_t dtype) {
@@ -127,7 +156,7 @@ extern "C" int pa_copy_blocks(void* const* k_caches, void* const* v_caches, int3
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t cpb = block_bytes / 16;
-  int64_t gx = (cpb + 1023) / 1024;   // ~4 chunks per thread
+  int64_t gx = (cpb + kCopyGroup - 1) / kCopyGroup;   // kCopyPerThread chunks per thread
   if (gx < 1) gx = 1;
   if (gx > 1024) gx = 1024;
   for (int32_t l0 = 0; l0 < num_layers; l0 += kMaxLayersPerLaunch) {
