@@ -284,6 +284,12 @@ class DecodeBench:
             step_ev[i][1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # The device's tables and lengths (uploaded only when changed) must
+        # be the block manager's after the last step.
+        tab_now, len_now = self.bm.export_batch(self.seqs, self.max_blocks, 0)
+        if not (np.array_equal(self.d_tab.cpu().numpy(), tab_now) and
+                np.array_equal(self.d_len.cpu().numpy(), len_now)):
+            raise RuntimeError("device block tables differ from the block manager's")
         step_gpu_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
         gpu_s = step_gpu_ms.sum() * 1e-3
         timed_s = gpu_s if small else wall
