@@ -221,7 +221,9 @@ class DecodeBench:
         return (buf[:o1].view(torch.int64), buf[o3:].view(torch.int32).view(B, mb),
                 buf[o1:o2].view(torch.int32), buf[o2:o3].view(torch.int32).view(B, 2))
 
-    def step(self, s, ev_pairs=None):
+    def step(self, s, ev_pairs=None, ev_start=None):
+        """One step; ev_start, if given, is recorded after the host work,
+        right before the step's first GPU operation (the upload)."""
         pkv, p = self.pkv, self.pin[s % 2]
         p["ev"].synchronize()                 # its previous upload has run
         h0 = time.perf_counter()
@@ -237,6 +239,8 @@ class DecodeBench:
         changed = self.first_upload or len(pairs) > 0 or bool(np.any(slots % self.bs == 0))
         self.first_upload = False
         used = self.stage_bytes if changed else self.tab_off
+        if ev_start is not None:
+            ev_start.record()
         self.d_stage[:used].copy_(p["buf"][:used], non_blocking=True)
         p["ev"].record()
         if len(pairs):
@@ -279,8 +283,7 @@ class DecodeBench:
         for i in range(args.steps):
             if small:
                 scratch.fill_(i & 0xff)
-            step_ev[i][0].record()
-            self.step(args.warmup + i, events.get(i))
+            self.step(args.warmup + i, events.get(i), step_ev[i][0])
             step_ev[i][1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
