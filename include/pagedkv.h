@@ -416,7 +416,8 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  *   q:    device [B][num_q_heads][head_dim] in `dtype`.
  *   k_cache, v_cache: device, one layer, layout above, in `dtype`.
  *   block_tables: device int32 [B][max_blocks_per_seq]; entries past a
- *     sequence's last block are never read.
+ *     sequence's last block are never read; may be NULL when
+ *     max_blocks_per_seq is 0.
  *   context_lens: device int32 [B].
  *   max_context_len: host-side upper bound of context_lens (sizes the grid;
  *     no device-to-host read is made).

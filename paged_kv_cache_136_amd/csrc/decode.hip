@@ -1028,7 +1028,8 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
   if (n_groups < 0 || max_shared_parts < 0 || max_private_parts < 0)
     return err_(PA_ERR_INVALID, "negative n_groups, max_shared_parts or max_private_parts");
   if (B == 0) { clear_error(); return PA_OK; }
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+  // A table of width 0 has no entries and may be NULL.
+  if (!out || !q || !k_cache || !v_cache || (!block_tables && max_blocks_per_seq > 0) || !context_lens)
     return err_(PA_ERR_INVALID, "null pointer");
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return err_(PA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");

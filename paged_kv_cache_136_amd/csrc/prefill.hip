@@ -413,7 +413,9 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     return fail(PA_ERR_UNSUPPORTED, "pa_prefill: float16 or bfloat16 only (matrix-core path)");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_prefill: bad scale");
   if (B == 0 || num_tokens == 0 || max_query_len == 0) { clear_error(); return PA_OK; }
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start || !context_lens)
+  // A table of width 0 has no entries and may be NULL.
+  if (!out || !q || !k_cache || !v_cache || (!block_tables && max_blocks_per_seq > 0) || !query_start ||
+      !context_lens)
     return fail(PA_ERR_INVALID, "pa_prefill: null pointer");
   const int32_t group = num_q_heads / num_kv_heads;
   const int32_t hg = group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;

@@ -236,6 +236,20 @@ def test_decode_edge_cases():
         pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(), lens_dev, 50, partition_tokens=24)
 
 
+@pytest.mark.parametrize("hq,hkv,dtype", [(4, 4, "f16"), (8, 2, "bf16"), (4, 2, "f32")])
+def test_decode_zero_width_tables(hq, hkv, dtype):
+    """Every sequence empty and tables of width 0: zero rows, nothing read."""
+    k, v = make_cache(4, 16, hkv, 64, dtype, seed=6)
+    q = workloads.normal_torch((3, hq, 64), 7, TORCH_DTYPES[dtype], "cuda")
+    say("decode zero-width tables", hq, hkv, dtype)
+    for pt in (0, 64):
+        out = pkv.pa_decode(q, k, v, torch.empty((3, 0), dtype=torch.int32, device="cuda"),
+                            torch.zeros(3, dtype=torch.int32, device="cuda"), 0,
+                            partition_tokens=pt)
+        torch.cuda.synchronize()
+        assert (out.cpu().numpy() == 0).all()
+
+
 def test_placement_invariance():
     """The same logical K/V under two different tables gives bitwise-equal
     outputs (the kernel's arithmetic depends only on logical positions)."""
