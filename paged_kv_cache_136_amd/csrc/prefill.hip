@@ -114,7 +114,9 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
   __shared__ __attribute__((aligned(16))) char s_k[2][SROWS * VROW];
   __shared__ __attribute__((aligned(16))) char s_v[2][SROWS * VROW];
 
-  const int tile = blockIdx.y, b = blockIdx.z;
+  // Heaviest tiles first: a tile's keys grow with its index (causal), so
+  // the grid dispatches the last tiles first and the cheap ones fill in.
+  const int tile = gridDim.y - 1 - blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar
   const int t = lane & 15, qa = lane >> 4;
