@@ -98,6 +98,38 @@ def test_prefill_many_sequences():
     assert np.abs(got - want).max() <= TOL["f16"]
 
 
+def test_prefill_bench_config_sampled():
+    """The bench's launch configuration at full size: 16 sequences share a
+    1024-token cached prefix (64 blocks, as prefix hits leave them) and each
+    adds 1024 uncached tokens; 32 heads x 128, fp16.  64 sampled rows against
+    the oracle, each as the one-token suffix at its own position."""
+    B, pre, sfx, H, D, bs = 16, 1024, 1024, 32, 128, 16
+    n = pre + sfx
+    shared, own = pre // bs, sfx // bs
+    nb = shared + B * own + 4
+    perm = np.random.default_rng(9).permutation(nb).astype(np.int32)
+    tables = np.zeros((B, n // bs), dtype=np.int32)
+    tables[:, :shared] = perm[:shared]
+    for b in range(B):
+        tables[b, shared:] = perm[shared + b * own:shared + (b + 1) * own]
+    lens = np.full(B, n, dtype=np.int32)
+    k, v = make_cache(nb, bs, H, D, "f16", seed=61, poison=poison_mask(tables, lens, nb, bs))
+    q = workloads.normal_torch((B * sfx, H, D), 62, torch.float16, "cuda")
+    qs = torch.arange(0, B * sfx + 1, sfx, dtype=torch.int32, device="cuda")
+    say("prefill bench config sampled")
+    out = pkv.pa_prefill(q, k, v, torch.from_numpy(tables).cuda(), qs,
+                         torch.from_numpy(lens).cuda(), sfx)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    qh, kh, vh = host_f32(q), host_f32(k), host_f32(v)
+    rows = np.random.default_rng(10).choice(B * sfx, size=64, replace=False)
+    for r in rows:
+        b, i = divmod(int(r), sfx)
+        want = oracle.ref_prefill(qh[r:r + 1], kh, vh, tables[b:b + 1], [1], [pre + i + 1])[0]
+        assert np.abs(got[r] - want).max() <= TOL["f16"], (r, b, i)
+
+
 def test_prefill_last_row_equals_decode():
     """The last suffix row's output is the decode of that token."""
     qlens, lens, hq, hkv, d = [40, 9], [300, 9], 8, 4, 128
