@@ -826,15 +826,100 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
 }
 
 // Phase 2: out = sum_p w_p * o_p with w_p = l_p 2^(m_p - M) / sum_q l_q 2^(m_q - M).
+//
+// Every memory access of a pair is issued so that few round trips are
+// serial: the (m, l) of the first 64 partitions are read once, one lane
+// each; a 64-partition window's weights are computed lane-parallel and each
+// is broadcast from its lane; and the partial rows are read four at a time
+// with buffer loads issued together.  A partition of weight exactly 0 (an
+// empty marker left by the matrix-core kernel's per-workgroup merge) adds
+// nothing, and its load gets an out-of-range offset, which the hardware
+// answers with zeros and no memory access; a NaN weight is read, so a bad
+// id keeps its NaN.
+
+// M = max_p m_p and the inverse of L = sum_p l_p 2^(m_p - M), the same in
+// every lane; l0 and m0 are this lane's partition of the first window.
+struct PairScale {
+  float M, inv, m0, l0;
+};
+__device__ __forceinline__ PairScale pair_scale(const DecodeArgs& a, size_t row0, int nparts, int lane) {
+  const int G = a.qgroup;
+  const float* pm = a.ws_m + row0;
+  const float* pl = a.ws_l + row0;
+  const bool in0 = lane < nparts;
+  PairScale ps;
+  ps.m0 = in0 ? pm[static_cast<size_t>(lane) * G] : -INFINITY;
+  ps.l0 = in0 ? pl[static_cast<size_t>(lane) * G] : 0.f;
+  float M = fmaxf(-INFINITY, ps.m0);
+  for (int p = lane + 64; p < nparts; p += 64) M = fmaxf(M, pm[static_cast<size_t>(p) * G]);
+  M = group_max<1, 64>(M);
+  float L = in0 ? ps.l0 * fast_exp2(ps.m0 - M) : 0.f;
+  for (int p = lane + 64; p < nparts; p += 64)
+    L += pl[static_cast<size_t>(p) * G] * fast_exp2(pm[static_cast<size_t>(p) * G] - M);
+  L = group_sum<1, 64>(L);
+  ps.M = M;
+  ps.inv = 1.f / L;
+  return ps;
+}
+
+// Weight of partition q0 + lane (0 past the last partition).
+__device__ __forceinline__ float window_weight(const DecodeArgs& a, size_t row0, int nparts, int q0,
+                                               const PairScale& ps, int lane) {
+  const int p = q0 + lane;
+  if (p >= nparts) return 0.f;
+  if (q0 == 0) return ps.l0 * fast_exp2(ps.m0 - ps.M) * ps.inv;
+  const size_t pr = static_cast<size_t>(p) * a.qgroup;
+  return a.ws_l[row0 + pr] * fast_exp2(a.ws_m[row0 + pr] - ps.M) * ps.inv;
+}
+
+// acc += w_p * o_p for p = q0 + lo .. q0 + hi - 1 in increasing order
+// (hi <= 64 and q0 + hi <= nparts; lo, hi wave-uniform), wl holding the
+// weight of partition q0 + lane.  Each lane owns D/64 adjacent dims.
+template <int D>
+__device__ __forceinline__ void accumulate_window(const DecodeArgs& a, size_t row0, int nparts, int q0,
+                                                  int lo, int hi, float wl, int lane,
+                                                  float (&acc)[D / 64]) {
+  constexpr int PER = D / 64;
+  const uint32_t row_stride = static_cast<uint32_t>(a.qgroup) * D * sizeof(float);
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(a.ws_o + row0 * D, 0,
+                                                    static_cast<int>(nparts * row_stride), kRsrcWord3);
+  const uint32_t lane_off = static_cast<uint32_t>(PER * lane) * sizeof(float);
+  for (int u0 = lo; u0 < hi; u0 += 4) {
+    float wt[4], v[4][PER];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int uu = u0 + u;
+      wt[u] = uu < hi ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(uu, 63))) : 0.f;
+      const uint32_t off =
+          wt[u] != 0.f ? static_cast<uint32_t>(q0 + uu) * row_stride + lane_off : 0x80000000u;
+      if constexpr (PER == 2) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        v[u][0] = __uint_as_float(t[0]);
+        v[u][1] = __uint_as_float(t[1]);
+      } else {
+        v[u][0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (wt[u] != 0.f) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt[u], v[u][e], acc[e]);
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
-  // One workgroup per (query head, sequence).  The four waves take every
-  // fourth partition (so four partial rows are in flight at once), each lane
-  // owning D/64 adjacent dims, and the four partial sums meet in LDS.
+  // One workgroup per (query head, sequence).  Each 64-partition window is
+  // split into four contiguous runs, one per wave, and the four partial
+  // sums meet in LDS.
   constexpr int PER = D / 64;
   static_assert(PER == 1 || PER == 2, "head_dim 64 or 128");
   __shared__ float s_acc[kWaves][D];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.lens[b];
   if (!len_valid(n, a)) return;
   const int nparts = num_parts_of(n, a.part_blocks);
@@ -842,31 +927,13 @@ __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
   const size_t bh = static_cast<size_t>(b) * a.hq + h;
   // Partition p's row is row0 + p * G (rows are [B][Hkv][P][G]).
   const size_t row0 = ws_row(a, b, h, 0);
-  const int G = a.qgroup;
-  const float* pm = a.ws_m + row0;
-  const float* pl = a.ws_l + row0;
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, pm[static_cast<size_t>(p) * G]);
-  M = group_max<1, 64>(M);
-  float L = 0.f;
-  for (int p = lane; p < nparts; p += 64)
-    L += pl[static_cast<size_t>(p) * G] * fast_exp2(pm[static_cast<size_t>(p) * G] - M);
-  L = group_sum<1, 64>(L);
-  const float inv = 1.f / L;
+  const PairScale ps = pair_scale(a, row0, nparts, lane);
   float acc[PER] = {};
-  const float* po = a.ws_o + row0 * D + PER * lane;
-#pragma unroll 4
-  for (int p = __builtin_amdgcn_readfirstlane(w); p < nparts; p += kWaves) {
-    const size_t pr = static_cast<size_t>(p) * G;
-    const float wgt = pl[pr] * fast_exp2(pm[pr] - M) * inv;
-    if (wgt == 0.f) continue;            // an empty partition (merged into another); NaN passes
-    if constexpr (PER == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(po + pr * D);
-      acc[0] = fmaf(wgt, v.x, acc[0]);
-      acc[1] = fmaf(wgt, v.y, acc[1]);
-    } else {
-      acc[0] = fmaf(wgt, po[pr * D], acc[0]);
-    }
+  for (int q0 = 0; q0 < nparts; q0 += 64) {
+    const int cnt = min(64, nparts - q0);
+    const int per = (cnt + kWaves - 1) / kWaves;
+    const float wl = window_weight(a, row0, nparts, q0, ps, lane);
+    accumulate_window<D>(a, row0, nparts, q0, min(w * per, cnt), min((w + 1) * per, cnt), wl, lane, acc);
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) s_acc[w][PER * lane + e] = acc[e];
@@ -879,9 +946,7 @@ __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
 // per workgroup, for batches of at most kReduceWaveParts partitions and
 // enough pairs to give every CU a workgroup: there a pair's few partial rows
 // leave four waves mostly waiting, and the LDS merge and barrier are pure
-// latency.  Each lane owns D/64 adjacent dims and walks
-// the partitions in order; a partition's weight comes from scalar reads of
-// its (m, l), the same in every lane.
+// latency.
 constexpr int kReduceWaveParts = 16;
 constexpr int kReduceWaveMinPairs = kWaves * 256;   // one workgroup per CU
 
@@ -898,31 +963,11 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_wave(DecodeArgs a) {
   const int nparts = num_parts_of(n, a.part_blocks);
   if (nparts <= 1) return;                 // phase 1 wrote the output
   const size_t row0 = ws_row(a, b, h, 0);
-  const int G = a.qgroup;
-  const float* pm = a.ws_m + row0;
-  const float* pl = a.ws_l + row0;
-  float M = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) M = fmaxf(M, pm[static_cast<size_t>(p) * G]);
-  M = group_max<1, 64>(M);
-  float L = 0.f;
-  for (int p = lane; p < nparts; p += 64)
-    L += pl[static_cast<size_t>(p) * G] * fast_exp2(pm[static_cast<size_t>(p) * G] - M);
-  L = group_sum<1, 64>(L);
-  const float inv = 1.f / L;
+  const PairScale ps = pair_scale(a, row0, nparts, lane);
   float acc[PER] = {};
-  const float* po = a.ws_o + row0 * D + PER * lane;
-#pragma unroll 4
-  for (int p = 0; p < nparts; ++p) {
-    const size_t pr = static_cast<size_t>(p) * G;
-    const float wgt = pl[pr] * fast_exp2(pm[pr] - M) * inv;
-    if (wgt == 0.f) continue;            // an empty partition (merged into another); NaN passes
-    if constexpr (PER == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(po + pr * D);
-      acc[0] = fmaf(wgt, v.x, acc[0]);
-      acc[1] = fmaf(wgt, v.y, acc[1]);
-    } else {
-      acc[0] = fmaf(wgt, po[pr * D], acc[0]);
-    }
+  for (int q0 = 0; q0 < nparts; q0 += 64) {
+    const float wl = window_weight(a, row0, nparts, q0, ps, lane);
+    accumulate_window<D>(a, row0, nparts, q0, 0, min(64, nparts - q0), wl, lane, acc);
   }
   float* orow = a.out + (static_cast<size_t>(b) * a.hq + h) * D + PER * lane;
   if constexpr (PER == 2)
