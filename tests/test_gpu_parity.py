@@ -81,7 +81,7 @@ def test_copy_blocks_bitexact():
 # ---------------------------------------------------------------- decode
 
 def _run_decode(lens, hq, hkv, d, dtype, partition, seed, poison=True, num_blocks=None,
-                q_scale=1.0):
+                q_scale=1.0, workspace=None):
     bs = 16
     need = sum(-(-int(n) // bs) for n in lens)
     num_blocks = num_blocks or need + 5
@@ -94,7 +94,7 @@ def _run_decode(lens, hq, hkv, d, dtype, partition, seed, poison=True, num_block
     max_len = int(max(lens)) if len(lens) else 0
     out = pkv.pa_decode(q, k, v, torch.from_numpy(tables).cuda(),
                         torch.tensor(lens, dtype=torch.int32, device="cuda"), max_len,
-                        partition_tokens=partition)
+                        partition_tokens=partition, workspace=workspace)
     torch.cuda.synchronize()
     want = oracle.ref_decode(host_f32(q), host_f32(k), host_f32(v), tables, lens)
     return out.cpu().numpy().astype(np.float64), want
@@ -120,6 +120,27 @@ def test_decode_partition_sizes(partition):
     say("decode_partition", partition)
     got, want = _run_decode([1, 300, 1000, 2049], 8, 4, 128, "f16", partition, seed=7)
     assert np.abs(got - want).max() <= TOL["f16"]
+
+
+@pytest.mark.parametrize("poison_ws", [False, True])
+@pytest.mark.parametrize("dtype,group", [("bf16", 4), ("f16", 8), ("f16", 1)])
+def test_decode_many_partitions_windows(dtype, group, poison_ws):
+    """More than 64 partitions per sequence: the reduce walks several
+    64-partition windows.  On the matrix-core path (groups 4 and 8) every
+    fourth row holds the merged result of its workgroup and the rest are
+    empty markers whose output rows are never written; a NaN-filled
+    workspace shows that no such row, and nothing outside the rows phase 1
+    wrote, reaches the output."""
+    lens = [1, 300, 1000, 2049, 3001]
+    hq = 2 * group
+    say("decode_many_parts", dtype, group, poison_ws)
+    ws = None
+    if poison_ws:
+        need = pkv.pa_decode_workspace_bytes(len(lens), hq, 128, max(lens), 16)
+        ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    got, want = _run_decode(lens, hq, 2, 128, dtype, 16, seed=11, workspace=ws)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]
 
 
 @pytest.mark.parametrize("partition", [16, 32, 48, 64, 512])
@@ -183,13 +204,20 @@ def test_decode_many_pairs(dtype, d, group):
     assert np.abs(got - want).max() <= TOL[dtype]
 
 
+@pytest.mark.parametrize("poison_ws", [False, True])
 @pytest.mark.parametrize("dtype,group", [("f16", 1), ("bf16", 4)])
-def test_decode_many_sequences(dtype, group):
+def test_decode_many_sequences(dtype, group, poison_ws):
     """3000 short sequences (1-48 tokens, 16-token partitions): a 3000-row
-    grid and 24,000 (head, sequence) pairs through the one-wave reduce."""
+    grid and 24,000 (head, sequence) pairs through the one-wave reduce, also
+    with a NaN-filled workspace (the matrix-core path leaves the output rows
+    of its empty markers unwritten)."""
     lens = [int(x) for x in np.random.default_rng(17).integers(1, 49, size=3000)]
-    say("decode_many_sequences", dtype, group)
-    got, want = _run_decode(lens, 8, 8 // group, 64, dtype, 16, seed=41 + group)
+    say("decode_many_sequences", dtype, group, poison_ws)
+    ws = None
+    if poison_ws:
+        need = pkv.pa_decode_workspace_bytes(len(lens), 8, 64, max(lens), 16)
+        ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    got, want = _run_decode(lens, 8, 8 // group, 64, dtype, 16, seed=41 + group, workspace=ws)
     assert np.isfinite(got).all()
     assert np.abs(got - want).max() <= TOL[dtype]
 
