@@ -423,7 +423,9 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  *     no device-to-host read is made).
  *   partition_tokens: multiple of block_size, or 0 for one partition.
  *   workspace: device, >= pa_decode_workspace_bytes(...) bytes, 16-byte
- *     aligned (may be NULL when that is 0).
+ *     aligned (may be NULL when that is 0).  Scratch owned by the caller:
+ *     its contents on entry do not matter, and it holds partition results
+ *     afterwards; calls that overlap on one workspace race.
  * Supported: dtype F32/F16/BF16, head_dim 64 or 128, block_size 16,
  * num_q_heads a multiple of num_kv_heads with group size 1, 2, 4 or 8.
  * Degenerate and invalid inputs: n == 0 gives a zero output row; a
