@@ -66,3 +66,74 @@ def test_device_calls_validate_before_touching_the_gpu():
         ((4 * 8 * 8 * 128 * 4 + 255) // 256 * 256) + 2 * ((4 * 8 * 8 * 4 + 255) // 256 * 256))
     assert L.pa_decode_workspace_bytes(4, 8, 128, 512, 512) == 0
     assert L.pa_decode_workspace_bytes(4, 8, 128, 4096, 0) == 0
+
+
+def _aligned_host_ptr(keep, nbytes=256):
+    """A 16-byte-aligned host address, used only as a stand-in pointer for
+    calls that must be rejected before any pointer is dereferenced."""
+    buf = ctypes.create_string_buffer(nbytes + 16)
+    keep.append(buf)
+    return (ctypes.addressof(buf) + 15) & ~15
+
+
+def test_decode_rejections_name_the_argument():
+    """Every pa_decode argument check returns its status and message from the
+    host, with non-null (host) stand-in pointers: the checks run before any
+    HIP call, so none of these reaches the device."""
+    from paged_kv_cache_136_amd import lib
+    L = lib()
+    keep = []
+    p = _aligned_host_ptr(keep)
+    base = dict(B=2, hq=8, hkv=2, d=128, bs=16, nb=64, scale=0.088, pt=0, dtype=1,
+                max_len=64, ws=None, ws_bytes=0, q=p)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.pa_decode(p, a["q"], p, p, p, 8, p, a["max_len"], a["B"], a["hq"], a["hkv"],
+                           a["d"], a["bs"], a["nb"], a["scale"], a["pt"], a["dtype"], a["ws"],
+                           a["ws_bytes"], None)
+
+    cases = [
+        (dict(hq=6, hkv=4), 2, b"multiple of num_kv_heads"),
+        (dict(hq=6, hkv=2), 3, b"group size"),
+        (dict(bs=8), 3, b"block_size"),
+        (dict(d=96), 3, b"head_dim"),
+        (dict(dtype=7), 3, b"dtype"),
+        (dict(pt=24), 2, b"partition_tokens"),
+        (dict(scale=float("nan")), 2, b"finite"),
+        (dict(q=p + 4), 2, b"aligned"),
+        (dict(B=70000), 3, b"65535 sequences"),
+        (dict(max_len=16 * 65536, pt=16), 3, b"partitions"),
+        (dict(max_len=4096, pt=512), 2, b"workspace too small"),
+        (dict(nb=0), 2, b"empty pool"),
+    ]
+    for kw, status, msg in cases:
+        assert call(**kw) == status, kw
+        assert msg in L.pa_last_error(), (kw, L.pa_last_error())
+
+
+def test_write_and_copy_rejections():
+    from paged_kv_cache_136_amd import lib
+    L = lib()
+    keep = []
+    p = _aligned_host_ptr(keep)
+    # pa_write_kv(k, v, k_new, v_new, slots, T, num_blocks, bs, hkv, d, dtype, stream)
+    assert L.pa_write_kv(p, p, p, p, p, 4, 8, 16, 1, 64, 9, None) == 3
+    assert b"dtype" in L.pa_last_error()
+    assert L.pa_write_kv(p, p, p, p, p, 4, 8, 16, 1, 4, 1, None) == 3      # 8-byte rows
+    assert b"multiple of 16 bytes" in L.pa_last_error()
+    assert L.pa_write_kv(p, p, p + 8, p, p, 4, 8, 16, 1, 64, 1, None) == 2
+    assert b"aligned" in L.pa_last_error()
+    assert L.pa_write_kv(p, p, p, p, p, 0, 8, 16, 1, 64, 1, None) == 0     # T == 0: nothing to do
+    # pa_copy_blocks(k_caches, v_caches, layers, block_bytes, num_blocks, pairs, num_pairs, stream)
+    arr = (ctypes.c_void_p * 1)(p)
+    nul = (ctypes.c_void_p * 1)(None)
+    assert L.pa_copy_blocks(arr, arr, 1, 24, 8, p, 1, None) == 2            # not a multiple of 16
+    assert b"block_bytes" in L.pa_last_error()
+    assert L.pa_copy_blocks(arr, arr, 1, 4096, 8, p, 70000, None) == 3
+    assert b"65535 pairs" in L.pa_last_error()
+    assert L.pa_copy_blocks(arr, nul, 1, 4096, 8, p, 1, None) == 2
+    assert b"null cache pointer" in L.pa_last_error()
+    mis = (ctypes.c_void_p * 1)(p + 4)
+    assert L.pa_copy_blocks(mis, arr, 1, 4096, 8, p, 1, None) == 2
+    assert b"aligned" in L.pa_last_error()
