@@ -137,3 +137,56 @@ def test_write_and_copy_rejections():
     mis = (ctypes.c_void_p * 1)(p + 4)
     assert L.pa_copy_blocks(mis, arr, 1, 4096, 8, p, 1, None) == 2
     assert b"aligned" in L.pa_last_error()
+
+
+def test_prefill_and_swap_rejections():
+    """The same for pa_prefill and the swap calls (their checks before the
+    first HIP call; swap's pinned-memory check is a HIP query and is left
+    to the GPU tests)."""
+    from paged_kv_cache_136_amd import lib
+    L = lib()
+    keep = []
+    p = _aligned_host_ptr(keep)
+
+    def prefill(hq=8, hkv=2, d=128, bs=16, dtype=1, scale=0.088, q=p, B=2, maxq=64):
+        # (out, q, k, v, tables, max_blocks, query_start, lens, B, num_tokens,
+        #  max_query_len, hq, hkv, d, bs, num_blocks, scale, dtype, stream)
+        return L.pa_prefill(p, q, p, p, p, 8, p, p, B, 128, maxq, hq, hkv, d, bs, 64, scale,
+                            dtype, None)
+
+    for kw, status, msg in [
+        (dict(hq=6, hkv=4), 2, b"Hq % Hkv"),
+        (dict(d=96), 3, b"head_dim"),
+        (dict(bs=32), 3, b"block_size"),
+        (dict(dtype=0), 3, b"float16 or bfloat16"),
+        (dict(scale=-1.0), 2, b"bad scale"),
+        (dict(scale=float("inf")), 2, b"bad scale"),
+        (dict(B=70000), 3, b"grid too large"),
+        (dict(q=p + 2), 2, b"aligned"),
+    ]:
+        assert prefill(**kw) == status, kw
+        assert msg in L.pa_last_error(), (kw, L.pa_last_error())
+    assert prefill(maxq=0) == 0                                         # nothing to do
+
+    arr = (ctypes.c_void_p * 1)(p)
+    nul = (ctypes.c_void_p * 1)(None)
+    mis = (ctypes.c_void_p * 1)(p + 4)
+    rec = 2 * 4096                                                      # one layer, K and V
+    for fn in (L.pa_swap_out, L.pa_swap_in):
+        # (k_caches, v_caches, layers, block_bytes, num_blocks, blocks, host_slots, n, host,
+        #  host_bytes, stream)
+        assert fn(arr, arr, 1, 24, 8, p, None, 1, p, rec, None) == 2
+        assert b"block_bytes" in L.pa_last_error()
+        assert fn(arr, arr, 1, 4096, 8, p, None, 70000, p, rec * 70000, None) == 3
+        assert b"65535 blocks" in L.pa_last_error()
+        assert fn(arr, arr, 1, 4096, 8, p, None, 3, p, 2 * rec, None) == 2
+        assert b"needed" in L.pa_last_error()
+        assert fn(arr, arr, 1, 4096, 8, p, p, 3, p, rec - 16, None) == 2    # not one record
+        assert b"at least one record" in L.pa_last_error()
+        assert fn(arr, arr, 1, 4096, 8, p, None, 1, p + 8, rec, None) == 2
+        assert b"host buffer must be 16-byte aligned" in L.pa_last_error()
+        assert fn(arr, nul, 1, 4096, 8, p, None, 1, p, rec, None) == 2
+        assert b"null cache pointer" in L.pa_last_error()
+        assert fn(mis, arr, 1, 4096, 8, p, None, 1, p, rec, None) == 2
+        assert b"caches must be 16-byte aligned" in L.pa_last_error()
+        assert fn(arr, arr, 1, 4096, 8, p, None, 0, p, rec, None) == 0     # n == 0
