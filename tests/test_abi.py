@@ -190,3 +190,29 @@ def test_prefill_and_swap_rejections():
         assert fn(mis, arr, 1, 4096, 8, p, None, 1, p, rec, None) == 2
         assert b"caches must be 16-byte aligned" in L.pa_last_error()
         assert fn(arr, arr, 1, 4096, 8, p, None, 0, p, rec, None) == 0     # n == 0
+
+
+def test_shared_decode_plan_rejections():
+    from paged_kv_cache_136_amd import lib
+    L = lib()
+    keep = []
+    p = _aligned_host_ptr(keep)
+
+    def shared(n_groups=1, seq_group=p, groups=p, dtype=1, pt=512, max_shared=1):
+        # pa_decode's arguments (64-token context, one partition: no workspace), then
+        # (seq_group, groups, n_groups, max_shared_parts, max_private_parts, ws, ws_bytes, stream)
+        return L.pa_decode_shared(p, p, p, p, p, 8, p, 64, 2, 8, 2, 128, 16, 64, 0.088, pt,
+                                  dtype, seq_group, groups, n_groups, max_shared, 1, None, 0,
+                                  None)
+
+    for kw, status, msg in [
+        (dict(n_groups=-1), 2, b"negative n_groups"),
+        (dict(seq_group=None), 2, b"null plan pointer"),
+        (dict(groups=None), 2, b"null plan pointer"),
+        (dict(dtype=0), 3, b"F16 or BF16"),
+        (dict(pt=0), 2, b"partition_tokens > 0"),
+        (dict(n_groups=70000), 3, b"65535 plan groups"),
+        (dict(max_shared=70000), 3, b"65535 plan groups or shared partitions"),
+    ]:
+        assert shared(**kw) == status, kw
+        assert msg in L.pa_last_error(), (kw, L.pa_last_error())
