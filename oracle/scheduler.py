@@ -8,9 +8,9 @@ step, so the batch stays full) and ``ContinuousBatchingScheduler.step``
 requests first-come first-served until the batch is full or memory runs
 short, putting the one that does not fit back at the front; 3. run the
 batch; 4. append each request's new token, and when no block is left,
-preempt: the running request with the most generated tokens has its KV
-copied to CPU memory and its blocks freed).  Blocks come from the P06 block
-manager (``RefBlockManager``).
+preempt: ``_preempt_request`` takes the running request with the most
+generated tokens, copies its KV to CPU memory and frees its blocks).
+Blocks come from the P06 block manager (``RefBlockManager``).
 
 Readings where the page stops short (each also in the design notes):
 
@@ -19,13 +19,26 @@ Readings where the page stops short (each also in the design notes):
   appends the previous token (its K/V is written) and decodes the next one.
   A request with ``generated == max_new_tokens`` leaves at the start of the
   next step.  Tokens are handed in after each step with ``commit``.
+* The appends run in running order over the list as it stood when they
+  began; a request preempted earlier in the loop is skipped.  When an
+  append finds no block, the victim is the page's: the request with the
+  most generated tokens among all running requests (the first such in
+  running order, as ``max`` does on the page's list), whether or not it
+  has appended or was admitted in this step.  The failing request then
+  tries again, until its append succeeds or it is the victim itself.
+* Nothing is undone.  A victim that already appended keeps that token: its
+  K/V is written before its blocks are copied out, and it is not decoded in
+  this step.  A request whose last token is in the cache but not yet
+  decoded (preempted after its append or after its admission, then swapped
+  back in) joins a later step's decode batch without appending.
+* The step's device work follows the order of the decisions: each
+  preemption closes an epoch, and the copies and writes of the appends made
+  before it precede its swap-out copies, while blocks it frees are reused
+  only by later epochs.  ``plan["cuts"]`` holds, per preemption, the number
+  of writes and copy-on-write pairs before it and the number of swap-out
+  pairs through it.
 * Preempted requests (swapped out) come back before new ones are admitted,
   oldest preemption first, through ``RefBlockManager.swap_in``.
-* The victim is chosen among the running requests that have not yet
-  appended in this step and were not admitted in it (the failing one is
-  always among them), so no append is ever undone and no prompt is left
-  without its first token; ties go to the earliest in running order, as
-  ``max`` does on the page's list.
 * Host swap space is a pool of ``host_slots`` block-sized records handed out
   first-in first-out.  A victim whose blocks do not fit is recomputed
   instead: its blocks are freed and it returns to the front of the waiting
@@ -41,7 +54,7 @@ from .block_manager import OutOfBlocks
 
 
 class _Req:
-    __slots__ = ("id", "tokens", "max_new", "generated", "pending", "host", "appended")
+    __slots__ = ("id", "tokens", "max_new", "generated", "pending", "host")
 
     def __init__(self, rid, prompt, max_new):
         self.id = rid
@@ -50,7 +63,6 @@ class _Req:
         self.generated = 0              # tokens produced (committed)
         self.pending = None             # produced, not yet appended
         self.host = []                  # host records while swapped out
-        self.appended = False
 
 
 class RefScheduler:
@@ -75,10 +87,11 @@ class RefScheduler:
         self.waiting.append(_Req(rid, prompt, max_new_tokens))
 
     @staticmethod
-    def _choose_victim(cands):
-        """article 130: the request with the most generated tokens (the
-        first such in running order, as max() on the page's list)."""
-        return max(cands, key=lambda x: x.generated)
+    def _choose_victim(running, plan):
+        """article 130 _preempt_request: the running request with the most
+        generated tokens (the first such in running order, as max() on the
+        page's list), whatever this step's ``plan`` holds so far."""
+        return max(running, key=lambda x: x.generated)
 
     def _preempt(self, victim, plan):
         """article 130 _preempt_request: KV to host memory, blocks freed."""
@@ -97,6 +110,7 @@ class RefScheduler:
                 victim.pending = None
             self.waiting.appendleft(victim)
             plan["recomputed"].append(victim.id)
+        plan["cuts"].append([len(plan["writes"]), len(plan["cow"]), len(plan["swap_out"])])
 
     def step(self):
         """One step; returns the plan of host decisions and device copies."""
@@ -104,7 +118,7 @@ class RefScheduler:
             raise RuntimeError("commit the previous step's tokens first")
         plan = {"finished": [], "resumed": [], "admitted": [], "preempted": [],
                 "recomputed": [], "swap_in": [], "swap_out": [], "prefill": [],
-                "batch": [], "slots": [], "cow": []}
+                "writes": [], "slots": [], "cow": [], "cuts": [], "batch": []}
         # 1. finished requests leave; their blocks are freed.
         for r in list(self.running):
             if r.generated >= r.max_new:
@@ -139,10 +153,8 @@ class RefScheduler:
             self.running.append(r)
             admitted.add(r.id)
             plan["admitted"].append(r.id)
-        # 4. append each running request's pending token (preempting when
-        #    no block is left).
-        for r in self.running:
-            r.appended = False
+        # 4. append each running request's pending token, preempting the
+        #    most-generated running request whenever no block is left.
         for r in list(self.running):
             if r.id in admitted or r.pending is None or r not in self.running:
                 continue
@@ -150,20 +162,21 @@ class RefScheduler:
                 try:
                     slot, cow = self.bm.append_slot(r.id, r.pending)
                 except OutOfBlocks:
-                    victim = self._choose_victim(
-                        [x for x in self.running if not x.appended and x.id not in admitted])
+                    victim = self._choose_victim(self.running, plan)
                     self._preempt(victim, plan)
                     if victim is r:
                         break
                     continue
                 r.tokens.append(r.pending)
                 r.pending = None
-                r.appended = True
-                plan["batch"].append(r.id)
+                plan["writes"].append(r.id)
                 plan["slots"].append(slot)
                 if cow is not None:
                     plan["cow"].append(cow)
                 break
+        # The decode batch: every running request not admitted in this step
+        # (each has its last token in the cache, appended now or earlier).
+        plan["batch"] = [r.id for r in self.running if r.id not in admitted]
         self.to_commit = set(plan["batch"]) | (admitted & {r.id for r in self.running})
         return plan
 

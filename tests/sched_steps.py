@@ -46,7 +46,7 @@ def run_script(sched, spec):
                 sched.add_request(req[0], req[1], req[2])
         plan = sched.step()
         for key in ("finished", "resumed", "admitted", "preempted", "recomputed", "swap_in",
-                    "swap_out", "prefill", "batch", "slots", "cow"):
+                    "swap_out", "prefill", "writes", "slots", "cow", "cuts", "batch"):
             assert _norm(plan[key]) == exp.get(key, []), (step, key, plan[key])
         st = sched.state()
         if "host_free" in exp:
@@ -54,3 +54,26 @@ def run_script(sched, spec):
         if "waiting" in exp:
             assert st["waiting"] == exp["waiting"], (step, st["waiting"])
         commit_step(sched, step)
+
+
+def device_ops(plan):
+    """The step's device work in the order its decisions require: swap-in
+    copies, prompt writes, then per preemption the copy-on-write copies and
+    K/V writes of the appends made before it followed by its swap-out
+    copies, then the rest of the copies and writes.  Yields (kind, a, b):
+    entries [a, b) of plan["swap_in"], plan["prefill"] (requests),
+    plan["cow"], plan["writes"] or plan["swap_out"]."""
+    if plan["swap_in"]:
+        yield "swap_in", 0, len(plan["swap_in"])
+    if plan["prefill"]:
+        yield "prefill", 0, len(plan["prefill"])
+    w = c = s = 0
+    for nw, nc, ns in list(plan["cuts"]) + [(len(plan["writes"]), len(plan["cow"]), None)]:
+        if nc > c:
+            yield "cow", c, nc
+        if nw > w:
+            yield "writes", w, nw
+        w, c = nw, nc
+        if ns is not None and ns > s:
+            yield "swap_out", s, ns
+            s = ns
