@@ -597,16 +597,19 @@ def run_serve(args, torch, pkv, workloads):
     queued up front, prompts log-uniform in [50, 2048] tokens (every other
     one starting with a shared 256-token system prompt), output budgets
     log-uniform in [16, 512].  Each step is DecodeEngine.step: the
-    scheduler's decisions, then swap/prompt/COW copies, the batch's K/V
-    writes and 32 decode launches, and a stream sync.  Reported: sustained
-    generated tokens/s and decode KV GB/s over the timed steps."""
+    scheduler's decisions, then swap copies, the admitted prompts' K/V
+    writes and their attention over the uncached suffix (pa_prefill, 32
+    layers), copy-on-write copies, the batch's K/V writes and 32 decode
+    launches, and a stream sync.  Reported: sustained generated tokens/s,
+    decode KV GB/s over the timed steps, and the GPU time of the prompt
+    phase and of the decode phase (HIP events on the launch stream)."""
     from paged_kv_cache_136_amd.engine import DecodeEngine
     L, H, D, bs, NB, batch, host_slots, n_req = 32, 32, 128, 16, 16384, 128, 256, 1024
     dev = torch.device("cuda:0")
     pt = args.partition_tokens if args.partition_tokens >= 0 else 512
     shared = args.shared_prefix == "on"
     eng = DecodeEngine(L, NB, bs, H, H, D, torch.float16, batch, host_slots, True,
-                       partition_tokens=pt, shared_prefix=shared)
+                       partition_tokens=pt, shared_prefix=shared, timing=True)
     rng = np.random.Generator(np.random.PCG64(11))
     system = workloads.token_ids(256, seed=12)
     lo, hi = math.log(50), math.log(2048)
@@ -620,37 +623,43 @@ def run_serve(args, torch, pkv, workloads):
     # Rows come from preallocated random pools (their values do not matter
     # for the rate, and no RNG kernel runs inside the timed steps).
     pool = workloads.normal_torch((batch * (2048 + 256), H, D), 13, torch.float16, dev)
-    qpool = workloads.normal_torch((batch, H, D), 14, torch.float16, dev)
 
     def kv_rows(layer, kind, plan):
-        n = len(plan["prefill_slots"]) if kind == "prefill" else len(plan["batch"])
+        n = len(plan["prefill_slots"]) if kind == "prompt" else len(plan["writes"])
         return pool[:n], pool[:n]
 
-    def q_rows(layer, plan):
-        return qpool[:len(plan["batch"])]
+    def q_rows(layer, kind, n):
+        return pool[:n]
 
-    def sample(owed, outs):
+    def sample(owed, outs, prompt_outs):
         return {i: (i * 131 + eng.step_no) % 32000 for i in owed}
 
     per_tok = 2 * H * D * 2 * L
     for _ in range(args.warmup):
         eng.step(kv_rows, q_rows, sample)
     torch.cuda.synchronize()
-    tokens = kv_bytes = 0
+    tokens = kv_bytes = prompt_rows = prompt_flops = 0
     counts = {"admitted": 0, "finished": 0, "preempted": 0, "resumed": 0, "recomputed": 0}
-    host0 = eng.host_seconds
+    host0, pms0, dms0 = eng.host_seconds, eng.prompt_ms, eng.decode_ms
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        plan, outs = eng.step(kv_rows, q_rows, sample)
+        plan, outs, prompt_outs, prompt_ids = eng.step(kv_rows, q_rows, sample)
         n_batch = len(plan["batch"])
-        tokens += n_batch + len(plan["admitted"])
+        tokens += n_batch + len(prompt_ids)
         if n_batch:
             kv_bytes += sum(eng.bm.seq_len(int(i)) for i in plan["batch"]) * per_tok
+        for rid, n in zip(plan["admitted"].tolist(), plan["prefill_counts"].tolist()):
+            if rid in prompt_ids:
+                total = eng.bm.seq_len(rid)
+                prompt_rows += n
+                # causal: row i of the suffix attends to total - n + i + 1 keys
+                prompt_flops += 4 * D * H * L * (n * (total - n) + n * (n + 1) // 2)
         for k in counts:
             counts[k] += len(plan[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tok_s = tokens / wall
+    prompt_ms, decode_ms = eng.prompt_ms - pms0, eng.decode_ms - dms0
     return {
         "metric": "continuous-batching decode: sustained generated tokens/s (KV GB/s beside it)",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -662,11 +671,18 @@ def run_serve(args, torch, pkv, workloads):
                    "requests": n_req, "prompts": "log-uniform [50, 2048], half after a shared "
                    "256-token system prompt", "budgets": "log-uniform [16, 512]",
                    "timing": "wall clock over whole engine steps (host scheduling, copies, "
-                             "writes, 32 decode launches, one sync per step)",
+                             "prompt writes and attention, writes, 32 decode launches, one sync "
+                             "per step)",
                    "partition_tokens": pt, "shared_prefix_decode": shared},
         "shared_groups_per_step": round(eng.shared_groups / max(eng.step_no, 1), 2),
         "kv_gbs": round(kv_bytes / wall / 1e9, 2),
         "pct_hbm_peak": round(100 * kv_bytes / wall / 1e9 / PEAK_HBM_GBS, 2),
+        "decode_phase_ms_per_step": round(decode_ms / args.steps, 4),
+        "decode_phase_kv_gbs": round(kv_bytes / (decode_ms * 1e-3) / 1e9, 2) if decode_ms else None,
+        "prompt_phase_ms_per_step": round(prompt_ms / args.steps, 4),
+        "prompt_rows": prompt_rows,
+        "prompt_attention_tflops": (round(prompt_flops / (prompt_ms * 1e-3) / 1e12, 2)
+                                    if prompt_ms else None),
         "host_sched_ms_per_step": round((eng.host_seconds - host0) / args.steps * 1e3, 4),
         "events": counts,
         "roofline": None,

@@ -237,45 +237,63 @@ int pa_bm_dump(const pa_bm* bm, int32_t* ref, int8_t* has_hash, int32_t* free_or
 /* ==== continuous-batching scheduler (host) =============================== */
 
 /* [A130] continuous-batching section: the step timeline and the scheduler's
- * step (finish, admit first come first served, run, append; preempt the
- * request with the most generated tokens when no block is left).  It
- * drives a pa_bm (which must outlive it and is used for nothing else while
- * the scheduler runs) and only decides: the caller does each step's device
- * work from the plan, in this order -- swap-in copies (pa_swap_in), prompt
- * K/V writes, swap-out copies (pa_swap_out), copy-on-write copies
- * (pa_copy_blocks), the batch's K/V writes (pa_write_kv), decode.  Blocks a
- * preemption frees can be handed out again in the same step, so the
- * swap-out copies must precede every write of that step's appends.
- * Readings where the page stops short: the admitting step runs the prompt
- * and yields the first token; a request whose budget is met leaves at the
- * next step; preempted requests resume before new admissions, oldest
- * first; the victim is chosen among running requests that have neither
- * appended nor been admitted in this step (the failing request always is
- * one), ties to the earliest; host swap space is a FIFO pool of
- * `host_slots` block records (pa_swap_out's record layout); a victim that
- * does not fit there is recomputed: freed and put back at the front of the
- * waiting queue with every token it produced as its prompt. */
+ * step (finish, admit first come first served, run, append; when an append
+ * finds no block, _preempt_request takes the running request with the most
+ * generated tokens).  It drives a pa_bm (which must outlive it and is used
+ * for nothing else while the scheduler runs) and only decides; the caller
+ * does each step's device work from the plan.
+ * Readings where the page stops short:
+ *   - the admitting step runs the prompt and yields the first token; each
+ *     later step appends the previous token and decodes the next one; a
+ *     request whose budget is met leaves at the next step;
+ *   - preempted requests resume before new admissions, oldest first;
+ *   - appends run in running order over the list as it stood when they
+ *     began, skipping requests preempted meanwhile; when one finds no
+ *     block, the victim is the request with the most generated tokens
+ *     among ALL running requests (ties to the earliest in running order),
+ *     whether or not it appended or was admitted in this step, and the
+ *     failing request retries until it succeeds or is the victim itself;
+ *   - nothing is undone: a victim that already appended keeps its token
+ *     (its K/V is written before its blocks are copied out) and is not
+ *     decoded in this step; a request whose last token is cached but not
+ *     yet decoded joins a later step's decode batch without appending;
+ *   - host swap space is a FIFO pool of `host_slots` block records
+ *     (pa_swap_out's record layout); a victim that does not fit there is
+ *     recomputed: freed and put back at the front of the waiting queue with
+ *     every token it produced or appended as its prompt.
+ * Device order of a step: swap-in copies (pa_swap_in); prompt K/V writes
+ * (and the prompts' attention, pa_prefill); then, for each preemption k in
+ * order, the copy-on-write copies (pa_copy_blocks) and K/V writes
+ * (pa_write_kv) of the appends made before it that no earlier preemption
+ * covered, followed by its swap-out copies (pa_swap_out); then the rest of
+ * the copies and writes; then decode of the batch.  A preemption can free
+ * blocks that later appends of the same step take again, and a victim's
+ * own write must reach its blocks before they are copied out: this order
+ * satisfies both. */
 typedef struct pa_sched pa_sched;
 
 /* One step's plan, in caller-owned host arrays.  Capacities (checked
  * before the step starts, so a step never stops half done): every id
- * array, batch, slots, prefill_counts and cow_pairs (pairs) hold ids_cap >=
- * max_batch entries; swap_in / swap_out hold pairs_cap >= host_slots pairs;
- * prefill_slots holds prefill_cap >= num_blocks * block_size entries.
- * pa_sched_step fills the n_* counts. */
+ * array, writes, slots, batch, prefill_counts, cow_pairs (pairs) and cuts
+ * (triples) hold ids_cap >= max_batch entries; swap_in / swap_out hold
+ * pairs_cap >= host_slots pairs; prefill_slots holds prefill_cap >=
+ * num_blocks * block_size entries.  pa_sched_step fills the n_* counts. */
 typedef struct pa_sched_plan {
   int32_t ids_cap, pairs_cap, prefill_cap;
   int64_t* finished;    int32_t n_finished;    /* left at this step */
   int64_t* resumed;     int32_t n_resumed;     /* swapped in */
   int64_t* admitted;    int32_t n_admitted;    /* prompt runs this step */
-  int64_t* preempted;   int32_t n_preempted;   /* swapped out or recomputed */
+  int64_t* preempted;   int32_t n_preempted;   /* swapped out or recomputed, in order */
   int64_t* recomputed;  int32_t n_recomputed;  /* the preempted ones sent back to waiting */
   int32_t* swap_in;     int32_t n_swap_in;     /* [n][2] (host record, block) */
   int32_t* swap_out;    int32_t n_swap_out;    /* [n][2] (block, host record) */
   int64_t* prefill_slots; int32_t n_prefill_slots;  /* uncached prompt tokens' slots */
   int32_t* prefill_counts;                     /* [n_admitted] slots per admitted request */
-  int64_t* batch;       int64_t* slots;  int32_t n_batch;  /* appended: decode batch */
+  int64_t* writes;      int64_t* slots;  int32_t n_writes;  /* appends: K/V to write at slots */
   int32_t* cow_pairs;   int32_t n_cow;         /* [n][2] (src, dst) */
+  int32_t* cuts;        /* [n_preempted][3]: writes and cow pairs made before
+                           preemption k, swap-out pairs through it */
+  int64_t* batch;       int32_t n_batch;       /* decode batch, running order */
 } pa_sched_plan;
 
 /* NULL on bad arguments (max_batch > 0, host_slots >= 0). */
@@ -290,8 +308,8 @@ int pa_sched_add_request(pa_sched* s, int64_t id, const int32_t* prompt, int32_t
  * previous step was not committed or the plan is too small. */
 int pa_sched_step(pa_sched* s, pa_sched_plan* plan);
 /* Tokens produced by the step just planned: exactly one for each request
- * in its batch and each one it admitted (any order).  PA_ERR_INVALID
- * (nothing changed) otherwise. */
+ * in its decode batch and each one it admitted that is still running (any
+ * order).  PA_ERR_INVALID (nothing changed) otherwise. */
 int pa_sched_commit(pa_sched* s, const int64_t* ids, const int32_t* tokens, int32_t n);
 /* State queries (arrays NULL = count only; PA_ERR_INVALID if too small):
  * running requests in batch order with their generated counts; waiting
@@ -415,9 +433,11 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  *   out:  device float32 [B][num_q_heads][head_dim] (written, never read).
  *   q:    device [B][num_q_heads][head_dim] in `dtype`.
  *   k_cache, v_cache: device, one layer, layout above, in `dtype`.
- *   block_tables: device int32 [B][max_blocks_per_seq]; entries past a
- *     sequence's last block are never read; may be NULL when
- *     max_blocks_per_seq is 0.
+ *   block_tables: device int32 [B][max_blocks_per_seq], every entry
+ *     readable: the kernel may read any entry of a row ahead of need
+ *     (indices are clamped into the row), but the values past a sequence's
+ *     last block are ignored and need not be valid block ids; may be NULL
+ *     when max_blocks_per_seq is 0.
  *   context_lens: device int32 [B].
  *   max_context_len: host-side upper bound of context_lens (sizes the grid;
  *     no device-to-host read is made).

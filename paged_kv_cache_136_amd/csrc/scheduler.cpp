@@ -7,7 +7,8 @@
 // is full or blocks run short (the one that does not fit stays at the
 // front); run the batch; append each request's new token, and when no
 // block is left preempt the running request with the most generated
-// tokens, whose KV goes to host memory and whose blocks are freed.
+// tokens (_preempt_request), whose KV goes to host memory and whose blocks
+// are freed.
 //
 // Where the page stops short:
 //   * the step that admits a request runs its prompt and yields its first
@@ -15,18 +16,23 @@
 //     next; a request whose budget is met leaves at the next step;
 //   * preempted requests resume (pa_bm_swap_in) before new admissions,
 //     oldest preemption first;
-//   * the victim is chosen among running requests that have neither
-//     appended nor been admitted in this step (the failing request is
-//     always one), so no append is undone;
+//   * the appends walk the running list as it stood when they began,
+//     skipping requests preempted meanwhile; the victim is the most
+//     generated over every running request (the first such in running
+//     order), and the failing request retries until it succeeds or is the
+//     victim itself;
+//   * nothing is undone: a victim that already appended keeps its token and
+//     owes a decode, which it gets in the first step after it resumes,
+//     without appending;
 //   * host swap space is a FIFO pool of block records; a victim that does
 //     not fit is recomputed instead: freed, and put back at the front of the
 //     waiting queue with every token it has produced as its prompt.
 //
-// The scheduler only decides; the caller performs the step's device work
-// from the plan, in this order: swap-in copies, prompt K/V writes, swap-out
-// copies, copy-on-write copies, the batch's K/V writes, decode.  Blocks a
-// preemption frees may be handed out again later in the same step, so the
-// swap-out copies must precede every write of the step's appends.
+// The scheduler only decides.  The caller performs the step's device work
+// from the plan in decision order: swap-in copies, prompt K/V writes, then
+// for each preemption the copy-on-write copies and writes of the appends
+// before it followed by its swap-out copies (plan->cuts), then the rest of
+// the copies and writes, then decode.
 #include <algorithm>
 #include <deque>
 #include <memory>
@@ -49,7 +55,6 @@ struct Req {
   bool has_pending = false;     // produced, not yet appended
   int32_t pending = 0;
   std::vector<int32_t> host;    // host records while swapped out
-  bool appended = false;
 };
 
 }  // namespace
@@ -118,6 +123,10 @@ int preempt(pa_sched* s, Req* v, pa_sched_plan* p) {
     if (!push(p->recomputed, &p->n_recomputed, s->max_batch, v->id))
       return fail(PA_ERR_INVALID, "pa_sched_step: plan full");
   }
+  int32_t* cut = p->cuts + 3 * (p->n_preempted - 1);
+  cut[0] = p->n_writes;
+  cut[1] = p->n_cow;
+  cut[2] = p->n_swap_out;
   return PA_OK;
 }
 
@@ -182,9 +191,8 @@ int step_locked(pa_sched* s, pa_sched_plan* p) {
     s->running.push_back(r);
     admitted.insert(r->id);
   }
-  // 4. append each running request's pending token, preempting when no
-  //    block is left.
-  for (Req* r : s->running) r->appended = false;
+  // 4. append each running request's pending token, preempting the most
+  //    generated running request whenever no block is left.
   const std::vector<Req*> order = s->running;
   for (Req* r : order) {
     if (admitted.count(r->id) || !r->has_pending) continue;
@@ -196,8 +204,7 @@ int step_locked(pa_sched* s, pa_sched_plan* p) {
       if (st == PA_ERR_OUT_OF_BLOCKS) {
         Req* victim = nullptr;   // most generated; the first such in running order
         for (Req* x : s->running)
-          if (!x->appended && !admitted.count(x->id) && (!victim || x->generated > victim->generated))
-            victim = x;
+          if (!victim || x->generated > victim->generated) victim = x;
         st = preempt(s, victim, p);
         if (st != PA_OK) return st;
         if (victim == r) break;
@@ -206,10 +213,9 @@ int step_locked(pa_sched* s, pa_sched_plan* p) {
       if (st != PA_OK) return st;
       r->tokens.push_back(r->pending);
       r->has_pending = false;
-      r->appended = true;
-      p->batch[p->n_batch] = r->id;
-      p->slots[p->n_batch] = slot;
-      ++p->n_batch;
+      p->writes[p->n_writes] = r->id;
+      p->slots[p->n_writes] = slot;
+      ++p->n_writes;
       if (src >= 0) {
         p->cow_pairs[2 * p->n_cow] = src;
         p->cow_pairs[2 * p->n_cow + 1] = dst;
@@ -218,9 +224,13 @@ int step_locked(pa_sched* s, pa_sched_plan* p) {
       break;
     }
   }
+  // The decode batch: every running request not admitted in this step; each
+  // has its last token in the cache (appended now, or before a preemption).
   s->to_commit.clear();
-  for (int32_t i = 0; i < p->n_batch; ++i) s->to_commit.insert(p->batch[i]);
-  for (int32_t i = 0; i < p->n_admitted; ++i) s->to_commit.insert(p->admitted[i]);
+  for (Req* r : s->running) {
+    s->to_commit.insert(r->id);
+    if (!admitted.count(r->id)) p->batch[p->n_batch++] = r->id;
+  }
   return PA_OK;
 }
 
@@ -271,7 +281,7 @@ int pa_sched_step(pa_sched* s, pa_sched_plan* p) {
   std::lock_guard<std::mutex> lock(s->mu);
   if (!s->to_commit.empty()) return fail(PA_ERR_INVALID, "pa_sched_step: commit the previous step first");
   if (!p->finished || !p->resumed || !p->admitted || !p->preempted || !p->recomputed ||
-      !p->prefill_counts || !p->batch || !p->slots || !p->cow_pairs ||
+      !p->prefill_counts || !p->writes || !p->slots || !p->cow_pairs || !p->cuts || !p->batch ||
       (s->host_total > 0 && (!p->swap_in || !p->swap_out)) || (p->prefill_cap > 0 && !p->prefill_slots) ||
       p->prefill_cap < 0)
     return fail(PA_ERR_INVALID, "pa_sched_step: plan arrays missing");
@@ -283,7 +293,7 @@ int pa_sched_step(pa_sched* s, pa_sched_plan* p) {
     return fail(PA_ERR_INVALID, "pa_sched_step: plan arrays need max_batch ids, host_slots pairs "
                                 "and num_blocks * block_size prefill slots");
   p->n_finished = p->n_resumed = p->n_admitted = p->n_preempted = p->n_recomputed = 0;
-  p->n_swap_in = p->n_swap_out = p->n_prefill_slots = p->n_batch = p->n_cow = 0;
+  p->n_swap_in = p->n_swap_out = p->n_prefill_slots = p->n_writes = p->n_cow = p->n_batch = 0;
   int st = step_locked(s, p);
   if (st == PA_OK) pkv::clear_error();
   return st;

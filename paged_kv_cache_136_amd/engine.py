@@ -1,14 +1,21 @@
 """Continuous-batching decode loop on one GPU (orchestration only).
 
 Each step asks the library's scheduler for a plan and performs its device
-work through the library's calls, in the order the plan requires:
+work through the library's calls, in the order the plan's decisions
+require:
 
   1. swap-in copies (pa_swap_in) of resumed requests;
-  2. prompt K/V writes (pa_write_kv) of admitted requests' uncached tokens;
-  3. swap-out copies (pa_swap_out) of preempted requests;
-  4. copy-on-write copies (pa_copy_blocks);
-  5. the batch's K/V writes (pa_write_kv) at the appended slots;
-  6. decode (pa_decode) of the batch, every layer; with ``shared_prefix``
+  2. prompt K/V writes (pa_write_kv) of admitted requests' uncached tokens,
+     then, for the admitted requests still running, the prompt's attention
+     over the uncached suffix (pa_prefill): after prefix hits only that
+     suffix needs a forward pass ("P06 · BlockManager" spec overview and
+     key-question answers);
+  3. for each preemption, in order: the copy-on-write copies
+     (pa_copy_blocks) and K/V writes (pa_write_kv) of the appends made
+     before it, then its swap-out copies (pa_swap_out) -- a victim's own
+     write lands before its blocks are copied out, and blocks it frees are
+     written again only afterwards; then the remaining copies and writes;
+  4. decode (pa_decode) of the batch, every layer; with ``shared_prefix``
      the host plans shared-prefix groups once per step (pa_shared_plan) and
      every layer decodes with pa_decode_shared, reading blocks that several
      sequences share (a common system prompt, forks) once per group.
@@ -26,7 +33,8 @@ import torch
 
 from .block_manager import BlockManager
 from .ops import (pa_copy_blocks, pa_decode, pa_decode_shared, pa_decode_workspace_bytes,
-                  pa_shared_plan, pa_swap_in, pa_swap_out, pa_write_kv, swap_record_bytes)
+                  pa_prefill, pa_shared_plan, pa_swap_in, pa_swap_out, pa_write_kv,
+                  swap_record_bytes)
 from .scheduler import Scheduler
 
 
@@ -37,14 +45,18 @@ class DecodeEngine:
 
     def __init__(self, num_layers, num_blocks, block_size, num_kv_heads, num_q_heads, head_dim,
                  dtype, max_batch, host_slots, enable_prefix_cache=True, partition_tokens=512,
-                 device="cuda", caches=None, shared_prefix=False):
+                 device="cuda", caches=None, shared_prefix=False, prompt_attention=True,
+                 timing=False):
         self.L, self.nb, self.bs = num_layers, num_blocks, block_size
         self.hkv, self.hq, self.d, self.dtype = num_kv_heads, num_q_heads, head_dim, dtype
         self.dev = torch.device(device)
         self.partition_tokens = partition_tokens
         if shared_prefix and (dtype == torch.float32 or partition_tokens <= 0):
             raise ValueError("shared_prefix needs 16-bit caches and partition_tokens > 0")
+        if prompt_attention and dtype == torch.float32:
+            raise ValueError("prompt attention (pa_prefill) needs 16-bit caches")
         self.shared_prefix = shared_prefix
+        self.prompt_attention = prompt_attention
         self.shared_groups = 0           # groups planned, summed over steps
         self.bm = BlockManager(num_blocks, block_size, enable_prefix_cache)
         self.sched = Scheduler(self.bm, max_batch, host_slots)
@@ -59,6 +71,11 @@ class DecodeEngine:
         self.ws = None                   # decode workspace, grown on demand
         self.step_no = 0
         self.host_seconds = 0.0          # time in scheduler / block-manager calls
+        # With ``timing``, HIP events on the launch stream bracket the prompt
+        # phase (writes and attention) and the decode phase of every step.
+        self.timing = timing
+        self.prompt_ms = 0.0
+        self.decode_ms = 0.0
 
     def add_request(self, rid, prompt, max_new_tokens):
         self.sched.add_request(rid, prompt, max_new_tokens)
@@ -66,16 +83,29 @@ class DecodeEngine:
     def _i32(self, a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev)
 
+    def _event(self):
+        if not self.timing:
+            return None
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
     def step(self, kv_rows, q_rows, sample):
         """One step.  ``kv_rows(layer, kind, plan)`` returns device K and V
-        rows [n, Hkv, D]: for kind "prefill" one per entry of
-        plan["prefill_slots"] (the admitted requests' uncached prompt
-        tokens, request after request, plan["prefill_counts"] each), for
-        "decode" one per entry of plan["batch"].  ``q_rows(layer, plan)``
-        returns the batch's queries [B, Hq, D].  ``sample(owed, outs)``
-        returns {id: token} for ``owed`` (the batch, then the admitted
-        requests) given the per-layer float32 decode outputs [B, Hq, D].
-        Returns (plan, outs)."""
+        rows [n, Hkv, D]: for kind "prompt" one per entry of
+        plan["prefill_slots"] (the admitted requests' uncached prompt tokens,
+        request after request, plan["prefill_counts"] each), for "append"
+        one per entry of plan["writes"] (the tokens appended in this step).
+        ``q_rows(layer, kind, n)`` returns n queries [n, Hq, D]: for
+        "prompt" one per prompt row of the requests in ``prompt_ids`` (the
+        admitted requests still running, in admission order; their rows are
+        their entries of plan["prefill_slots"]), for "decode" one per entry
+        of plan["batch"].  ``sample(owed, outs, prompt_outs)``
+        returns {id: token} for ``owed`` (the decode batch, then
+        ``prompt_ids``) given the per-layer float32 decode outputs [B, Hq, D]
+        and prompt-attention outputs [rows, Hq, D] (the last row of each
+        request yields its first token).
+        Returns (plan, outs, prompt_outs, prompt_ids)."""
         self.step_no += 1
         h0 = time.perf_counter()
         plan = self.sched.step_arrays()
@@ -84,61 +114,109 @@ class DecodeEngine:
         if len(plan["swap_in"]):
             pa_swap_in(self.k, self.v, self._i32(plan["swap_in"][:, 1]), self.host,
                        host_slots=self._i32(plan["swap_in"][:, 0]))
-        # 2. prompt K/V of admitted requests
-        if len(plan["prefill_slots"]):
-            slots = torch.from_numpy(plan["prefill_slots"].copy()).to(self.dev)
-            for layer in range(self.L):
-                k, v = kv_rows(layer, "prefill", plan)
-                pa_write_kv(self.k[layer], self.v[layer], k, v, slots)
-        # 3. swap-out copies
-        if len(plan["swap_out"]):
-            pa_swap_out(self.k, self.v, self._i32(plan["swap_out"][:, 0]), self.host,
-                        host_slots=self._i32(plan["swap_out"][:, 1]))
-        # 4. copy-on-write
-        if len(plan["cow"]):
-            pa_copy_blocks(self.k, self.v, self._i32(plan["cow"]))
-        # 5-6. the batch: new tokens' K/V, then decode every layer
-        ids = plan["batch"].copy()
-        outs = []
-        if len(ids):
-            B = len(ids)
-            slots = torch.from_numpy(plan["slots"].copy()).to(self.dev)
-            h0 = time.perf_counter()
-            tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
-            splan = None
-            if self.shared_prefix:
-                sg, groups, mx, mp = pa_shared_plan(tables, lens, self.bs, self.partition_tokens,
-                                                    self.hq // self.hkv)
-                self.shared_groups += len(groups)
-                if len(groups):
-                    splan = (torch.from_numpy(sg).to(self.dev),
-                             torch.from_numpy(groups).to(self.dev), mx, mp)
-            self.host_seconds += time.perf_counter() - h0
-            max_len = int(lens.max())
-            d_tab = torch.from_numpy(tables).to(self.dev)
-            d_len = torch.from_numpy(lens).to(self.dev)
-            need = pa_decode_workspace_bytes(B, self.hq, self.d, max_len, self.partition_tokens)
-            if need and (self.ws is None or self.ws.numel() < need):
-                self.ws = torch.empty(2 * need, dtype=torch.uint8, device=self.dev)
-            for layer in range(self.L):
-                k, v = kv_rows(layer, "decode", plan)
-                pa_write_kv(self.k[layer], self.v[layer], k, v, slots)
-                if splan is None:
-                    outs.append(pa_decode(q_rows(layer, plan), self.k[layer], self.v[layer], d_tab,
-                                          d_len, max_len, partition_tokens=self.partition_tokens,
-                                          workspace=self.ws))
-                else:
-                    outs.append(pa_decode_shared(q_rows(layer, plan), self.k[layer], self.v[layer],
-                                                 d_tab, d_len, max_len, *splan,
-                                                 partition_tokens=self.partition_tokens,
-                                                 workspace=self.ws))
+        # 2. prompt K/V of admitted requests, then their prompt attention
+        e_p0 = self._event()
+        prompt_outs, prompt_ids = self._prompts(plan, kv_rows, q_rows)
+        e_p1 = self._event()
+        # 3. copy-on-write copies, the appended tokens' K/V and swap-outs,
+        #    epoch by epoch
+        writes = plan["writes"]
+        rows = [kv_rows(layer, "append", plan) for layer in range(self.L)] if len(writes) else None
+        slots = torch.from_numpy(plan["slots"].copy()).to(self.dev) if len(writes) else None
+        w = c = so = 0
+        for nw, nc, ns in plan["cuts"].tolist():
+            self._cow_and_writes(plan, rows, slots, c, nc, w, nw)
+            if ns > so:
+                sw = plan["swap_out"][so:ns]
+                pa_swap_out(self.k, self.v, self._i32(sw[:, 0]), self.host,
+                            host_slots=self._i32(sw[:, 1]))
+            w, c, so = nw, nc, ns
+        self._cow_and_writes(plan, rows, slots, c, len(plan["cow"]), w, len(writes))
+        # 4. decode every layer
+        e_d0 = self._event()
+        outs = self._decode(plan, q_rows)
+        e_d1 = self._event()
         torch.cuda.current_stream().synchronize()
-        owed = ids.tolist() + plan["admitted"].tolist()
-        toks = sample(owed, outs)
+        if self.timing:
+            self.prompt_ms += e_p0.elapsed_time(e_p1)
+            self.decode_ms += e_d0.elapsed_time(e_d1)
+        owed = plan["batch"].tolist() + prompt_ids
+        toks = sample(owed, outs, prompt_outs)
         h0 = time.perf_counter()
         self.sched.commit(toks)
         self.host_seconds += time.perf_counter() - h0
-        return plan, outs
+        return plan, outs, prompt_outs, prompt_ids
+
+    def _prompts(self, plan, kv_rows, q_rows):
+        if not len(plan["prefill_slots"]):
+            return [], []
+        slots = torch.from_numpy(plan["prefill_slots"].copy()).to(self.dev)
+        for layer in range(self.L):
+            k, v = kv_rows(layer, "prompt", plan)
+            pa_write_kv(self.k[layer], self.v[layer], k, v, slots)
+        preempted = set(plan["preempted"].tolist())
+        ids, counts = [], []
+        for rid, n in zip(plan["admitted"].tolist(), plan["prefill_counts"].tolist()):
+            if rid not in preempted:
+                ids.append(rid)
+                counts.append(n)
+        if not ids or not self.prompt_attention:
+            return [], ids
+        h0 = time.perf_counter()
+        tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
+        self.host_seconds += time.perf_counter() - h0
+        qstart = np.zeros(len(ids) + 1, dtype=np.int32)
+        qstart[1:] = np.cumsum(counts)
+        d_tab = torch.from_numpy(tables).to(self.dev)
+        d_len = torch.from_numpy(lens).to(self.dev)
+        d_qs = torch.from_numpy(qstart).to(self.dev)
+        outs = []
+        for layer in range(self.L):
+            outs.append(pa_prefill(q_rows(layer, "prompt", int(qstart[-1])), self.k[layer],
+                                   self.v[layer], d_tab, d_qs, d_len, max(counts)))
+        return outs, ids
+
+    def _cow_and_writes(self, plan, rows, slots, c0, c1, w0, w1):
+        if c1 > c0:
+            pa_copy_blocks(self.k, self.v, self._i32(plan["cow"][c0:c1]))
+        if w1 > w0:
+            for layer in range(self.L):
+                k, v = rows[layer]
+                pa_write_kv(self.k[layer], self.v[layer], k[w0:w1], v[w0:w1], slots[w0:w1])
+
+    def _decode(self, plan, q_rows):
+        ids = plan["batch"]
+        outs = []
+        if not len(ids):
+            return outs
+        B = len(ids)
+        h0 = time.perf_counter()
+        tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
+        splan = None
+        if self.shared_prefix:
+            sg, groups, mx, mp = pa_shared_plan(tables, lens, self.bs, self.partition_tokens,
+                                                self.hq // self.hkv)
+            self.shared_groups += len(groups)
+            if len(groups):
+                splan = (torch.from_numpy(sg).to(self.dev),
+                         torch.from_numpy(groups).to(self.dev), mx, mp)
+        self.host_seconds += time.perf_counter() - h0
+        max_len = int(lens.max())
+        d_tab = torch.from_numpy(tables).to(self.dev)
+        d_len = torch.from_numpy(lens).to(self.dev)
+        need = pa_decode_workspace_bytes(B, self.hq, self.d, max_len, self.partition_tokens)
+        if need and (self.ws is None or self.ws.numel() < need):
+            self.ws = torch.empty(2 * need, dtype=torch.uint8, device=self.dev)
+        for layer in range(self.L):
+            q = q_rows(layer, "decode", B)
+            if splan is None:
+                outs.append(pa_decode(q, self.k[layer], self.v[layer], d_tab, d_len, max_len,
+                                      partition_tokens=self.partition_tokens, workspace=self.ws))
+            else:
+                outs.append(pa_decode_shared(q, self.k[layer], self.v[layer], d_tab, d_len, max_len,
+                                             *splan, partition_tokens=self.partition_tokens,
+                                             workspace=self.ws))
+        return outs
 
     def _table_width(self, ids):
         return max(-(-self.bm.seq_len(int(i)) // self.bs) for i in ids)

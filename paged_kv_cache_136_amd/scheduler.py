@@ -12,8 +12,8 @@ from ._lib import P_i32, P_i64, check, lib
 
 
 def plan_lists(a):
-    """A plan from step_arrays() as plain lists (pairs as tuples, prompt
-    slots grouped per admitted request)."""
+    """A plan from step_arrays() as plain lists (pairs and cuts as lists of
+    lists, prompt slots grouped per admitted request)."""
     prefill, o = [], 0
     for rid, n in zip(a["admitted"].tolist(), a["prefill_counts"].tolist()):
         prefill.append((rid, a["prefill_slots"][o:o + n].tolist()))
@@ -24,8 +24,9 @@ def plan_lists(a):
         "recomputed": a["recomputed"].tolist(),
         "swap_in": [tuple(x) for x in a["swap_in"].tolist()],
         "swap_out": [tuple(x) for x in a["swap_out"].tolist()], "prefill": prefill,
-        "batch": a["batch"].tolist(), "slots": a["slots"].tolist(),
-        "cow": [tuple(x) for x in a["cow"].tolist()],
+        "writes": a["writes"].tolist(), "slots": a["slots"].tolist(),
+        "cow": [tuple(x) for x in a["cow"].tolist()], "cuts": a["cuts"].tolist(),
+        "batch": a["batch"].tolist(),
     }
 
 
@@ -42,8 +43,10 @@ class Plan(ctypes.Structure):
         ("swap_out", P_i32), ("n_swap_out", ctypes.c_int32),
         ("prefill_slots", P_i64), ("n_prefill_slots", ctypes.c_int32),
         ("prefill_counts", P_i32),
-        ("batch", P_i64), ("slots", P_i64), ("n_batch", ctypes.c_int32),
+        ("writes", P_i64), ("slots", P_i64), ("n_writes", ctypes.c_int32),
         ("cow_pairs", P_i32), ("n_cow", ctypes.c_int32),
+        ("cuts", P_i32),
+        ("batch", P_i64), ("n_batch", ctypes.c_int32),
     ]
 
 
@@ -68,8 +71,9 @@ class Scheduler:
             "admitted": np.empty(ids, np.int64), "preempted": np.empty(ids, np.int64),
             "recomputed": np.empty(ids, np.int64), "swap_in": np.empty((pairs, 2), np.int32),
             "swap_out": np.empty((pairs, 2), np.int32), "prefill_slots": np.empty(nb * bs, np.int64),
-            "prefill_counts": np.empty(ids, np.int32), "batch": np.empty(ids, np.int64),
+            "prefill_counts": np.empty(ids, np.int32), "writes": np.empty(ids, np.int64),
             "slots": np.empty(ids, np.int64), "cow_pairs": np.empty((ids, 2), np.int32),
+            "cuts": np.empty((ids, 3), np.int32), "batch": np.empty(ids, np.int64),
         }
         p = Plan()
         p.ids_cap, p.pairs_cap, p.prefill_cap = ids, pairs, nb * bs
@@ -101,10 +105,12 @@ class Scheduler:
             "swap_out": a["swap_out"][:p.n_swap_out],
             "prefill_slots": a["prefill_slots"][:p.n_prefill_slots],
             "prefill_counts": a["prefill_counts"][:p.n_admitted],
-            "batch": a["batch"][:p.n_batch], "slots": a["slots"][:p.n_batch],
-            "cow": a["cow_pairs"][:p.n_cow],
+            "writes": a["writes"][:p.n_writes], "slots": a["slots"][:p.n_writes],
+            "cow": a["cow_pairs"][:p.n_cow], "cuts": a["cuts"][:p.n_preempted],
+            "batch": a["batch"][:p.n_batch],
         }
-        self.to_commit = set(out["batch"].tolist()) | set(out["admitted"].tolist())
+        self.to_commit = (set(out["batch"].tolist())
+                          | (set(out["admitted"].tolist()) - set(out["preempted"].tolist())))
         return out
 
     def step(self):
@@ -113,8 +119,8 @@ class Scheduler:
         return plan_lists(self.step_arrays())
 
     def commit(self, tokens):
-        """{request id: token} for every request of the last step's batch
-        and admissions."""
+        """{request id: token} for every request of the last step's decode
+        batch and every admission still running."""
         ids = np.fromiter(tokens.keys(), dtype=np.int64, count=len(tokens))
         toks = np.fromiter(tokens.values(), dtype=np.int32, count=len(tokens))
         check(lib().pa_sched_commit(self._h, ids.ctypes.data_as(P_i64), toks.ctypes.data_as(P_i32),

@@ -238,14 +238,15 @@ static void run_sched(uint32_t seed, int nb, int bs, int batch, int host, int pr
   REQUIRE(s);
   const int cap_ids = batch, cap_pairs = std::max(host, 1), cap_pre = nb * bs;
   std::vector<int64_t> fin(cap_ids), res(cap_ids), adm(cap_ids), pre(cap_ids), rec(cap_ids),
-      pslots(cap_pre), batch_ids(cap_ids), slots(cap_ids);
-  std::vector<int32_t> swin(2 * cap_pairs), swout(2 * cap_pairs), pcnt(cap_ids), cow(2 * cap_ids);
+      pslots(cap_pre), batch_ids(cap_ids), writes(cap_ids), slots(cap_ids);
+  std::vector<int32_t> swin(2 * cap_pairs), swout(2 * cap_pairs), pcnt(cap_ids), cow(2 * cap_ids),
+      cuts(3 * cap_ids);
   pa_sched_plan p{};
   p.ids_cap = cap_ids; p.pairs_cap = cap_pairs; p.prefill_cap = cap_pre;
   p.finished = fin.data(); p.resumed = res.data(); p.admitted = adm.data(); p.preempted = pre.data();
   p.recomputed = rec.data(); p.swap_in = swin.data(); p.swap_out = swout.data();
-  p.prefill_slots = pslots.data(); p.prefill_counts = pcnt.data(); p.batch = batch_ids.data();
-  p.slots = slots.data(); p.cow_pairs = cow.data();
+  p.prefill_slots = pslots.data(); p.prefill_counts = pcnt.data(); p.writes = writes.data();
+  p.slots = slots.data(); p.cow_pairs = cow.data(); p.cuts = cuts.data(); p.batch = batch_ids.data();
   pa_sched_plan small = p;
   small.prefill_cap = cap_pre - 1;
   REQUIRE(pa_sched_step(s, &small) == PA_ERR_INVALID);          // refused before any change
@@ -262,16 +263,24 @@ static void run_sched(uint32_t seed, int nb, int bs, int batch, int host, int pr
       ++next;
     }
     REQUIRE(pa_sched_step(s, &p) == PA_OK);
-    if (p.n_batch + p.n_admitted > 0) {                           // tokens owed: commit first
-      pa_sched_plan again = p;
-      REQUIRE(pa_sched_step(s, &again) == PA_ERR_INVALID);
-    }
     for (int i = 0; i < p.n_finished; ++i) REQUIRE(produced[fin[i]] == budget[fin[i]]);
     preempted += p.n_preempted;
     resumed += p.n_resumed;
-    REQUIRE(p.n_batch <= batch && p.n_swap_in <= host && p.n_swap_out <= host);
+    REQUIRE(p.n_batch <= batch && p.n_writes <= batch && p.n_swap_in <= host && p.n_swap_out <= host);
+    int32_t pw = 0, pc = 0, ps = 0;                               // cuts never go backwards
+    for (int i = 0; i < p.n_preempted; ++i) {
+      REQUIRE(cuts[3 * i] >= pw && cuts[3 * i + 1] >= pc && cuts[3 * i + 2] >= ps);
+      pw = cuts[3 * i]; pc = cuts[3 * i + 1]; ps = cuts[3 * i + 2];
+    }
+    REQUIRE(pw <= p.n_writes && pc <= p.n_cow && ps == p.n_swap_out);
     std::vector<int64_t> ids(batch_ids.begin(), batch_ids.begin() + p.n_batch);
-    ids.insert(ids.end(), adm.begin(), adm.begin() + p.n_admitted);
+    for (int i = 0; i < p.n_admitted; ++i)                        // admitted and still running
+      if (std::find(pre.begin(), pre.begin() + p.n_preempted, adm[i]) == pre.begin() + p.n_preempted)
+        ids.push_back(adm[i]);
+    if (!ids.empty()) {                                           // tokens owed: commit first
+      pa_sched_plan again = p;
+      REQUIRE(pa_sched_step(s, &again) == PA_ERR_INVALID);
+    }
     std::vector<int32_t> toks(ids.size());
     for (auto& t : toks) t = rng() % 4;
     for (int64_t id : ids) ++produced[id];

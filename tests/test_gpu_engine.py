@@ -1,13 +1,17 @@
 """GPU parity of the continuous-batching loop ("qaqbuyan.com article 130",
 continuous-batching section): the library's scheduler driving the device
 calls, against the oracle scheduler driving the oracle's copies and
-float64 decode, step by step.
+float64 attention, step by step.
 
 Every step's plan must be identical, every cache byte bit-exact after the
-step, and every layer's decode output within the attention tolerance.
-Requests share prompt prefixes (prefix hits), the pool is small enough to
-force preemption, and the host swap pool is either roomy (swap-out/in) or
-absent (recompute).
+step, every layer's decode output and every admitted prompt's attention
+output (pa_prefill over the uncached suffix, "P06 · BlockManager" spec
+overview) within the attention tolerance.  The oracle side applies the
+step's device work in the plan's decision order (epochs split at each
+preemption).  Requests share prompt prefixes (prefix hits), the pool is
+small enough to force preemption -- including victims that already
+appended in their step -- and the host swap pool is either roomy
+(swap-out/in) or absent (recompute).
 """
 
 import numpy as np
@@ -17,6 +21,7 @@ import torch
 import oracle
 import workloads
 from tests.gpu_util import TOL, make_cache, say
+from tests.sched_steps import device_ops
 
 pytestmark = pytest.mark.gpu
 
@@ -65,55 +70,77 @@ def test_serve_loop_matches_oracle(host, shared):
     rows = {}
 
     def kv_rows(layer, kind, plan):
-        n = len(plan["prefill_slots"]) if kind == "prefill" else len(plan["batch"])
-        seed = 100_000 * eng.step_no + 10 * layer + (0 if kind == "prefill" else 5)
+        n = len(plan["prefill_slots"]) if kind == "prompt" else len(plan["writes"])
+        seed = 100_000 * eng.step_no + 10 * layer + (0 if kind == "prompt" else 5)
         k = workloads.normal_torch((n, hkv, d), seed, torch.float16, "cuda")
         v = workloads.normal_torch((n, hkv, d), seed + 1, torch.float16, "cuda")
         rows[(layer, kind)] = (k, v)
         return k, v
 
-    def q_rows(layer, plan):
-        q = workloads.normal_torch((len(plan["batch"]), hq, d), 100_000 * eng.step_no + 10 * layer + 7,
-                                   torch.float16, "cuda")
-        rows[(layer, "q")] = q
+    def q_rows(layer, kind, n):
+        q = workloads.normal_torch((n, hq, d), 100_000 * eng.step_no + 10 * layer + 7
+                                   + (0 if kind == "decode" else 1), torch.float16, "cuda")
+        rows[(layer, "q", kind)] = q
         return q
 
-    def sample(owed, outs):
+    def sample(owed, outs, prompt_outs):
         return {i: (i * 131 + eng.step_no) % 50 for i in owed}
 
-    seen = {"preempted": 0, "recomputed": 0, "resumed": 0, "hits": 0}
+    seen = {"preempted": 0, "recomputed": 0, "resumed": 0, "hits": 0, "appended_victim": 0,
+            "decode_only": 0, "prompt_rows": 0}
     for step in range(1, 600):
         rows.clear()
-        plan_arrays, outs = eng.step(kv_rows, q_rows, sample)
+        plan_arrays, outs, prompt_outs, prompt_ids = eng.step(kv_rows, q_rows, sample)
         got = plan_lists(plan_arrays)
         want = rsc.step()
         assert got == want, step
         for key in ("preempted", "recomputed", "resumed"):
             seen[key] += len(want[key])
-        seen["hits"] += sum(rbm.num_cached_tokens(r) > 0 for r in want["admitted"])
-        # The oracle applies the same device work, in the same order.
-        if want["swap_in"]:
-            recs, blocks = zip(*want["swap_in"])
-            oracle.ref_swap_in(kb, vb, blocks, hrec[list(recs)], inplace=True)
-        if want["prefill"]:
-            slots = [s for _, ss in want["prefill"] for s in ss]
-            for layer in range(L):
-                k, v = rows[(layer, "prefill")]
-                oracle.ref_write_kv(kb[layer], vb[layer], _bits(k), _bits(v), slots, inplace=True)
-        if want["swap_out"]:
-            blocks, recs = zip(*want["swap_out"])
-            hrec[list(recs)] = oracle.ref_swap_out(kb, vb, blocks)
-        if want["cow"]:
-            oracle.ref_copy_blocks(kb, vb, want["cow"], inplace=True)
+        seen["appended_victim"] += len(set(want["preempted"]) & set(want["writes"]))
+        seen["decode_only"] += len(set(want["batch"]) - set(want["writes"]))
+        seen["hits"] += sum(rbm.num_cached_tokens(r) > 0 for r in want["admitted"]
+                            if r not in want["preempted"])
+        assert prompt_ids == [r for r in want["admitted"] if r not in want["preempted"]]
+        # The oracle applies the same device work, in the plan's order.
+        for kind, a, b in device_ops(want):
+            if kind == "swap_in":
+                recs, blocks = zip(*want["swap_in"][a:b])
+                oracle.ref_swap_in(kb, vb, blocks, hrec[list(recs)], inplace=True)
+            elif kind == "prefill":
+                slots = [s for _, ss in want["prefill"] for s in ss]
+                for layer in range(L):
+                    k, v = rows[(layer, "prompt")]
+                    oracle.ref_write_kv(kb[layer], vb[layer], _bits(k), _bits(v), slots, inplace=True)
+                if prompt_ids:
+                    counts = [len(ss) for r, ss in want["prefill"] if r in prompt_ids]
+                    tables = [rbm.get_table(r) for r in prompt_ids]
+                    width = max(len(t) for t in tables)
+                    tab = np.array([t + [0] * (width - len(t)) for t in tables], dtype=np.int32)
+                    lens = [rbm.seq_len(r) for r in prompt_ids]
+                    seen["prompt_rows"] += sum(counts)
+                    for layer in range(L):
+                        ref = oracle.ref_prefill(_bits(rows[(layer, "q", "prompt")]).view(np.float16),
+                                                 kb[layer].view(np.float16), vb[layer].view(np.float16),
+                                                 tab, counts, lens)
+                        err = np.abs(prompt_outs[layer].cpu().numpy() - ref).max()
+                        assert err <= TOL["f16"], (step, layer, "prompt", err)
+            elif kind == "cow":
+                oracle.ref_copy_blocks(kb, vb, want["cow"][a:b], inplace=True)
+            elif kind == "writes":
+                for layer in range(L):
+                    k, v = rows[(layer, "append")]
+                    oracle.ref_write_kv(kb[layer], vb[layer], _bits(k)[a:b], _bits(v)[a:b],
+                                        want["slots"][a:b], inplace=True)
+            else:
+                blocks, recs = zip(*want["swap_out"][a:b])
+                hrec[list(recs)] = oracle.ref_swap_out(kb, vb, blocks)
         if want["batch"]:
             tables, lens = eng.bm.export_batch(want["batch"], max(-(-rbm.seq_len(i) // bs) for i in want["batch"]), 0)
             assert lens.tolist() == [rbm.seq_len(i) for i in want["batch"]]
             assert all(rbm.get_table(i) == tables[j, :len(rbm.get_table(i))].tolist()
                        for j, i in enumerate(want["batch"]))
             for layer in range(L):
-                k, v = rows[(layer, "decode")]
-                oracle.ref_write_kv(kb[layer], vb[layer], _bits(k), _bits(v), want["slots"], inplace=True)
-                ref = oracle.ref_decode(_bits(rows[(layer, "q")]).view(np.float16),
+                ref = oracle.ref_decode(_bits(rows[(layer, "q", "decode")]).view(np.float16),
                                         kb[layer].view(np.float16), vb[layer].view(np.float16),
                                         tables, lens)
                 err = np.abs(outs[layer].cpu().numpy() - ref).max()
@@ -121,15 +148,17 @@ def test_serve_loop_matches_oracle(host, shared):
         for layer in range(L):
             assert np.array_equal(_bits(eng.k[layer]), kb[layer]), (step, layer)
             assert np.array_equal(_bits(eng.v[layer]), vb[layer]), (step, layer)
-        rsc.commit(sample(want["batch"] + want["admitted"], None))
+        rsc.commit(sample(want["batch"] + prompt_ids, None, None))
         if eng.idle():
             break
     else:
         raise AssertionError("the loop did not drain")
-    assert seen["preempted"] > 0 and seen["hits"] > 0
+    say("serve loop seen", seen)
+    assert seen["preempted"] > 0 and seen["hits"] > 0 and seen["appended_victim"] > 0
+    assert seen["prompt_rows"] > 0
     assert (eng.shared_groups > 0) == shared
     if host:
-        assert seen["resumed"] > 0
+        assert seen["resumed"] > 0 and seen["decode_only"] > 0
     else:
         assert seen["recomputed"] > 0
     assert eng.bm.num_free_blocks == nb

@@ -45,7 +45,8 @@ def test_random_stream_parity(seed, nb, bs, batch, host, prefix):
             "enable_prefix_cache": prefix}
     a, b = make(spec, True), make(spec, False)
     shared = [rng.randrange(50) for _ in range(3 * bs)]
-    nxt, seen = 1, {"preempted": 0, "recomputed": 0, "resumed": 0, "cow": 0}
+    nxt, seen = 1, {"preempted": 0, "recomputed": 0, "resumed": 0, "cow": 0, "appended_victim": 0,
+                    "decode_only": 0}
     for step in range(1, 3000):
         while nxt <= 60 and rng.random() < 0.3:
             prompt = shared[:rng.randrange(0, 3 * bs)] + [rng.randrange(50) for _ in range(rng.randrange(1, 3 * bs))]
@@ -59,6 +60,8 @@ def test_random_stream_parity(seed, nb, bs, batch, host, prefix):
         assert a.bm.dump() == b.bm.dump(), step
         for k in ("preempted", "recomputed", "resumed", "cow"):
             seen[k] += len(pa[k])
+        seen["appended_victim"] += len(set(pa["preempted"]) & set(pa["writes"]))
+        seen["decode_only"] += len(set(pa["batch"]) - set(pa["writes"]))
         assert a.to_commit == b.to_commit
         toks = {i: rng.randrange(50) for i in b.to_commit}
         a.commit(toks)
@@ -68,9 +71,9 @@ def test_random_stream_parity(seed, nb, bs, batch, host, prefix):
             break
     else:
         raise AssertionError("did not drain")
-    assert seen["preempted"] > 0
+    assert seen["preempted"] > 0 and seen["appended_victim"] > 0
     if host:
-        assert seen["resumed"] > 0
+        assert seen["resumed"] > 0 and seen["decode_only"] > 0
     a.bm.check_invariants()
     assert a.bm.num_free_blocks == nb
 
@@ -85,7 +88,7 @@ def test_commit_and_argument_errors():
     with pytest.raises(PagedKVError):
         sc.add_request(1, [4], 3)                   # id in use
     plan = sc.step()
-    assert plan["admitted"] == [1]
+    assert plan["admitted"] == [1] and plan["batch"] == [] and plan["writes"] == []
     with pytest.raises(PagedKVError):
         sc.step()                                   # previous step not committed
     with pytest.raises(PagedKVError):
@@ -93,7 +96,8 @@ def test_commit_and_argument_errors():
     with pytest.raises(PagedKVError):
         sc.commit({1: 5, 2: 6})                     # 2 is owed nothing
     sc.commit({1: 5})
-    assert sc.step()["batch"] == [1]
+    plan = sc.step()
+    assert plan["batch"] == [1] and plan["writes"] == [1]
     sc.commit({1: 6})
 
 
