@@ -60,24 +60,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Buffer-descriptor word 3 for raw (untyped) dword access on CDNA:
 // DATA_FORMAT = 32-bit, everything else 0.
 constexpr int kRsrcWord3 = 0x00020000;
-#ifndef PKV_LOAD_AUX
-#define PKV_LOAD_AUX 2             // K/V loads are nontemporal (read once: nt)
-#endif
-#ifndef PKV_NBUF
-#define PKV_NBUF 3                 // K/V blocks in flight per wave (1, 2 groups)
-#endif
-#ifndef PKV_NBUF_MFMA
-#define PKV_NBUF_MFMA 1            // same, matrix-core path (groups of 4 and 8)
-#endif
-#ifndef PKV_MFMA_K_LDS
-#define PKV_MFMA_K_LDS 1           // K rows staged through LDS (row-layout loads) on the MFMA path
-#endif
-#ifndef PKV_WG_MAP
-#define PKV_WG_MAP 1               // 0: head = x; 1: head = (x + y + z) mod Hkv; 2: XCD tiles
-#endif
-#ifndef PKV_NBUF_G4
-#define PKV_NBUF_G4 1              // same, query group of 4 (VGPR-limited)
-#endif
+constexpr int kLoadAux = 2;        // cache policy of K/V loads: nontemporal (read once)
+constexpr int kNbuf = 3;           // K/V blocks in flight per wave, vector path (groups of 1, 2)
+constexpr int kNbufG4 = 1;         // same, fp32 query group of 4 (VGPR-limited)
+constexpr int kNbufMfma = 1;       // same, matrix-core path (groups of 4 and 8)
 
 struct DecodeArgs {
   float* out;            // [B][Hq][D]
@@ -114,44 +100,22 @@ __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
 // XCDs round-robin by linear id, and x (the head) is the fastest index, so
 // with head = x every XCD would read the same head columns of every block
 // (with 32 heads, XCD k gets heads k, k+8, ...: fixed 256-byte columns of
-// each 8 KB row).  Map 1 (default) rotates the head by rot: every XCD still
+// each 8 KB row).  The head is therefore rotated by rot: every XCD still
 // gets a share of every (y, z) tile, which keeps the XCDs balanced when
 // tiles differ in cost (mixed lengths), while its reads spread over all
-// head columns; measured 3-5% more bandwidth than map 0.  The caller picks
-// rot so that sequences sharing blocks (forks, beams: same first block)
-// keep one head -> XCD assignment and meet their shared blocks in that
-// XCD's L2.  Map 2 gives each XCD whole tiles (linear id
-// L = 8 * (Hkv * q + head) + xcd serves tile 8q + xcd, a last partial group
-// of tiles dealt head-fastest): as fast or slightly faster when all tiles
-// cost the same, 10% slower on mixed lengths, where XCD k always gets the
-// sequences b = k mod 8.
+// head columns; measured 3-5% more bandwidth than head = x.  The caller
+// picks rot so that sequences sharing blocks (forks, beams: same first
+// block) keep one head -> XCD assignment and meet their shared blocks in
+// that XCD's L2.
 struct WgCoord {
   int g, y, z;
 };
-__device__ __forceinline__ WgCoord wg_coord(int hkv) {
-  if constexpr (PKV_WG_MAP == 2) {
-    const uint32_t Y = gridDim.y;
-    const uint32_t L = blockIdx.x + hkv * (blockIdx.y + Y * blockIdx.z);
-    const uint32_t T = Y * gridDim.z;               // tiles
-    const uint32_t full = (T / 8) * 8 * hkv;        // ids in whole groups of 8 tiles
-    uint32_t g, tile;
-    if (L < full) {
-      const uint32_t slot = L >> 3;
-      g = slot % hkv;
-      tile = (slot / hkv) * 8 + (L & 7);
-    } else {
-      const uint32_t loc = L - full;
-      g = loc % hkv;
-      tile = (T / 8) * 8 + loc / hkv;
-    }
-    return {static_cast<int>(g), static_cast<int>(tile % Y), static_cast<int>(tile / Y)};
-  } else {
-    return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
-  }
+__device__ __forceinline__ WgCoord wg_coord(int) {
+  return {static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z)};
 }
 
 __device__ __forceinline__ int rotate_head(int g, int hkv, uint32_t rot) {
-  return PKV_WG_MAP == 1 ? static_cast<int>((g + rot) % hkv) : g;
+  return static_cast<int>((g + rot) % hkv);
 }
 
 // The scalar reads a private-grid workgroup starts with, issued together
@@ -385,11 +349,11 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < LPB; ++i)
       kw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            kd, lane_off, i * RPI * row_bytes, PKV_LOAD_AUX));
+                                            kd, lane_off, i * RPI * row_bytes, kLoadAux));
 #pragma unroll
     for (int i = 0; i < LPB; ++i)
       vw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            vd, lane_off, i * RPI * row_bytes, PKV_LOAD_AUX));
+                                            vd, lane_off, i * RPI * row_bytes, kLoadAux));
   };
   auto consume = [&](const uint4 (&kw)[LPB], const uint4 (&vw)[LPB], int gblk) {
     const int vr = n - gblk * kBlock;
@@ -627,9 +591,8 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
 
   const uint32_t row_bytes = static_cast<uint32_t>(a.hkv) * D * ELEM;
   const uint32_t block_bytes = row_bytes * kBlock;
-  // K in MFMA A layout: token t, dims 32j + 8qa; V in row layout: token
-  // i*RPI + vr, dims 8vc .. +8.
-  const uint32_t k_off = t * row_bytes + static_cast<uint32_t>(g * D + 8 * qa) * ELEM;
+  // K and V are loaded in row layout (token i*RPI + vr, dims 8vc .. +8)
+  // and K is re-read from LDS in the MFMA A layout.
   const int vr = lane / LPR, vc = lane % LPR;
   const uint32_t v_off = vr * row_bytes + static_cast<uint32_t>(g * D + 8 * vc) * ELEM;
   char* lds_v = s_wave[w];
@@ -662,12 +625,11 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < KSTEPS; ++j)
       kw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            kd, PKV_MFMA_K_LDS ? v_off : k_off + 64 * j,
-                                            PKV_MFMA_K_LDS ? j * RPI * row_bytes : 0, PKV_LOAD_AUX));
+                                            kd, v_off, j * RPI * row_bytes, kLoadAux));
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i)
       vw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            vd, v_off, i * RPI * row_bytes, PKV_LOAD_AUX));
+                                            vd, v_off, i * RPI * row_bytes, kLoadAux));
   };
 
   auto consume = [&](const uint4 (&kw)[KSTEPS], const uint4 (&vw)[VLOADS], int gblk) {
@@ -681,20 +643,15 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       *reinterpret_cast<uint4*>(lds_v + row * VROW + 16 * vc) = val;
     }
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (PKV_MFMA_K_LDS) {
-      // K rows through LDS too: row-layout loads, MFMA-layout reads.
-      static_assert(KSTEPS == VLOADS, "K row loads reuse the V row mapping");
+    // K rows through LDS too: row-layout loads, MFMA-layout reads.
+    static_assert(KSTEPS == VLOADS, "K row loads reuse the V row mapping");
 #pragma unroll
-      for (int i = 0; i < VLOADS; ++i)
-        *reinterpret_cast<uint4*>(lds_k + (i * RPI + vr) * VROW + 16 * vc) = kw[i];
+    for (int i = 0; i < VLOADS; ++i)
+      *reinterpret_cast<uint4*>(lds_k + (i * RPI + vr) * VROW + 16 * vc) = kw[i];
 #pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) {
-        const uint4 kk = *reinterpret_cast<const uint4*>(lds_k + t * VROW + (32 * j + 8 * qa) * ELEM);
-        sacc = M::qk(kk, qb[j], sacc);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KSTEPS; ++j) sacc = M::qk(kw[j], qb[j], sacc);
+    for (int j = 0; j < KSTEPS; ++j) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(lds_k + t * VROW + (32 * j + 8 * qa) * ELEM);
+      sacc = M::qk(kk, qb[j], sacc);
     }
     float sc[4];
 #pragma unroll
@@ -982,21 +939,21 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
   // skips), then every sequence's private partitions, then the reduce.
   if constexpr (DT != PA_DTYPE_F32) {
     if (a.n_groups > 0)
-      decode_phase1_mfma<DT, D, 16, PKV_NBUF_MFMA, true>
+      decode_phase1_mfma<DT, D, 16, kNbufMfma, true>
           <<<dim3(a.hkv, a.n_groups, (a.max_shared_parts + kWaves - 1) / kWaves), kThreads, 0, st>>>(a);
   }
   dim3 grid(a.hkv, B, a.grid_parts);
   // The matrix-core kernel gives each wave a whole partition.
   dim3 grid_w(a.hkv, B, (a.grid_parts + kWaves - 1) / kWaves);
   switch (group) {
-    case 1: decode_phase1<DT, D, 1, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
-    case 2: decode_phase1<DT, D, 2, PKV_NBUF><<<grid, kThreads, 0, st>>>(a); break;
+    case 1: decode_phase1<DT, D, 1, kNbuf><<<grid, kThreads, 0, st>>>(a); break;
+    case 2: decode_phase1<DT, D, 2, kNbuf><<<grid, kThreads, 0, st>>>(a); break;
     case 4:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, PKV_NBUF_MFMA, false><<<grid_w, kThreads, 0, st>>>(a);
-      else decode_phase1<DT, D, 4, PKV_NBUF_G4><<<grid, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, kNbufMfma, false><<<grid_w, kThreads, 0, st>>>(a);
+      else decode_phase1<DT, D, 4, kNbufG4><<<grid, kThreads, 0, st>>>(a);
       break;
     case 8:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, PKV_NBUF_MFMA, false><<<grid_w, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, kNbufMfma, false><<<grid_w, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a);
       break;
     default: return hipErrorInvalidValue;

@@ -53,20 +53,9 @@ constexpr int kPBlock = 16;                 // tokens per KV block
 constexpr float kPMinusBig = -1e30f;
 constexpr float kPRescaleLog2 = 8.f;
 constexpr int kPRsrcWord3 = 0x00020000;     // buffer descriptor word 3: 32-bit raw access
-#ifndef PKV_PF_QW
-#define PKV_PF_QW 2        // 16-row query tiles per wave
-#endif
-#ifndef PKV_PF_KB
-#define PKV_PF_KB 2        // KV blocks per LDS stage (one barrier each)
-#endif
-#ifndef PKV_PF_WAVES_PER_EU
-#define PKV_PF_WAVES_PER_EU 3  // waves per SIMD the register budget is fitted to
-#endif
-#ifndef PKV_PF_SPLIT_F16
-#define PKV_PF_SPLIT_F16 0 // also split P into two halves for float16 inputs
-#endif
-constexpr int kQW = PKV_PF_QW;
-constexpr int kKB = PKV_PF_KB;
+constexpr int kQW = 2;                      // 16-row query tiles per wave
+constexpr int kKB = 2;                      // KV blocks per LDS stage (one barrier each)
+constexpr int kWavesPerEu = 3;              // waves per SIMD the register budget is fitted to
 constexpr int kQTile = 16 * kQW * kPWaves;  // query rows per workgroup of one head
 
 struct PrefillArgs {
@@ -97,7 +86,7 @@ __device__ __forceinline__ float max_across_rows(float x) {
 }
 
 template <int DT, int D>
-__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_PF_WAVES_PER_EU, PKV_PF_WAVES_PER_EU))) void prefill_mfma(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEu, kWavesPerEu))) void prefill_mfma(PrefillArgs a) {
   using M = MfmaOps<DT>;
   constexpr int ELEM = 2;
   constexpr int KSTEPS = D / 32;
@@ -108,8 +97,8 @@ __global__ __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(PKV_P
   constexpr int CHUNKS = SROWS * CPR;              // chunks per stage (K or V)
   constexpr int LPT = (CHUNKS + kPThreads - 1) / kPThreads;   // chunks per thread
   // bfloat16 keeps 8 bits of p: p goes through the MFMA as a high and a
-  // low part.  float16 keeps 11, enough on its own unless asked otherwise.
-  constexpr bool SPLIT = DT == PA_DTYPE_BF16 || PKV_PF_SPLIT_F16;
+  // low part.  float16 keeps 11, enough on its own.
+  constexpr bool SPLIT = DT == PA_DTYPE_BF16;
 
   __shared__ __attribute__((aligned(16))) char s_k[2][SROWS * VROW];
   __shared__ __attribute__((aligned(16))) char s_v[2][SROWS * VROW];
