@@ -8,7 +8,7 @@ import ctypes
 
 import numpy as np
 
-from ._lib import P_i8, P_i32, P_i64, check, lib
+from ._lib import P_i8, P_i32, P_i64, PagedKVError, check, lib
 
 
 def _i32p(a):
@@ -57,16 +57,26 @@ class BlockManager:
 
     def append_slots(self, seqs, tokens):
         """Batched append_slot.  Returns (slots int64 [B], cow pairs int32
-        [n_cow, 2]).  Raises on the first failure (earlier appends stay)."""
+        [n_cow, 2]).  On the first failing append it raises the library's
+        error with the completed appends attached, since they stay done:
+        ``err.n_done``, ``err.slots`` (their slots) and ``err.cow_pairs``
+        (their copy-on-write pairs, which still have to be copied)."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int64)
         tokens = np.ascontiguousarray(tokens, dtype=np.int32)
         B = len(seqs)
         slots = np.empty(B, dtype=np.int64)
         pairs = np.empty((max(B, 1), 2), dtype=np.int32)
         ncow, ndone = ctypes.c_int32(), ctypes.c_int32()
-        check(lib().pa_bm_append_slots(self._h, seqs.ctypes.data_as(P_i64), _i32p(tokens), B,
-                                       slots.ctypes.data_as(P_i64), _i32p(pairs),
-                                       ctypes.byref(ncow), ctypes.byref(ndone)))
+        st = lib().pa_bm_append_slots(self._h, seqs.ctypes.data_as(P_i64), _i32p(tokens), B,
+                                      slots.ctypes.data_as(P_i64), _i32p(pairs),
+                                      ctypes.byref(ncow), ctypes.byref(ndone))
+        try:
+            check(st)
+        except PagedKVError as err:
+            err.n_done = ndone.value
+            err.slots = slots[:ndone.value].copy()
+            err.cow_pairs = pairs[:ncow.value].copy()
+            raise
         return slots, pairs[:ncow.value].copy()
 
     def fork(self, parent, child):

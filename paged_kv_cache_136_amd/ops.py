@@ -1,10 +1,14 @@
 """torch-tensor front end of the device calls (argument marshalling only).
 
-Each function checks shapes, dtypes and devices, then calls the C entry
-point of the same name on the current HIP stream.  Every step of the path
-runs in the library's kernels; nothing here computes.
+Each function checks shapes, dtypes and devices (every tensor argument,
+outputs and workspaces included, must be a contiguous GPU tensor), then
+calls the C entry point of the same name on the current HIP stream, or on
+``stream`` when one is given; temporaries a call allocates (a defaulted
+output, a workspace) are then allocated on that stream.  Every step of the
+path runs in the library's kernels; nothing here computes.
 """
 
+import contextlib
 import ctypes
 import math
 
@@ -36,6 +40,20 @@ def _dev(*ts):
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream):
+    """Context for allocating a call's temporaries on the stream the call
+    is launched on: torch's caching allocator then hands their memory to
+    the next allocation only in that stream's order, so a temporary freed
+    when the call returns cannot be reused while the kernel is queued."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _check_workspace(workspace):
+    _dev(workspace)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a contiguous uint8 [bytes] GPU tensor")
 
 
 def pa_write_kv(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
@@ -139,7 +157,7 @@ def pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partiti
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 partition_tokens, out, workspace):
+                 partition_tokens, out, workspace, stream):
     _dev(q, k_cache, v_cache, block_tables, context_lens)
     B, hq, d = q.shape
     nb, bs, hkv, d2 = k_cache.shape
@@ -153,15 +171,20 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_le
         raise ValueError("context_lens must be int32 [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
-    elif out.dtype != torch.float32 or out.shape != (B, hq, d) or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 [B, Hq, D]")
+    if out is not None:
+        _dev(out)
+        if out.dtype != torch.float32 or out.shape != (B, hq, d):
+            raise ValueError("out must be contiguous float32 [B, Hq, D] on the GPU")
+    if workspace is not None:
+        _check_workspace(workspace)
     need = pa_decode_workspace_bytes(B, hq, d, int(max_context_len), int(partition_tokens))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+        if need and (workspace is None or workspace.numel() < need):
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
-    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    ws_bytes = workspace.numel() if ws_ptr else 0
     head = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
             int(max_context_len), B, hq, hkv, d, bs, nb, float(scale), int(partition_tokens),
@@ -177,7 +200,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
     block_tables int32 [B, max_blocks]; context_lens int32 [B];
     max_context_len is a host int bounding context_lens."""
     out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
-                                 max_context_len, scale, partition_tokens, out, workspace)
+                                 max_context_len, scale, partition_tokens, out, workspace, stream)
     check(lib().pa_decode(*head, *ws, _stream(stream)))
     return out
 
@@ -210,7 +233,7 @@ def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, max_contex
     max_private_parts are the plan's host-side grid bounds (0 for the
     latter: no bound)."""
     out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
-                                 max_context_len, scale, partition_tokens, out, workspace)
+                                 max_context_len, scale, partition_tokens, out, workspace, stream)
     n = 0 if groups is None else groups.shape[0]
     if n:
         _dev(seq_group, groups)
@@ -248,9 +271,12 @@ def pa_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, max
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
-    elif out.dtype != torch.float32 or out.shape != (T, hq, d) or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 [T, Hq, D]")
+        with _on(stream):
+            out = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    else:
+        _dev(out)
+        if out.dtype != torch.float32 or out.shape != (T, hq, d):
+            raise ValueError("out must be contiguous float32 [T, Hq, D] on the GPU")
     check(lib().pa_prefill(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                            block_tables.data_ptr(), block_tables.shape[1], query_start.data_ptr(),
                            context_lens.data_ptr(), B, T, int(max_query_len), hq, hkv, d, bs, nb,

@@ -245,3 +245,37 @@ def test_fork_free_batch_errors():
     bm.free_batch([3, 99, 2])                      # unknown ids are no-ops
     assert bm.seq_ids() == [1]
     bm.check_invariants()
+
+
+def test_append_slots_failure_reports_completed_appends():
+    """A batch that runs out of blocks part way keeps its completed appends,
+    and the raised error hands back their slots and copy-on-write pairs
+    (the caller still has to copy those blocks).  The oracle manager run
+    op by op gives the same slots, pairs and state."""
+    bs, nb = 4, 5
+    lib_bm, ref = BlockManager(nb, bs, False), oracle.RefBlockManager(nb, bs, False)
+    for m in (lib_bm, ref):
+        m.allocate(1, [1, 2, 3, 4, 5, 6])     # blocks 0, 1 (the second half full)
+        m.fork(1, 2)                          # both share blocks 0 and 1
+        m.allocate(3, [7, 8, 9, 10])          # block 2, full
+        m.allocate(4, [11])                   # block 3
+    # seq 1 copies its shared partial block into block 4 (the last free one);
+    # seq 2 then owns block 1 alone and writes in place; seq 3 needs a new
+    # block and fails.
+    seqs, toks = [1, 2, 3, 4], [50, 51, 52, 53]
+    with pytest.raises(OutOfBlocks) as info:
+        lib_bm.append_slots(seqs, toks)
+    err = info.value
+    want_slots, want_pairs = [], []
+    for s, t in zip(seqs, toks):
+        try:
+            slot, cow = ref.append_slot(s, t)
+        except oracle.OutOfBlocks:
+            break
+        want_slots.append(slot)
+        if cow is not None:
+            want_pairs.append(list(cow))
+    assert err.n_done == 2 == len(want_slots)
+    assert err.slots.tolist() == want_slots == [4 * bs + 2, 1 * bs + 2]
+    assert err.cow_pairs.tolist() == want_pairs == [[1, 4]]
+    _same(lib_bm, ref)

@@ -1,0 +1,101 @@
+"""The torch front end's argument checks and stream handling, on the GPU.
+
+A host tensor handed to a device call as an output or a workspace would
+reach a kernel as an address the GPU has not mapped, so the front end must
+refuse it with a ValueError before anything is launched.  A call on a
+stream other than the current one must allocate its temporaries on that
+stream; its result is checked against the float64 oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, make_cache, random_tables, say
+
+pytestmark = pytest.mark.gpu
+
+pkv = pytest.importorskip("paged_kv_cache_136_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def _case(B=3, hq=4, hkv=4, d=64, n=200, seed=5):
+    nb, bs = 128, 16
+    lens = np.array([n, n // 2 + 1, 17][:B], dtype=np.int32)
+    tab = random_tables(lens, bs, nb, seed)
+    k, v = make_cache(nb, bs, hkv, d, "f16", seed=seed)
+    q = workloads.normal_torch((B, hq, d), seed + 9, torch.float16, "cuda")
+    return q, k, v, tab, lens
+
+
+def test_decode_rejects_host_out_and_workspace():
+    q, k, v, tab, lens = _case()
+    say("frontend host out / workspace")
+    args = (q, k, v, torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda(), int(lens.max()))
+    need = pkv.pa_decode_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], int(lens.max()), 64)
+    assert need > 0
+    with pytest.raises(ValueError):
+        pkv.pa_decode(*args, partition_tokens=64, out=torch.empty(q.shape, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        pkv.pa_decode(*args, partition_tokens=64, workspace=torch.empty(need, dtype=torch.uint8))
+    with pytest.raises(ValueError):                 # not contiguous
+        pkv.pa_decode(*args, partition_tokens=64,
+                      workspace=torch.empty(2 * need, dtype=torch.uint8, device="cuda")[::2])
+    with pytest.raises(ValueError):                 # not bytes
+        pkv.pa_decode(*args, partition_tokens=64,
+                      workspace=torch.empty(need, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):                 # not contiguous
+        pkv.pa_decode(*args, partition_tokens=64,
+                      out=torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32,
+                                      device="cuda").transpose(1, 2))
+    sg = torch.full((q.shape[0],), -1, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        pkv.pa_decode_shared(*args, sg, None, 0, partition_tokens=64,
+                             workspace=torch.empty(need, dtype=torch.uint8))
+    torch.cuda.synchronize()
+
+
+def test_prefill_rejects_host_out():
+    nb, bs, hkv, d = 32, 16, 2, 64
+    say("frontend prefill host out")
+    k, v = make_cache(nb, bs, hkv, d, "f16", seed=40)
+    lens = np.array([40], dtype=np.int32)
+    tab = random_tables(lens, bs, nb, 41)
+    q = workloads.normal_torch((8, 2, d), 42, torch.float16, "cuda")
+    qs = torch.tensor([0, 8], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        pkv.pa_prefill(q, k, v, torch.from_numpy(tab).cuda(), qs, torch.from_numpy(lens).cuda(), 8,
+                       out=torch.empty((8, 2, d), dtype=torch.float32))
+    torch.cuda.synchronize()
+
+
+def test_decode_on_a_side_stream():
+    """Defaulted out and workspace on a non-current stream; the current
+    stream allocates and writes over freed memory meanwhile."""
+    q, k, v, tab, lens = _case(n=900, seed=7)
+    say("frontend side stream")
+    d_tab, d_len = torch.from_numpy(tab).cuda(), torch.from_numpy(lens).cuda()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(4):
+        outs.append(pkv.pa_decode(q, k, v, d_tab, d_len, int(lens.max()), partition_tokens=64,
+                                  stream=side))
+        junk = torch.full((1 << 20,), float("nan"), device="cuda")   # current stream
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    want = oracle.ref_decode(q.float().cpu().numpy(), k.float().cpu().numpy(),
+                             v.float().cpu().numpy(), tab, lens)
+    for o in outs:
+        assert np.abs(o.cpu().numpy() - want).max() <= TOL["f16"]

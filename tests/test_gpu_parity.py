@@ -137,7 +137,7 @@ def test_decode_many_partitions_windows(dtype, group, poison_ws):
     ws = None
     if poison_ws:
         need = pkv.pa_decode_workspace_bytes(len(lens), hq, 128, max(lens), 16)
-        ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
     got, want = _run_decode(lens, hq, 2, 128, dtype, 16, seed=11, workspace=ws)
     assert np.isfinite(got).all()
     assert np.abs(got - want).max() <= TOL[dtype]
@@ -216,7 +216,7 @@ def test_decode_many_sequences(dtype, group, poison_ws):
     ws = None
     if poison_ws:
         need = pkv.pa_decode_workspace_bytes(len(lens), 8, 64, max(lens), 16)
-        ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
     got, want = _run_decode(lens, 8, 8 // group, 64, dtype, 16, seed=41 + group, workspace=ws)
     assert np.isfinite(got).all()
     assert np.abs(got - want).max() <= TOL[dtype]
