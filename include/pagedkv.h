@@ -459,6 +459,28 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
               int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, semantics, supported shapes and
+ * errors as pa_decode, except that the split-KV partition results go to a
+ * scratch array inside the library: a file-scope device array of
+ * pa_decode_noalloc_max_bytes() bytes (64 MiB), one per GPU the library
+ * runs on, held until the process ends.  The call itself allocates nothing
+ * (no hipMalloc, no hipFree); its first call on a device looks up that
+ * device's copy of the array once.  Sizes whose workspace
+ * (pa_decode_workspace_bytes) exceeds the scratch size are rejected with
+ * PA_ERR_INVALID before anything is launched.  The scratch needs no
+ * initialisation.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one device (on different streams, or from several
+ * threads without ordering) race. */
+size_t pa_decode_noalloc_max_bytes(void);
+int pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, float scale,
+                      int32_t partition_tokens, int32_t dtype, void* stream);
+
 /* ---- shared-prefix decode ------------------------------------------------
  * Sequences forked from one parent share the parent's blocks ([D31] fork
  * and copy-on-write) and prefix-cache hits share full blocks ([P06] spec

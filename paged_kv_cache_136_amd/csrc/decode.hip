@@ -43,6 +43,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "device_common.hpp"
@@ -1013,7 +1014,40 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int3
   return ws_layout(B, num_q_heads, head_dim, P).total;
 }
 
+// Split-KV scratch of pa_decode_noalloc: the partition results live in this
+// file-scope device array instead of a caller's workspace.  Each GPU the
+// library runs on holds its own copy for the life of the process.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in): the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current and kept per device.
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_ptr(const std::string& name, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(PA_ERR_DEVICE, name + ": hipGetDevice failed: " + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, name + ": device index beyond " + std::to_string(kMaxDevices));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PA_ERR_DEVICE, name + ": hipGetSymbolAddress(scratch) failed: " +
+                                     hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
 
 int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -1022,7 +1056,7 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
                 int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
                 const int32_t* seq_group, const int32_t* groups, int32_t n_groups,
                 int32_t max_shared_parts, int32_t max_private_parts, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool use_scratch = false) {
   const std::string name(fn);
   auto err_ = [&](int code, const std::string& msg) { return fail(code, name + ": " + msg); };
   if (B < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
@@ -1063,6 +1097,16 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
   if (a.num_parts > 65535)
     return err_(PA_ERR_UNSUPPORTED, "more than 65535 partitions; use larger partitions");
   const WsLayout wl = ws_layout(B, num_q_heads, head_dim, a.num_parts);
+  if (use_scratch && wl.total > 0) {
+    if (wl.total > kScratchBytes)
+      return err_(PA_ERR_INVALID, "needs " + std::to_string(wl.total) +
+                                      " bytes of split-KV scratch; the library's scratch holds " +
+                                      std::to_string(kScratchBytes) +
+                                      " (use larger partitions, fewer sequences, or pa_decode)");
+    const int st = scratch_ptr(name, &workspace);
+    if (st != PA_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (wl.total > 0) {
     if (!workspace || workspace_bytes < wl.total)
       return err_(PA_ERR_INVALID, "workspace too small (need " +
@@ -1149,4 +1193,19 @@ extern "C" int pa_decode_shared(float* out, const void* q, const void* k_cache,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
                      dtype, seq_group, groups, n_groups, max_shared_parts, max_private_parts,
                      workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int pa_decode_noalloc(float* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, int32_t B, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, float scale, int32_t partition_tokens,
+                                 int32_t dtype, void* stream) {
+  return decode_impl("pa_decode_noalloc", out, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, B, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
+                     dtype, nullptr, nullptr, 0, 0, 0, nullptr, 0, stream, true);
 }

@@ -157,7 +157,7 @@ def pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partiti
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 partition_tokens, out, workspace, stream):
+                 partition_tokens, out, workspace, stream, with_workspace=True):
     _dev(q, k_cache, v_cache, block_tables, context_lens)
     B, hq, d = q.shape
     nb, bs, hkv, d2 = k_cache.shape
@@ -177,7 +177,8 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_le
             raise ValueError("out must be contiguous float32 [B, Hq, D] on the GPU")
     if workspace is not None:
         _check_workspace(workspace)
-    need = pa_decode_workspace_bytes(B, hq, d, int(max_context_len), int(partition_tokens))
+    need = (pa_decode_workspace_bytes(B, hq, d, int(max_context_len), int(partition_tokens))
+            if with_workspace else 0)
     with _on(stream):
         if out is None:
             out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
@@ -203,6 +204,24 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
                                  max_context_len, scale, partition_tokens, out, workspace, stream)
     check(lib().pa_decode(*head, *ws, _stream(stream)))
     return out
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
+                      scale=None, partition_tokens=512, stream=None):
+    """pa_decode whose split-KV partials live in the library's per-device
+    scratch array (pa_decode_noalloc_max_bytes() bytes) instead of a
+    workspace: the caller passes every buffer, ``out`` included, and the
+    call allocates nothing.  Calls that overlap on one GPU race."""
+    if out is None:
+        raise ValueError("pa_decode_noalloc needs a caller-owned out")
+    out, head, _ = _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                                scale, partition_tokens, out, None, stream, with_workspace=False)
+    check(lib().pa_decode_noalloc(*head, _stream(stream)))
+    return out
+
+
+def pa_decode_noalloc_max_bytes():
+    return lib().pa_decode_noalloc_max_bytes()
 
 
 def pa_shared_plan(block_tables, context_lens, block_size, partition_tokens, query_group):

@@ -216,3 +216,22 @@ def test_shared_decode_plan_rejections():
     ]:
         assert shared(**kw) == status, kw
         assert msg in L.pa_last_error(), (kw, L.pa_last_error())
+
+
+def test_noalloc_decode_rejects_oversize_before_touching_the_gpu():
+    """pa_decode_noalloc checks every argument, then whether the partials
+    fit the library's scratch, before its first HIP call."""
+    from paged_kv_cache_136_amd import lib
+    L = lib()
+    keep = []
+    p = _aligned_host_ptr(keep)
+    cap = L.pa_decode_noalloc_max_bytes()
+    assert cap == 64 << 20
+    # 4 sequences x 32 heads x 128 dims, contexts up to 2^20 tokens in
+    # 512-token partitions: 2048 partitions, ~136 MB of partials.
+    assert L.pa_decode_workspace_bytes(4, 32, 128, 1 << 20, 512) > cap
+    st = L.pa_decode_noalloc(p, p, p, p, p, 65536, p, 1 << 20, 4, 32, 8, 128, 16, 64, 0.088, 512,
+                             2, None)
+    assert st == 2 and b"scratch" in L.pa_last_error()
+    st = L.pa_decode_noalloc(p, p, p, p, p, 8, p, 64, 2, 8, 2, 96, 16, 64, 0.088, 0, 1, None)
+    assert st == 3 and b"head_dim" in L.pa_last_error()
