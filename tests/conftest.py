@@ -32,3 +32,14 @@ def pytest_sessionstart(session):
     if not os.path.exists(lib):
         import runpy
         runpy.run_path(os.path.join(ROOT, "paged_kv_cache_136_amd", "build.py"))["build"]()
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the figures GPU tests recorded (max abs errors of the full-size
+    parity cases), so a run's log carries them even when every test passes."""
+    mod = sys.modules.get("tests.gpu_util")
+    rows = getattr(mod, "REPORT", [])
+    if rows:
+        terminalreporter.section("parity figures")
+        for name, value in rows:
+            terminalreporter.write_line(f"{name}: {value:.3e}")

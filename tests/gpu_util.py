@@ -12,9 +12,17 @@ TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat
 TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3}
 
 
+REPORT = []
+
+
 def say(*args):
     """Name the case before each GPU step (flushed, so a crash still shows it)."""
     print("[gpu-case]", *args, file=sys.stderr, flush=True)
+
+
+def report(name, value):
+    """Record a measured figure (a max abs error) for the end-of-run summary."""
+    REPORT.append((name, value))
 
 
 def host_f32(t):
