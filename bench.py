@@ -34,8 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, published
-PMC_FILE = os.path.join(ROOT, "profiles", "pa_decode_mixed_7b_pmc.json")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_136_amd", "csrc", "decode.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "paged_kv_cache_136_amd", "csrc")
+DECODE_SRC = os.path.join(CSRC, "decode.hip")
 
 
 def parse_args():
@@ -44,8 +45,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="mixed_7b",
-                   choices=["mixed_7b", "13b_layer", "gqa_long", "fork_cow", "swap", "serve", "beam",
-                            "prefill", "prefill_gqa"],
+                   choices=["mixed_7b", "tiny", "13b_layer", "gqa_long", "fork_cow", "swap", "serve",
+                            "beam", "prefill", "prefill_gqa"],
                    help="mixed_7b is the headline workload; the others are reported lines")
     p.add_argument("--shared-prefix", choices=["on", "off"], default=None,
                    help="serve: decode with pa_decode_shared (default: the workload's choice)")
@@ -55,14 +56,19 @@ def parse_args():
                    help="target CPU time of the oracle baseline sample (0 = skip)")
     p.add_argument("--calibrate", action="store_true",
                    help="instead of the step: run pa_copy_blocks over a known number of "
-                        "bytes (3 launches of 8192 x 128 KiB blocks, K and V), for scaling "
-                        "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+                        "bytes (3 launches of 8192 x 128 KiB blocks, K and V) and "
+                        "pa_stream_read over 8 GiB (3 launches), for scaling rocprofv3 "
+                        "FETCH_SIZE / WRITE_SIZE readings")
+    p.add_argument("--read-gib", type=int, default=8,
+                   help="size of the streaming-read ceiling measurement (0 = skip)")
     return p.parse_args()
 
 
 def calibrate():
     """pa_copy_blocks over 8192 disjoint block pairs of 128 KiB in one layer's
-    K and V: each launch reads and writes exactly 2 * 8192 * 128 KiB = 2 GiB."""
+    K and V: each launch reads and writes exactly 2 * 8192 * 128 KiB = 2 GiB.
+    Then pa_stream_read over 8 GiB: each launch reads exactly 8 GiB and
+    writes nothing."""
     import torch
 
     import paged_kv_cache_136_amd as pkv
@@ -75,8 +81,55 @@ def calibrate():
         pkv.pa_copy_blocks([k], [v], pairs)
     torch.cuda.synchronize()
     nbytes = 2 * 8192 * k[0].numel() * k.element_size()
-    print(json.dumps({"calibration": "pa_copy_blocks", "launches": 3,
-                      "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}))
+    del k, v
+    buf = torch.zeros(8 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pkv.pa_stream_read(buf, 4096, sink)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": ["pa_copy_blocks", "pa_stream_read"], "launches": 3,
+                      "copy_read_bytes_per_launch": nbytes, "copy_write_bytes_per_launch": nbytes,
+                      "stream_read_bytes_per_launch": 8 << 30}))
+
+
+def stream_read_ceiling(torch, pkv, gib):
+    """HBM read rate reachable on this GPU: pa_stream_read over a ``gib``
+    GiB buffer (far above the 256 MB Infinity Cache) with 1024, 4096 and
+    16384 workgroups, 2 untimed then 5 timed launches each (HIP events);
+    the best median.  Run after the timed steps, outside them."""
+    if gib <= 0:
+        return None
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    T = torch.cuda.Event
+    per = {}
+    for wg in (1024, 4096, 16384):
+        for _ in range(2):
+            pkv.pa_stream_read(buf, wg, sink)
+        ev = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(5)]
+        for a, b in ev:
+            a.record()
+            pkv.pa_stream_read(buf, wg, sink)
+            b.record()
+        torch.cuda.synchronize()
+        per[wg] = nbytes / (float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    best = max(per, key=per.get)
+    return {"gbs": round(per[best], 2), "bytes": nbytes, "workgroups": best,
+            "by_workgroups": {str(k): round(v, 2) for k, v in per.items()},
+            "kernel": "pa_stream_read (nontemporal 16-byte buffer loads, one contiguous "
+                      "chunk per workgroup)"}
+
+
+def with_ceiling(roofline, ceiling):
+    """Adds the measured read ceiling and the achieved fraction of it."""
+    if roofline is not None and ceiling is not None:
+        roofline["measured_read_gbs"] = ceiling["gbs"]
+        roofline["frac_of_measured_read"] = round(roofline["achieved"] / ceiling["gbs"], 4)
+        roofline["measured_read"] = ceiling
+    return roofline
 
 
 def source_sha(path):
@@ -84,15 +137,18 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, or None if absent or taken on a different kernel source."""
+def load_traffic(name):
+    """HBM bytes per launch of a workload's dominant kernel from its
+    committed rocprofv3 counter summary (profiles/<name>_pmc.json), or None
+    if absent or taken on a different source of the kernel."""
     try:
-        with open(PMC_FILE) as f:
+        with open(os.path.join(PROFILES, name + "_pmc.json")) as f:
             pmc = json.load(f)
     except (OSError, ValueError):
         return None
-    if pmc.get("decode_source_sha") != source_sha(DECODE_SRC):
+    src = os.path.join(CSRC, pmc.get("source_file", "decode.hip"))
+    sha = pmc.get("source_sha", pmc.get("decode_source_sha"))
+    if not os.path.exists(src) or sha != source_sha(src):
         return None
     return pmc.get("traffic_bytes_per_launch")
 
@@ -103,7 +159,11 @@ TORCH_DTYPE_NAMES = {"f32": "float32", "f16": "float16", "bf16": "bfloat16"}
 def cpu_baseline(lens, hq, hkv, D, bs, dtype, seconds, layers, workload):
     """The oracle timed on the host over one layer of the same workload
     shape (a prefix of the sequences, all heads), with fresh seeded inputs,
-    repeated until about ``seconds``; BLAS limited to one thread."""
+    repeated until about ``seconds``.  The sample's sequences are split
+    over one thread per core this process may run on (at most 16), each
+    calling the oracle on its share with BLAS limited to one thread."""
+    import concurrent.futures
+
     import torch
     from threadpoolctl import threadpool_limits
 
@@ -128,19 +188,25 @@ def cpu_baseline(lens, hq, hkv, D, bs, dtype, seconds, layers, workload):
     q = workloads.normal_torch((len(lens), hq, D), 14, tdt, "cuda").float().cpu().numpy()
     elem = workloads.ELEM_BYTES[dtype]
     sample_bytes = int(np.sum(lens)) * 2 * hkv * D * elem
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), len(lens)))
+
+    def run_seq(b):
+        oracle.ref_decode(q[b:b + 1], k, v, tables[b:b + 1], lens[b:b + 1])
+
     reps, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=1), concurrent.futures.ThreadPoolExecutor(cores) as ex:
         while True:
-            oracle.ref_decode(q, k, v, tables, lens)
+            list(ex.map(run_seq, range(len(lens))))
             reps += 1
             el = time.perf_counter() - t0
             if el >= seconds:
                 break
-    return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+    return {"value": round(sample_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"one layer of the {workload} step restricted to its first {nseq} sequences "
                       f"({int(np.sum(lens))} tokens x {hq} query heads, fresh seeded {dtype} inputs), "
-                      f"{reps} repetitions in {el:.1f} s, float64 NumPy, BLAS 1 thread",
+                      f"{reps} repetitions in {el:.1f} s, float64 NumPy, one sequence per task on "
+                      f"{cores} threads, BLAS 1 thread each",
             "seqs_per_s": round(nseq * reps / el / layers, 4)}
 
 
@@ -330,12 +396,14 @@ class DecodeBench:
             "host_bm_ms_per_step": round(1e3 * float(np.mean(self.host_s)), 4),
             "gpu_step_ms_p10_p50_p90": [round(float(x), 4) for x in
                                         np.percentile(step_gpu_ms, [10, 50, 90])],
-            "roofline": {"kernel": "pa_decode (split-KV phase 1 + reduce), one layer",
-                         "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                         "traffic": load_traffic() if self.name == "mixed_7b" else None,
-                         "avg_launch_ms": round(float(dec_ms.mean()), 5),
-                         "algorithmic_bytes_per_launch": int(launch_bytes.mean())},
+            "roofline": with_ceiling(
+                {"kernel": "pa_decode (split-KV phase 1 + reduce), one layer",
+                 "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                 "traffic": load_traffic("pa_decode_" + self.name),
+                 "avg_launch_ms": round(float(dec_ms.mean()), 5),
+                 "algorithmic_bytes_per_launch": int(launch_bytes.mean())},
+                stream_read_ceiling(torch, self.pkv, args.read_gib)),
         }
 
 
@@ -442,6 +510,19 @@ def run_fork_cow(args, torch, pkv, workloads):
     round_ev[1].record()
     torch.cuda.synchronize()
     cow_ms, round_ms = cow_ev[0].elapsed_time(cow_ev[1]), round_ev[0].elapsed_time(round_ev[1])
+    # The same copies again (idempotent: each destination gets its source's
+    # bytes once more), each after a 1 GiB scratch write so its blocks come
+    # from HBM as in the round itself: five more event-timed launches.
+    scratch = torch.empty(2**30, dtype=torch.uint8, device=dev)
+    rep_ev = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(5)]
+    for i, (a, b) in enumerate(rep_ev):
+        scratch.fill_(i)
+        a.record()
+        pkv.pa_copy_blocks([k], [v], d_pairs)
+        b.record()
+    torch.cuda.synchronize()
+    del scratch
+    cow_rep_ms = np.array([a.elapsed_time(b) for a, b in rep_ev])
     # Rounds 2..X untimed (the flow up to 2305 tokens per sequence).
     for r in range(2, X + 1):
         d_slot, _, n = append(seqs, toks)
@@ -488,6 +569,12 @@ def run_fork_cow(args, torch, pkv, workloads):
     value = float(logical.sum() / (step_ms.sum() * 1e-3) / 1e9)
     achieved_u = float(unique.mean() / (dec_ms.mean() * 1e-3) / 1e9)
     cow_bytes = npairs * 2 * 2 * k[0].numel() * 2          # K and V, read + write
+    cow_med = float(np.median(np.append(cow_rep_ms, cow_ms)))
+    ceiling = stream_read_ceiling(torch, pkv, args.read_gib)
+    cpu = (cpu_baseline([n_last] * B, cfg["hq"], H, D, bs, "f16", args.cpu_seconds, 1, "fork_cow")
+           if args.cpu_seconds > 0 else None)
+    if cpu is not None:
+        cpu["sample"] += "; logical bytes (the oracle reads every sequence's blocks)"
     return {
         "metric": "paged decode attention: achieved KV GB/s (% of HBM peak) and seqs/s",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -506,17 +593,28 @@ def run_fork_cow(args, torch, pkv, workloads):
         "used_blocks": int(NB - bm.num_free_blocks),
         "cow_round": {"pairs": npairs, "copy_ms": round(cow_ms, 4),
                       "copy_gbs": round(cow_bytes / (cow_ms * 1e-3) / 1e9, 2),
-                      "round_ms": round(round_ms, 4)},
+                      "round_ms": round(round_ms, 4),
+                      "copy_ms_repeats": [round(float(x), 4) for x in cow_rep_ms],
+                      "roofline": {"kernel": "copy_blocks_kernel (448 pairs, K and V, one layer)",
+                                   "bound": "hbm", "unit": "GB/s",
+                                   "achieved": round(cow_bytes / (cow_med * 1e-3) / 1e9, 2),
+                                   "peak": PEAK_HBM_GBS,
+                                   "frac": round(cow_bytes / (cow_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "avg_launch_ms": round(cow_med, 5),
+                                   "algorithmic_bytes_per_launch": cow_bytes,
+                                   "traffic": load_traffic("copy_blocks_fork_cow")}},
         "shared_prefix": {"groups": n_groups, "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
                           "decode_ms": round(float(dec_ms.mean()), 5),
                           "plain_pa_decode_ms": round(float(plain_ms.mean()), 5),
                           "plain_unique_gbs": round(float(unique[-1] / (plain_ms.mean() * 1e-3) / 1e9), 2)},
-        "roofline": {"kernel": "pa_decode_shared (shared phase + private phase + reduce), unique bytes",
-                     "bound": "hbm", "achieved": round(achieved_u, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved_u / PEAK_HBM_GBS, 4),
-                     "traffic": None, "avg_launch_ms": round(float(dec_ms.mean()), 5),
-                     "algorithmic_bytes_per_launch": int(unique.mean())},
-        "cpu_baseline": None,
+        "roofline": with_ceiling(
+            {"kernel": "pa_decode_shared (shared phase + private phase + reduce), unique bytes",
+             "bound": "hbm", "achieved": round(achieved_u, 2), "peak": PEAK_HBM_GBS,
+             "unit": "GB/s", "frac": round(achieved_u / PEAK_HBM_GBS, 4),
+             "traffic": load_traffic("pa_decode_shared_fork_cow"),
+             "avg_launch_ms": round(float(dec_ms.mean()), 5),
+             "algorithmic_bytes_per_launch": int(unique.mean())}, ceiling),
+        "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
     }
 
@@ -685,7 +783,16 @@ def run_serve(args, torch, pkv, workloads):
                                     if prompt_ms else None),
         "host_sched_ms_per_step": round((eng.host_seconds - host0) / args.steps * 1e3, 4),
         "events": counts,
-        "roofline": None,
+        "roofline": with_ceiling(
+            {"kernel": "decode phase of the engine step: 32 x pa_decode with table export and "
+                       "upload, unique KV bytes of the batch",
+             "bound": "hbm", "unit": "GB/s",
+             "achieved": round(kv_bytes / (decode_ms * 1e-3) / 1e9, 2) if decode_ms else None,
+             "peak": PEAK_HBM_GBS,
+             "frac": round(kv_bytes / (decode_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if decode_ms else None,
+             "traffic": None, "avg_launch_ms": round(decode_ms / args.steps / L, 5),
+             "algorithmic_bytes_per_launch": int(kv_bytes / args.steps / L)},
+            stream_read_ceiling(torch, pkv, args.read_gib)),
         "cpu_baseline": None,
         "wall_s": round(wall, 3),
     }
@@ -837,7 +944,17 @@ def run_beam(args, torch, pkv, workloads):
         "decode_ms_per_step": round(float(dec_ms.mean()), 4),
         "host_ms_per_step": round(float(np.mean([x[3] for x in info]) * 1e3), 4),
         "final_batch_decode": cmp,
-        "roofline": None, "cpu_baseline": None, "wall_s": round(wall, 3),
+        "roofline": with_ceiling(
+            {"kernel": "pa_decode_shared (shared phase + private phase + reduce), unique bytes",
+             "bound": "hbm", "unit": "GB/s",
+             "achieved": round(float(uniq.mean() * bs * per_tok / (dec_ms.mean() * 1e-3) / 1e9), 2),
+             "peak": PEAK_HBM_GBS,
+             "frac": round(float(uniq.mean() * bs * per_tok / (dec_ms.mean() * 1e-3) / 1e9)
+                           / PEAK_HBM_GBS, 4),
+             "traffic": None, "avg_launch_ms": round(float(dec_ms.mean()), 5),
+             "algorithmic_bytes_per_launch": int(uniq.mean() * bs * per_tok)},
+            stream_read_ceiling(torch, pkv, args.read_gib)),
+        "cpu_baseline": None, "wall_s": round(wall, 3),
     }
 
 
@@ -934,6 +1051,7 @@ def run_prefill(args, torch, pkv, workloads):
 
 
 LENGTH_NOTES = {
+    "tiny": "[7, 16, 31, 48, 63] (day31 block-count script), +1 token per step",
     "mixed_7b": "log-uniform [50, 4096], PCG64 seed 0, +1 token per step",
     "13b_layer": "10 x 4096, +1 token per step",
     "gqa_long": "32 x 32768, +1 token per step",

@@ -555,6 +555,18 @@ int pa_decode_shared(float* out, const void* q, const void* k_cache, const void*
                      int32_t max_private_parts, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* ==== measurement helper (gfx950) ========================================
+ * Streaming read of `bytes` bytes of device memory at `buf` (both multiples
+ * of 16): `workgroups` workgroups each read one contiguous chunk once, with
+ * the nontemporal 16-byte buffer loads the decode kernels use.  Used to
+ * measure the HBM read rate actually reachable on the GPU, which the decode
+ * bandwidth is reported beside.  Nothing is written except, rarely, a
+ * checksum into sink[workgroup] (device, >= workgroups uint32 entries),
+ * which exists only so the loads are not optimised away.  workgroups in
+ * [1, 2^24]; a chunk must stay under 2 GiB.  bytes == 0 launches nothing. */
+int pa_stream_read(const void* buf, uint64_t bytes, int32_t workgroups, uint32_t* sink,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

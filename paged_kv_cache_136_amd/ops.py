@@ -301,3 +301,17 @@ def pa_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, max
                            context_lens.data_ptr(), B, T, int(max_query_len), hq, hkv, d, bs, nb,
                            float(scale), _dtype_code(q), _stream(stream)))
     return out
+
+
+def pa_stream_read(buf, workgroups, sink, stream=None):
+    """Streaming read of every byte of the GPU tensor ``buf`` (a size that is
+    a multiple of 16 bytes) by ``workgroups`` workgroups, each reading one
+    contiguous chunk; ``sink`` is an int32 GPU tensor of >= workgroups
+    entries (rarely written).  Measures the HBM read rate reachable on the
+    GPU."""
+    _dev(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    if sink.dtype != torch.int32 or sink.numel() < workgroups:
+        raise ValueError("sink must be an int32 GPU tensor of >= workgroups entries")
+    check(lib().pa_stream_read(buf.data_ptr(), nbytes, int(workgroups), sink.data_ptr(),
+                               _stream(stream)))
