@@ -116,6 +116,18 @@ def test_decode_ragged(dtype, d, group):
     assert err <= TOL[dtype], err
 
 
+@pytest.mark.parametrize("dtype,d,hkv,group", [("bf16", 128, 3, 4), ("f16", 64, 5, 8),
+                                               ("f16", 128, 6, 4), ("bf16", 64, 4, 8)])
+def test_decode_mfma_head_counts(dtype, d, hkv, group):
+    """The matrix-core path takes two adjacent KV heads per wave when the
+    KV head count is even and one otherwise: odd and even head counts, both
+    group sizes, ragged lengths, NaN-poisoned unused slots."""
+    say("decode_mfma_heads", dtype, d, hkv, group)
+    got, want = _run_decode(RAGGED, hkv * group, hkv, d, dtype, 64, seed=300 + hkv + group)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]
+
+
 @pytest.mark.parametrize("partition", [0, 16, 64, 256, 512, 4096])
 def test_decode_partition_sizes(partition):
     say("decode_partition", partition)
