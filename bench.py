@@ -9,12 +9,9 @@ permutation).  One step is one pass of the whole hot path:
   host   pa_bm_append_slots (one new token per sequence: slot, table growth)
          pa_bm_export_batch into a pinned staging buffer, one async upload
          (the block tables only when they changed)
-  device pa_copy_blocks when appends report copy-on-write pairs (none in
-         this workload); for each layer pa_write_kv (the new token's K/V)
-         and pa_decode (split-KV phase 1 + reduce).  The writes go to a
-         second stream right after the upload, so later layers' writes run
-         beside earlier layers' decodes; each decode waits on its layer's
-         write.
+  device for each layer: pa_write_kv (the new token's K/V), pa_decode
+         (split-KV phase 1 + reduce); pa_copy_blocks when appends report
+         copy-on-write pairs (none in this workload)
 
 Sequences grow by one token per step, as in real decoding; the KV bytes of
 every step are counted exactly.  The metric is achieved KV GB/s (valid
@@ -276,13 +273,6 @@ class DecodeBench:
         for p in self.pin:
             p["ev"].record()
         self.new_tok = np.full(B, 7, dtype=np.int32)
-        # With several layers, every layer's K/V write goes to a second
-        # stream (default priority) as soon as the step's upload is done, so
-        # the writes of later layers run beside the decodes of earlier ones;
-        # each layer's decode waits on its own write.
-        self.side = torch.cuda.Stream() if L > 1 else None
-        self.ev_up = torch.cuda.Event()
-        self.ev_w = [torch.cuda.Event() for _ in range(L)]
         self.k_layers = [self.pool[layer, 0] for layer in range(L)]
         self.v_layers = [self.pool[layer, 1] for layer in range(L)]
         self.host_s = []
@@ -322,20 +312,9 @@ class DecodeBench:
         if len(pairs):
             pkv.pa_copy_blocks(self.k_layers, self.v_layers, self.d_pairs[:len(pairs)])
         max_len = int(self.lens0.max()) + s
-        main = self.torch.cuda.current_stream()
-        if self.side is not None:
-            self.ev_up.record(main)
-            self.side.wait_event(self.ev_up)
-            for layer in range(self.L):
-                pkv.pa_write_kv(self.k_layers[layer], self.v_layers[layer], self.k_new[layer],
-                                self.v_new[layer], self.d_slot, stream=self.side)
-                self.ev_w[layer].record(self.side)
         for layer in range(self.L):
-            if self.side is None:
-                pkv.pa_write_kv(self.k_layers[layer], self.v_layers[layer], self.k_new[layer],
-                                self.v_new[layer], self.d_slot)
-            else:
-                main.wait_event(self.ev_w[layer])
+            pkv.pa_write_kv(self.k_layers[layer], self.v_layers[layer], self.k_new[layer],
+                            self.v_new[layer], self.d_slot)
             if ev_pairs is not None:
                 ev_pairs[layer][0].record()
             pkv.pa_decode(self.q[layer], self.k_layers[layer], self.v_layers[layer], self.d_tab,
