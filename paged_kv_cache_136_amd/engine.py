@@ -66,8 +66,10 @@ class DecodeEngine:
                       [torch.zeros(shape, dtype=dtype, device=self.dev) for _ in range(num_layers)])
         self.k, self.v = caches
         self.record_bytes = swap_record_bytes(self.k)
+        # Pinned, so the swap kernels can reach it (a host pool for a CPU
+        # device only serves tests that stand in for the device calls).
         self.host = torch.empty(max(host_slots, 1) * self.record_bytes, dtype=torch.uint8,
-                                pin_memory=True)
+                                pin_memory=self.dev.type == "cuda")
         self.ws = None                   # decode workspace, grown on demand
         self.step_no = 0
         self.host_seconds = 0.0          # time in scheduler / block-manager calls
@@ -84,7 +86,7 @@ class DecodeEngine:
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev)
 
     def _event(self):
-        if not self.timing:
+        if not self.timing or self.dev.type != "cuda":
             return None
         e = torch.cuda.Event(enable_timing=True)
         e.record()
@@ -136,8 +138,9 @@ class DecodeEngine:
         e_d0 = self._event()
         outs = self._decode(plan, q_rows)
         e_d1 = self._event()
-        torch.cuda.current_stream().synchronize()
-        if self.timing:
+        if self.dev.type == "cuda":
+            torch.cuda.current_stream().synchronize()
+        if e_p0 is not None:
             self.prompt_ms += e_p0.elapsed_time(e_p1)
             self.decode_ms += e_d0.elapsed_time(e_d1)
         owed = plan["batch"].tolist() + prompt_ids
