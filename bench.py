@@ -287,9 +287,15 @@ class DecodeBench:
         return (buf[:o1].view(torch.int64), buf[o3:].view(torch.int32).view(B, mb),
                 buf[o1:o2].view(torch.int32), buf[o2:o3].view(torch.int32).view(B, 2))
 
-    def step(self, s, ev_pairs=None, ev_start=None):
+    def step(self, s, ev_pairs=None, ev_start=None, ev_end=None):
         """One step; ev_start, if given, is recorded after the host work,
-        right before the step's first GPU operation (the upload)."""
+        right before the step's first GPU operation (the upload), and ev_end
+        after its last.  ev_pairs[layer] brackets that layer's pa_decode; the
+        last layer's end is ev_end itself when given.  Every event record
+        leaves the GPU idle for a few microseconds (the next dispatch waits
+        for the marker), so the step records only these, and the staging
+        buffer's reuse event goes at the end of the step rather than between
+        the upload and the first kernel."""
         pkv, p = self.pkv, self.pin[s % 2]
         p["ev"].synchronize()                 # its previous upload has run
         h0 = time.perf_counter()
@@ -308,7 +314,6 @@ class DecodeBench:
         if ev_start is not None:
             ev_start.record()
         self.d_stage[:used].copy_(p["buf"][:used], non_blocking=True)
-        p["ev"].record()
         if len(pairs):
             pkv.pa_copy_blocks(self.k_layers, self.v_layers, self.d_pairs[:len(pairs)])
         max_len = int(self.lens0.max()) + s
@@ -320,8 +325,11 @@ class DecodeBench:
             pkv.pa_decode(self.q[layer], self.k_layers[layer], self.v_layers[layer], self.d_tab,
                           self.d_len, max_len, partition_tokens=self.partition,
                           out=self.out[layer], workspace=self.ws)
-            if ev_pairs is not None:
+            if ev_pairs is not None and not (layer == self.L - 1 and ev_end is not None):
                 ev_pairs[layer][1].record()
+        if ev_end is not None:
+            ev_end.record()
+        p["ev"].record()                      # the staging buffer may be refilled after this
 
     def run(self):
         """Time the steps.  Working sets under 4 GiB per step could be served
@@ -337,20 +345,21 @@ class DecodeBench:
             self.step(s)
         torch.cuda.synchronize()
         T = torch.cuda.Event
-        # Per-launch events (two per layer) cost a few microseconds of GPU
-        # time each when timed alone, so they ride on every fourth timed
-        # step only (all of its layers).
-        timed = [i for i in range(args.steps) if i % 4 == 3] or [args.steps - 1]
-        events = {i: [(T(enable_timing=True), T(enable_timing=True)) for _ in range(self.L)]
-                  for i in timed}
+        # Per-launch events (two per layer) leave the GPU idle a few
+        # microseconds each, so they ride on a few evenly spaced timed steps
+        # only (all of their layers): about 64 launches, and at most every
+        # fourth step.
+        stride = max(4, args.steps // -(-64 // self.L))
+        timed = [i for i in range(args.steps) if i % stride == stride - 1] or [args.steps - 1]
         step_ev = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
+        events = {i: [(T(enable_timing=True), T(enable_timing=True)) for _ in range(self.L - 1)] +
+                     [(T(enable_timing=True), step_ev[i][1])] for i in timed}
         self.host_s.clear()
         t0 = time.perf_counter()
         for i in range(args.steps):
             if small:
                 scratch.fill_(i & 0xff)
-            self.step(args.warmup + i, events.get(i), step_ev[i][0])
-            step_ev[i][1].record()
+            self.step(args.warmup + i, events.get(i), *step_ev[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         # The device's tables and lengths (uploaded only when changed) must
