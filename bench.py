@@ -9,9 +9,9 @@ permutation).  One step is one pass of the whole hot path:
   host   pa_bm_append_slots (one new token per sequence: slot, table growth)
          pa_bm_export_batch into a pinned staging buffer, one async upload
          (the block tables only when they changed)
-  device for each layer: pa_write_kv (the new token's K/V), pa_decode
-         (split-KV phase 1 + reduce); pa_copy_blocks when appends report
-         copy-on-write pairs (none in this workload)
+  device pa_copy_blocks when appends report copy-on-write pairs (none in
+         this workload), then for each layer pa_write_kv (the new token's
+         K/V) and pa_decode (split-KV phase 1 + reduce)
 
 Sequences grow by one token per step, as in real decoding; the KV bytes of
 every step are counted exactly.  The metric is achieved KV GB/s (valid
