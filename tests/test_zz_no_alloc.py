@@ -80,3 +80,45 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
                               partition_tokens=512)
     torch.cuda.synchronize()
     assert not out.any()                           # nothing was launched
+
+
+def test_noalloc_replays_from_a_captured_graph():
+    """The callers this entry point is for: a decode captured into a HIP
+    graph (nothing may allocate during capture) and replayed with new
+    queries.  Between replays the program does its own eager work (a new
+    query, a NaN fill of the output) and synchronizes; every replay must
+    equal an eager pa_decode with a workspace on the same inputs."""
+    d, hq, hkv, pt = 128, 32, 8, 512
+    rng = np.random.default_rng(9)
+    lens = [int(x) for x in rng.integers(1, 5000, size=24)]
+    q, k, v, tables = _case(lens, hq, hkv, d, "bf16", seed=80)
+    d_tab = torch.from_numpy(tables).cuda()
+    d_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    max_len = max(lens)
+    need = pkv.pa_decode_workspace_bytes(len(lens), hq, d, max_len, pt)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty((len(lens), hq, d), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                  # warm-up outside the capture
+        pkv.pa_decode_noalloc(q, k, v, d_tab, d_len, max_len, out, partition_tokens=pt)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("noalloc graph capture")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pkv.pa_decode_noalloc(q, k, v, d_tab, d_len, max_len, out, partition_tokens=pt)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say("noalloc graph replay", rep)
+        q.copy_(workloads.normal_torch(tuple(q.shape), 90 + rep, q.dtype, "cuda"))
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_out = pkv.pa_decode(q, k, v, d_tab, d_len, max_len, partition_tokens=pt, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.int32), ref_out.cpu().numpy().view(np.int32)), rep
+        if rep == 3:
+            want = oracle.ref_decode(host_f32(q), host_f32(k), host_f32(v), tables, lens)
+            assert np.abs(got - want).max() <= TOL["bf16"]
