@@ -6,7 +6,8 @@ instead of a caller's workspace.  Two calls in a row, the second with a
 smaller batch, must give the same output as pa_decode with a workspace on
 the same inputs (the same kernels: bit-identical), and both within the
 attention tolerance of the float64 oracle; a size whose partials exceed
-the scratch is rejected before anything is launched.
+the scratch is rejected before anything is launched; and the call captured
+into a HIP graph replays correctly with new queries.
 """
 
 import numpy as np
