@@ -447,7 +447,7 @@ def run_fork_cow(args, torch, pkv, workloads):
     vn = workloads.normal_torch((B, H, D), 43, torch.float16, dev)
     q = workloads.normal_torch((B, cfg["hq"], D), 44, torch.float16, dev)
     out = torch.empty((B, cfg["hq"], D), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(pkv.pa_decode_workspace_bytes(B, cfg["hq"], D, L0 + 1 + S, 512), 1),
+    ws = torch.empty(max(pkv.pa_decode_shared_workspace_bytes(B, cfg["hq"], D, L0 + 1 + S, 512), 1),
                      dtype=torch.uint8, device=dev)
     tab_h = torch.empty((B, max_blocks), dtype=torch.int32).pin_memory()
     len_h = torch.empty(B, dtype=torch.int32).pin_memory()
@@ -837,7 +837,7 @@ def run_beam(args, torch, pkv, workloads):
     q = workloads.normal_torch((B, cfg["hq"], D), 74, torch.float16, dev)
     out = torch.empty((B, cfg["hq"], D), dtype=torch.float32, device=dev)
     maxlen = int(lens0.max()) + args.warmup + args.steps + 1
-    ws = torch.empty(max(pkv.pa_decode_workspace_bytes(B, cfg["hq"], D, maxlen, 512), 1),
+    ws = torch.empty(max(pkv.pa_decode_shared_workspace_bytes(B, cfg["hq"], D, maxlen, 512), 1),
                      dtype=torch.uint8, device=dev)
     width = -(-maxlen // bs)
     T = torch.cuda.Event
@@ -919,9 +919,9 @@ def run_beam(args, torch, pkv, workloads):
     for pt in (512, 128):
         sg, groups, mx, mp = pkv.pa_shared_plan(tables, lens, bs, pt, cfg["hq"] // H)
         d_sg, d_gr = torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev)
-        ws2 = torch.empty(max(pkv.pa_decode_workspace_bytes(B, cfg["hq"], D, mlen, pt), 1),
+        ws2 = torch.empty(max(pkv.pa_decode_shared_workspace_bytes(B, cfg["hq"], D, mlen, pt), 1),
                           dtype=torch.uint8, device=dev)
-        cmp[f"shared_pt{pt}"] = {"groups": len(groups), "shared_partitions": int(groups[:, 0].sum()),
+        cmp[f"shared_pt{pt}"] = {"groups": len(groups), "shared_blocks": int(groups[:, 0].sum()),
                                  "ms": timed(lambda: pkv.pa_decode_shared(
                                      q, k, v, d_tab, d_len, mlen, d_sg, d_gr, mx, mp,
                                      partition_tokens=pt, out=out, workspace=ws2))}

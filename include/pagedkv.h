@@ -486,44 +486,47 @@ int pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void
  * and copy-on-write) and prefix-cache hits share full blocks ([P06] spec
  * overview), so in a batch several block tables can start with the same
  * physical blocks.  pa_decode reads such a block once per sequence;
- * pa_decode_shared reads the shared leading partitions of a group of
- * sequences once for the whole group, then each member's own partitions.
- * The output is the attention pa_decode defines (same formula, same
- * float32 accumulation; partial results are merged in a different order).
+ * pa_decode_shared reads the shared leading blocks of a group of sequences
+ * once for the whole group, then each member's own blocks.  The output is
+ * the attention pa_decode defines (same formula, same float32
+ * accumulation; partial results are merged in a different order).
  *
  * A plan is two int32 arrays:
  *   seq_group [B]: the group of sequence b, or -1;
- *   groups [n_groups][PA_SHARED_ROW]: row = {P, m_0, ..., m_15}: P shared
- *     split-KV partitions (P * partition_tokens leading tokens), then the
- *     batch indices of the members, -1 in unused slots.  At most
- *     PA_SHARED_MAX_MEMBERS / (num_q_heads / num_kv_heads) slots are used.
- * Sequence b is a member of group g when seq_group[b] == g, b is listed in
- * row g, 1 <= P <= max_shared_parts, and b's blocks before its last one
- * cover at least the P partitions (P * partition_tokens / block_size <
- * number of blocks of b).  A member's first P partitions are computed from
- * the table row of m_0 (which need not be a member itself); the rest of
- * its partitions, and every sequence that is not a member, as in
- * pa_decode.  A member whose table differs from row m_0 inside those
- * partitions, or a group whose m_0 is outside [0, B), gives NaN output
- * rows for those members (nothing is read out of range). */
+ *   groups [n_groups][PA_SHARED_ROW]: row = {S, m_0, ..., m_15}: S shared
+ *     leading blocks (S * block_size tokens), then the batch indices of the
+ *     members, -1 in unused slots.  At most PA_SHARED_MAX_MEMBERS /
+ *     (num_q_heads / num_kv_heads) slots are used.
+ * The shared blocks are cut into ceil(S * block_size / partition_tokens)
+ * shared partitions from block 0 (the last may be short).  Sequence b is a
+ * member of group g when seq_group[b] == g, b is listed in row g, S >= 1,
+ * the shared partitions number at most max_shared_parts, and S is below
+ * b's block count (its last block is never shared).  A member's first S
+ * blocks are read from the table row of m_0 (which need not be a member
+ * itself); its other blocks, cut into partitions from block S on, and every
+ * sequence that is not a member, as in pa_decode.  A member whose table
+ * differs from row m_0 inside the shared blocks, or a group whose m_0 is
+ * outside [0, B), gives NaN output rows for those members (nothing is read
+ * out of range). */
 #define PA_SHARED_MAX_MEMBERS 16
 #define PA_SHARED_ROW (1 + PA_SHARED_MAX_MEMBERS)
 
 /* A plan for pa_decode_shared from the host copies of the batch's tables
- * and lengths.  Candidates are sequences with at least one whole partition
- * of full blocks before their last block.  They are bucketed by first
- * block id and sorted by table row; a bucket is cut greedily into groups of
- * at most PA_SHARED_MAX_MEMBERS / query_group sequences, a sequence joining
- * the open group while (members - 1) x shared partitions does not drop; a
- * group's P is the common leading run of its rows, in whole partitions.
+ * and lengths.  Candidates are sequences with at least 2 full blocks
+ * before their last block.  They are bucketed by first block id and sorted
+ * by table row; a bucket is cut greedily into groups of at most
+ * PA_SHARED_MAX_MEMBERS / query_group sequences, a sequence joining the
+ * open group while (members - 1) x shared blocks does not drop; a group's
+ * S is the common leading run of its rows (at least 2 blocks).
  *   tables: host int32 [B][max_blocks]; lens: host int32 [B].
  *   partition_tokens: the value pa_decode_shared will get (> 0, multiple of
  *     block_size); query_group: num_q_heads / num_kv_heads (1, 2, 4, 8).
  *   seq_group_out: host int32 [B].
  *   groups_out: host int32 [B / 2][PA_SHARED_ROW] (unused if B < 2).
- *   *n_groups_out: groups written; *max_parts_out: largest P (0 if none);
- *   *max_private_parts_out: the most partitions any sequence has outside
- *     its group's P (a sequence in no group: all of its partitions).
+ *   *n_groups_out: groups written; *max_parts_out: the most shared
+ *     partitions of any group (0 if none);
+ *   *max_private_parts_out: the most partitions any sequence has after its
+ *     group's shared blocks (a sequence in no group: all of its partitions).
  * Every group it writes satisfies the membership rule above for all its
  * members. */
 int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t B,
@@ -536,15 +539,20 @@ int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const int32_t* len
  *   seq_group: device int32 [B]; groups: device int32
  *     [n_groups][PA_SHARED_ROW]; both may be NULL when n_groups == 0, which
  *     makes the call exactly pa_decode.
- *   max_shared_parts: host-side bound on every group's P (sizes the grid;
- *     a group with a larger P has no members).
+ *   max_shared_parts: host-side bound on every group's shared partitions
+ *     (sizes the grid; a group with more has no members).
  *   max_private_parts: host-side bound on the partitions any sequence has
- *     outside its group's P (sizes the private grid; 0 = no bound, the
- *     grid then covers max_context_len).  A sequence with more gets NaN
- *     output rows.
+ *     after its group's shared blocks (sizes the private grid; 0 = no
+ *     bound, the grid then covers max_context_len).  A sequence with more
+ *     gets NaN output rows.
  * With n_groups > 0: dtype F16 or BF16 (the shared partitions run on the
- * matrix cores with up to 16 query columns: members x query group), and
- * partition_tokens > 0.  The workspace is the one pa_decode needs. */
+ * matrix cores with up to 16 query columns: members x query group),
+ * partition_tokens > 0, and, when max_shared_parts > 0, a workspace of
+ * pa_decode_shared_workspace_bytes(...) bytes (a member's partitions can
+ * number one more than the plain split).  Otherwise the workspace is the
+ * one pa_decode needs. */
+size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t partition_tokens);
 int pa_decode_shared(float* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, int32_t max_context_len, int32_t B,

@@ -76,6 +76,7 @@ SIGNATURES = {
     "pa_shared_plan": (ctypes.c_int, [P_i32, c_i32, P_i32, c_i32, c_i32, c_i32, c_i32, P_i32,
                                       P_i32, P_i32, P_i32, P_i32]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_shared_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz, c_vp]),
     "pa_stream_read": (ctypes.c_int, [c_vp, ctypes.c_uint64, c_i32, c_vp, c_vp]),

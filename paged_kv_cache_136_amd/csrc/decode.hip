@@ -81,7 +81,7 @@ struct DecodeArgs {
   int32_t hq, hkv;
   int32_t num_blocks;
   int32_t part_blocks;   // blocks per partition
-  int32_t num_parts;     // P = partitions of max_len
+  int32_t num_parts;     // workspace slots per (sequence, head): the split of max_len, +1 with a plan
   float scale_log2;      // scale * log2(e)
   // Shared-prefix plan (seq_group == nullptr: none).
   const int32_t* seq_group;  // [B]
@@ -90,7 +90,7 @@ struct DecodeArgs {
   int32_t max_shared_parts;
   int32_t batch;             // B
   int32_t qgroup;            // query heads per KV head
-  int32_t grid_parts;        // z extent of the private grid (<= num_parts)
+  int32_t grid_parts;        // z extent of the private grid (<= the split of max_len)
 };
 
 __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
@@ -121,7 +121,8 @@ __device__ __forceinline__ int rotate_head(int g, int hkv, uint32_t rot) {
 
 // The scalar reads a private-grid workgroup starts with, issued together
 // so the first K/V loads wait for one round trip: the sequence's length,
-// its first table entry (for the head rotation) and the table entries of
+// its shared-prefix group (with a plan), its first table entry (for the
+// head rotation) and the table entries of
 // the wave's first NBUF blocks of partition z (used when there is no
 // shared-prefix plan, whose partitions start elsewhere).  Every index is
 // clamped into the row and no read sits behind a branch; a table of width
@@ -133,6 +134,7 @@ struct Prologue {
   int32_t n;
   int32_t spec[NBUF];
   uint32_t rot;
+  int32_t gi;            // the sequence's plan group (-1 without a plan)
 };
 
 // z: the partition the ids are read for; rot_z: the one the rotation adds
@@ -145,6 +147,7 @@ __device__ __forceinline__ Prologue<NBUF> prologue(const DecodeArgs& a, int b, i
   const int last_idx = max(a.max_blocks, 1) - 1;
   const uint32_t e0 = static_cast<uint32_t>(p.trow[0]);
   p.n = a.lens[b];
+  p.gi = a.seq_group != nullptr ? a.seq_group[b] : -1;
 #pragma unroll
   for (int sl = 0; sl < NBUF; ++sl)
     p.spec[sl] = p.trow[min(z * a.part_blocks + wv + sl * WAVES, last_idx)];
@@ -164,33 +167,50 @@ __device__ __forceinline__ size_t ws_row(const DecodeArgs& a, int b, int h, int 
   return ((static_cast<size_t>(b) * a.hkv + g) * a.num_parts + part) * a.qgroup + c;
 }
 
-__device__ __forceinline__ int num_parts_of(int n, int part_blocks) {
-  int nb = (n + kBlock - 1) / kBlock;
-  return nb == 0 ? 1 : (nb + part_blocks - 1) / part_blocks;
+// Partitions of S shared blocks: the shared kernel cuts them at the
+// partition size from block 0, the last one possibly short.
+__device__ __forceinline__ int shared_parts_of(int S, int part_blocks) {
+  return (S + part_blocks - 1) / part_blocks;
 }
 
-// Shared partitions P of a group row when P is in range and leaves at least
-// one private block to a sequence of nblk blocks, else 0.  Both the shared
-// and the private kernels decide membership through this one rule, so every
-// partition of every sequence is computed by exactly one of them.
-__device__ __forceinline__ int shared_parts_for(const DecodeArgs& a, const int32_t* row, int nblk) {
-  const int P = row[0];
-  const bool ok = P >= 1 && P <= a.max_shared_parts &&
-                  static_cast<int64_t>(P) * a.part_blocks < nblk;
-  return ok ? P : 0;
+// Shared leading blocks S of a group row when S is in range and leaves at
+// least one private block to a sequence of nblk blocks, else 0.  Both the
+// shared and the private kernels decide membership through this one rule,
+// so every block of every sequence is read by exactly one of them.
+__device__ __forceinline__ int shared_blocks_for(const DecodeArgs& a, const int32_t* row, int nblk) {
+  const int S = row[0];
+  const bool ok = S >= 1 && S < nblk && shared_parts_of(S, a.part_blocks) <= a.max_shared_parts;
+  return ok ? S : 0;
 }
 
-// Partitions of sequence b computed by the shared kernel (0: not a member).
-// nblk is b's block count, 0 for an invalid length.
-__device__ __forceinline__ int shared_start(const DecodeArgs& a, int b, int nblk) {
-  if (a.seq_group == nullptr) return 0;
-  const int gi = a.seq_group[b];
-  if (gi < 0 || gi >= a.n_groups) return 0;
+// Blocks of sequence b read by the shared kernel (0: not a member).  gi is
+// seq_group[b] (read by the caller, so it can travel with its other first
+// reads); nblk is b's block count, 0 for an invalid length.
+__device__ __forceinline__ int shared_start(const DecodeArgs& a, int b, int gi, int nblk) {
+  if (a.seq_group == nullptr || gi < 0 || gi >= a.n_groups) return 0;
   const int32_t* row = a.groups + static_cast<size_t>(gi) * PA_SHARED_ROW;
   const int slots = PA_SHARED_MAX_MEMBERS / a.qgroup;
   bool listed = false;
   for (int sl = 0; sl < slots; ++sl) listed |= row[1 + sl] == b;
-  return listed ? shared_parts_for(a, row, nblk) : 0;
+  return listed ? shared_blocks_for(a, row, nblk) : 0;
+}
+
+// Partition geometry of sequence b (nblk blocks, 0 for an invalid length).
+// A member's S shared blocks fill workspace slots 0 .. Ps-1 (shared
+// kernel); its private partitions start at block S, private partition i
+// covering blocks S + i*pb .. and filling slot Ps + i.  A sequence in no
+// group has S = Ps = 0: partition i covers blocks i*pb .. (slot i).
+// `total` counts every slot (1 for an empty or invalid sequence, which
+// phase 1 answers directly); with S not a multiple of pb it can exceed
+// the partitions of the plain split by one.
+struct SeqParts {
+  int S, Ps, total;
+};
+__device__ __forceinline__ SeqParts seq_parts(const DecodeArgs& a, int b, int gi, int nblk) {
+  const int S = shared_start(a, b, gi, nblk);
+  const int Ps = shared_parts_of(S, a.part_blocks);
+  const int Pp = nblk == 0 ? 1 : (nblk - S + a.part_blocks - 1) / a.part_blocks;
+  return {S, Ps, Ps + Pp};
 }
 
 // Running softmax state of one lane: every lane of a row group (the LPR
@@ -286,10 +306,10 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   const int n = pro.n;
   const bool valid = len_valid(n, a);
   const int nblk = valid ? (n + kBlock - 1) / kBlock : 0;
-  const int nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
-  const int start = shared_start(a, b, nblk);
-  const int part = wc.z + start;
-  if (part >= nparts) return;
+  const SeqParts sp = seq_parts(a, b, pro.gi, nblk);
+  const int nparts = sp.total;
+  const int slot = sp.Ps + wc.z;           // this private partition's workspace slot
+  if (slot >= nparts) return;
   const int h0 = g * G;
 
   // Degenerate rows: empty sequence -> 0, invalid length -> NaN.
@@ -324,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   const uint32_t block_bytes = row_bytes * kBlock;
   const uint32_t lane_off = r * row_bytes + static_cast<uint32_t>(g * D + c * EPL) * ELEM;
 
-  const int first = part * a.part_blocks;
+  const int first = sp.S + wc.z * a.part_blocks;
   const int last = min(nblk, first + a.part_blocks);   // exclusive
   // Block ids come straight from the table with scalar loads (uniform
   // addresses, served by the scalar cache; tables are tiny and stay in L2),
@@ -333,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   // flags the sequence; its output becomes NaN after the merge.
   // A grid sized below this sequence's private partitions (a host bound
   // that was too small) leaves some uncomputed: flag it like a bad id.
-  bool bad_ids = nparts - start > static_cast<int>(gridDim.z);
+  bool bad_ids = nparts - sp.Ps > static_cast<int>(gridDim.z);
   auto check_id = [&](int32_t e) -> int {
     const bool ok = e >= 0 && e < a.num_blocks;
     bad_ids |= !ok;
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     if (nparts == 1) {
       a.out[bh * D + d] = res;
     } else {
-      const size_t bhp = ws_row(a, b, h0 + hh, part);
+      const size_t bhp = ws_row(a, b, h0 + hh, slot);
       a.ws_o[bhp * D + d] = res;
       if (d == 0) {
         a.ws_m[bhp] = bad ? 0.f : M;
@@ -522,10 +542,14 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   int p0, pend;                           // the group's partitions: [p0, pend)
   if constexpr (SHARED) {
     const int32_t* row = a.groups + static_cast<size_t>(b) * PA_SHARED_ROW;
-    const int P = row[0];
+    const int S = row[0];                 // shared blocks
     part = zp;
     p0 = wc.z * kWaves;
-    if (P < 1 || P > a.max_shared_parts || p0 >= P) return;   // uniform over the workgroup
+    // uniform over the workgroup (S is checked before its partitions are
+    // counted, so a wild value cannot overflow them)
+    if (S < 1 || S > static_cast<int64_t>(a.max_shared_parts) * a.part_blocks) return;
+    const int P = shared_parts_of(S, a.part_blocks);
+    if (p0 >= P) return;
     pend = min(P, p0 + kWaves);
     active = part < P;
     const int slots = PA_SHARED_MAX_MEMBERS / a.qgroup;
@@ -536,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       if (m < 0 || m >= a.batch || a.seq_group[m] != b) return -1;
       const int nm = a.lens[m];
       if (!len_valid(nm, a)) return -1;
-      return shared_parts_for(a, row, (nm + kBlock - 1) / kBlock) > 0 ? m : -1;
+      return shared_blocks_for(a, row, (nm + kBlock - 1) / kBlock) > 0 ? m : -1;
     };
     col_seq = member(t / a.qgroup);
     chk_seq = member(t);
@@ -546,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     trow = a.tables + static_cast<size_t>(src_ok ? lead : 0) * a.max_blocks;
     first = part * a.part_blocks;
     // within max_blocks: a member exists
-    last = src_ok && active ? first + a.part_blocks : first;
+    last = src_ok && active ? min(first + a.part_blocks, S) : first;
     n = last * kBlock;                               // shared blocks are full
     nblk = last;
     nparts = 0;
@@ -555,14 +579,16 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     const bool valid = len_valid(nn, a);
     n = nn;
     nblk = valid ? (n + kBlock - 1) / kBlock : 0;
-    nparts = valid ? num_parts_of(n, a.part_blocks) : 1;
-    const int start = shared_start(a, b, nblk);
-    part = zp + start;
-    p0 = wc.z * kWaves + start;
+    const SeqParts sp = seq_parts(a, b, pro.gi, nblk);
+    nparts = sp.total;
+    // wave w streams private partition zp (slot Ps + zp); the workgroup's
+    // merged result goes to its first slot p0
+    part = sp.Ps + zp;
+    p0 = sp.Ps + wc.z * kWaves;
     if (p0 >= nparts) return;             // uniform over the workgroup
     pend = min(nparts, p0 + kWaves);
     active = part < nparts;
-    short_grid = nparts - start > static_cast<int>(gridDim.z) * kWaves;
+    short_grid = nparts - sp.Ps > static_cast<int>(gridDim.z) * kWaves;
     if (!valid || n == 0) {               // uniform: nparts == 1, p0 == 0
       const float fill = valid ? 0.f : __builtin_nanf("");
       for (int i = threadIdx.x; i < G * D; i += kThreads)
@@ -570,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       return;
     }
     trow = pro.trow;
-    first = part * a.part_blocks;
+    first = sp.S + zp * a.part_blocks;
     last = active ? min(nblk, first + a.part_blocks) : first;
   }
 
@@ -880,7 +906,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = a.lens[b];
   if (!len_valid(n, a)) return;
-  const int nparts = num_parts_of(n, a.part_blocks);
+  const int gi = a.seq_group != nullptr ? a.seq_group[b] : -1;
+  const int nparts = seq_parts(a, b, gi, (n + kBlock - 1) / kBlock).total;
   if (nparts <= 1) return;                 // phase 1 wrote the output
   const size_t bh = static_cast<size_t>(b) * a.hq + h;
   // Partition p's row is row0 + p * G (rows are [B][Hkv][P][G]).
@@ -918,7 +945,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_wave(DecodeArgs a) {
   if (h >= a.hq) return;
   const int n = a.lens[b];
   if (!len_valid(n, a)) return;
-  const int nparts = num_parts_of(n, a.part_blocks);
+  const int gi = a.seq_group != nullptr ? a.seq_group[b] : -1;
+  const int nparts = seq_parts(a, b, gi, (n + kBlock - 1) / kBlock).total;
   if (nparts <= 1) return;                 // phase 1 wrote the output
   const size_t row0 = ws_row(a, b, h, 0);
   const PairScale ps = pair_scale(a, row0, nparts, lane);
@@ -998,6 +1026,12 @@ WsLayout ws_layout(int32_t B, int32_t hq, int32_t D, int32_t P) {
   return w;
 }
 
+// Partitions of the plain split of max_context_len.
+int32_t plain_parts(int32_t max_context_len, int32_t part_blocks) {
+  const int32_t nb = (max_context_len + kBlock - 1) / kBlock;
+  return nb == 0 ? 1 : (nb + part_blocks - 1) / part_blocks;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -1009,9 +1043,17 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int3
     return 0;
   const int32_t pb = part_blocks_for(max_context_len, partition_tokens);
   if (pb <= 0) return 0;
-  const int32_t nb = (max_context_len + kBlock - 1) / kBlock;
-  const int32_t P = nb == 0 ? 1 : (nb + pb - 1) / pb;
-  return ws_layout(B, num_q_heads, head_dim, P).total;
+  return ws_layout(B, num_q_heads, head_dim, plain_parts(max_context_len, pb)).total;
+}
+
+// With a shared-prefix plan a member's shared blocks need not end on a
+// partition boundary: its slots can number one more than the plain split.
+extern "C" size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_dim,
+                                                   int32_t max_context_len, int32_t partition_tokens) {
+  if (B <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 || partition_tokens <= 0)
+    return 0;
+  const int32_t pb = part_blocks_for(max_context_len, partition_tokens);
+  return ws_layout(B, num_q_heads, head_dim, plain_parts(max_context_len, pb) + 1).total;
 }
 
 // Split-KV scratch of pa_decode_noalloc: the partition results live in this
@@ -1090,12 +1132,25 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
   // Grid limits: KV heads on x, sequences on y (<= 65535), partitions on z.
   if (B > 65535) return err_(PA_ERR_UNSUPPORTED, "more than 65535 sequences");
 
+  if (n_groups > 0) {
+    if (!seq_group || !groups) return err_(PA_ERR_INVALID, "null plan pointer");
+    if (dtype == PA_DTYPE_F32)
+      return err_(PA_ERR_UNSUPPORTED, "a shared-prefix plan needs F16 or BF16 K/V");
+    if (partition_tokens == 0)
+      return err_(PA_ERR_INVALID, "a shared-prefix plan needs partition_tokens > 0");
+    if (n_groups > 65535 || max_shared_parts > 65535)
+      return err_(PA_ERR_UNSUPPORTED, "more than 65535 plan groups or shared partitions");
+  }
+  // With a plan in force a member's slots can exceed the plain split by
+  // one (its shared blocks need not end on a partition boundary).
+  const bool plan = n_groups > 0 && max_shared_parts > 0;
+
   DecodeArgs a{};
   a.part_blocks = part_blocks_for(max_context_len, partition_tokens);
-  const int32_t nb = (max_context_len + kBlock - 1) / kBlock;
-  a.num_parts = nb == 0 ? 1 : (nb + a.part_blocks - 1) / a.part_blocks;
-  if (a.num_parts > 65535)
+  const int32_t P = plain_parts(max_context_len, a.part_blocks);
+  if (P > 65535)
     return err_(PA_ERR_UNSUPPORTED, "more than 65535 partitions; use larger partitions");
+  a.num_parts = P + (plan ? 1 : 0);        // workspace slots per (sequence, head)
   const WsLayout wl = ws_layout(B, num_q_heads, head_dim, a.num_parts);
   if (use_scratch && wl.total > 0) {
     if (wl.total > kScratchBytes)
@@ -1132,22 +1187,13 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
   a.scale_log2 = scale * kLog2e;
   a.batch = B;
   a.qgroup = group;
-  a.grid_parts = a.num_parts;
-  if (n_groups > 0) {
-    if (!seq_group || !groups) return err_(PA_ERR_INVALID, "null plan pointer");
-    if (dtype == PA_DTYPE_F32)
-      return err_(PA_ERR_UNSUPPORTED, "a shared-prefix plan needs F16 or BF16 K/V");
-    if (partition_tokens == 0)
-      return err_(PA_ERR_INVALID, "a shared-prefix plan needs partition_tokens > 0");
-    if (n_groups > 65535 || max_shared_parts > 65535)
-      return err_(PA_ERR_UNSUPPORTED, "more than 65535 plan groups or shared partitions");
-    if (max_shared_parts > 0) {
-      a.seq_group = seq_group;
-      a.groups = groups;
-      a.n_groups = n_groups;
-      a.max_shared_parts = max_shared_parts;
-      if (max_private_parts > 0) a.grid_parts = std::min(a.num_parts, max_private_parts);
-    }
+  a.grid_parts = P;                        // private partitions of any sequence <= P
+  if (plan) {
+    a.seq_group = seq_group;
+    a.groups = groups;
+    a.n_groups = n_groups;
+    a.max_shared_parts = max_shared_parts;
+    if (max_private_parts > 0) a.grid_parts = std::min(P, max_private_parts);
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);

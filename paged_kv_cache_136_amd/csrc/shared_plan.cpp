@@ -6,18 +6,19 @@
 // copies only a shared, partly filled block it writes into) and prefix-cache
 // hits share full blocks ("P06 · BlockManager" spec overview).  Plain decode
 // reads a shared block once per sequence that holds it; pa_decode_shared
-// reads the shared partitions of a group once for all its members.
+// reads the shared leading blocks of a group once for all its members.
 //
 // Grouping (a heuristic: any plan that satisfies the rules in the header is
-// correct, this one aims at many members times many shared partitions):
-//   * a sequence is a candidate when at least one whole partition of full
-//     blocks precedes its last block (the last block always stays private);
+// correct, this one aims at many members times many shared blocks):
+//   * a sequence is a candidate when at least kMinShared full blocks
+//     precede its last block (the last block always stays private);
 //   * candidates are bucketed by their first block id and sorted
 //     lexicographically by table row, so rows with long common prefixes are
 //     adjacent and a run's common prefix is that of its first and last row;
 //   * runs are cut greedily: a row joins the open group while the group's
-//     saving, (members - 1) x shared partitions, does not drop, up to
-//     16 / query_group members.
+//     saving, (members - 1) x shared blocks, does not drop, up to
+//     16 / query_group members; a group needs at least two members and
+//     kMinShared shared blocks.
 #include <algorithm>
 #include <numeric>
 #include <unordered_map>
@@ -29,6 +30,10 @@
 using pkv::fail;
 
 namespace {
+
+// Fewest shared blocks worth a group: below this the group's extra partial
+// result per member costs about what its shared reads save.
+constexpr int32_t kMinShared = 2;
 
 struct Cand {
   int32_t seq;
@@ -77,7 +82,7 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
     if (n <= 0 || n > static_cast<int64_t>(max_blocks) * block_size) continue;
     const int32_t nblk = (n + block_size - 1) / block_size;
     const int32_t cap = nblk - 1;          // every block before the last is full
-    if (cap < pb) continue;
+    if (cap < kMinShared) continue;
     const int32_t first = row(b)[0];
     auto it = buckets.find(first);
     if (it == buckets.end()) {
@@ -88,15 +93,15 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
   }
 
   int32_t ng = 0, max_parts = 0;
-  auto emit = [&](const std::vector<Cand>& c, size_t lo, size_t hi, int32_t parts) {
+  auto emit = [&](const std::vector<Cand>& c, size_t lo, size_t hi, int32_t shared) {
     int32_t* g = groups_out + static_cast<size_t>(ng) * PA_SHARED_ROW;
-    g[0] = parts;
+    g[0] = shared;
     for (int32_t s = 0; s < PA_SHARED_MAX_MEMBERS; ++s) g[1 + s] = -1;
     for (size_t i = lo; i < hi; ++i) {
       g[1 + (i - lo)] = c[i].seq;
       seq_group_out[c[i].seq] = ng;
     }
-    max_parts = std::max(max_parts, parts);
+    max_parts = std::max(max_parts, (shared + pb - 1) / pb);
     ++ng;
   };
   for (int32_t key : order) {
@@ -110,30 +115,31 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
     while (lo < c.size()) {
       // Grow [lo, hi) while the saving does not drop.
       size_t hi = lo + 1;
-      int32_t parts = c[lo].cap / pb;
+      int32_t shared = c[lo].cap;
       while (hi < c.size() && static_cast<int32_t>(hi - lo) < cap_members) {
-        const int32_t p2 = std::min(parts, lcp(c[lo], c[hi]) / pb);
-        const int64_t old_save = static_cast<int64_t>(hi - lo - 1) * parts;
-        const int64_t new_save = static_cast<int64_t>(hi - lo) * p2;
-        if (p2 < 1 || new_save < old_save) break;
-        parts = p2;
+        const int32_t s2 = std::min(shared, lcp(c[lo], c[hi]));
+        const int64_t old_save = static_cast<int64_t>(hi - lo - 1) * shared;
+        const int64_t new_save = static_cast<int64_t>(hi - lo) * s2;
+        if (s2 < kMinShared || new_save < old_save) break;
+        shared = s2;
         ++hi;
       }
-      if (hi - lo >= 2) emit(c, lo, hi, parts);
+      if (hi - lo >= 2) emit(c, lo, hi, shared);
       lo = hi;
     }
   }
-  // Private partitions left to each sequence (every partition when it is
-  // in no group; one for an empty or invalid length, as in decode).
+  // Private partitions left to each sequence: those of the blocks after its
+  // group's shared ones (every partition when it is in no group; one for an
+  // empty or invalid length, as in decode).
   int32_t max_private = 0;
   for (int32_t b = 0; b < B; ++b) {
     const int32_t n = lens[b];
     const bool ok = n > 0 && n <= static_cast<int64_t>(max_blocks) * block_size;
     const int32_t nblk = ok ? (n + block_size - 1) / block_size : 0;
-    const int32_t nparts = nblk == 0 ? 1 : (nblk + pb - 1) / pb;
     const int32_t gi = seq_group_out[b];
     const int32_t shared = gi >= 0 ? groups_out[static_cast<size_t>(gi) * PA_SHARED_ROW] : 0;
-    max_private = std::max(max_private, nparts - shared);
+    const int32_t priv = nblk == 0 ? 1 : (nblk - shared + pb - 1) / pb;
+    max_private = std::max(max_private, priv);
   }
   *n_groups_out = ng;
   *max_parts_out = max_parts;

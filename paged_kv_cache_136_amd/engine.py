@@ -18,7 +18,11 @@ require:
   4. decode (pa_decode) of the batch, every layer; with ``shared_prefix``
      the host plans shared-prefix groups once per step (pa_shared_plan) and
      every layer decodes with pa_decode_shared, reading blocks that several
-     sequences share (a common system prompt, forks) once per group.
+     sequences share (a common system prompt, forks) once per group -- when
+     the plan saves at least ``shared_min_saving`` of the batch's block
+     reads; below that the shared pass costs more than it saves (the
+     repeated reads of a short common prefix mostly hit in L2), and the
+     step decodes with pa_decode.
 
 There is no model here: the caller supplies the K/V rows to write, the
 queries and the sampled tokens through functions, so every value the
@@ -32,9 +36,9 @@ import numpy as np
 import torch
 
 from .block_manager import BlockManager
-from .ops import (pa_copy_blocks, pa_decode, pa_decode_shared, pa_decode_workspace_bytes,
-                  pa_prefill, pa_shared_plan, pa_swap_in, pa_swap_out, pa_write_kv,
-                  swap_record_bytes)
+from .ops import (pa_copy_blocks, pa_decode, pa_decode_shared, pa_decode_shared_workspace_bytes,
+                  pa_decode_workspace_bytes, pa_prefill, pa_shared_plan, pa_swap_in, pa_swap_out,
+                  pa_write_kv, swap_record_bytes)
 from .scheduler import Scheduler
 
 
@@ -46,7 +50,7 @@ class DecodeEngine:
     def __init__(self, num_layers, num_blocks, block_size, num_kv_heads, num_q_heads, head_dim,
                  dtype, max_batch, host_slots, enable_prefix_cache=True, partition_tokens=512,
                  device="cuda", caches=None, shared_prefix=False, prompt_attention=True,
-                 timing=False):
+                 timing=False, shared_min_saving=0.25):
         self.L, self.nb, self.bs = num_layers, num_blocks, block_size
         self.hkv, self.hq, self.d, self.dtype = num_kv_heads, num_q_heads, head_dim, dtype
         self.dev = torch.device(device)
@@ -56,8 +60,9 @@ class DecodeEngine:
         if prompt_attention and dtype == torch.float32:
             raise ValueError("prompt attention (pa_prefill) needs 16-bit caches")
         self.shared_prefix = shared_prefix
+        self.shared_min_saving = shared_min_saving
         self.prompt_attention = prompt_attention
-        self.shared_groups = 0           # groups planned, summed over steps
+        self.shared_groups = 0           # groups decoded through a plan, summed over steps
         self.bm = BlockManager(num_blocks, block_size, enable_prefix_cache)
         self.sched = Scheduler(self.bm, max_batch, host_slots)
         if caches is None:
@@ -199,15 +204,19 @@ class DecodeEngine:
         if self.shared_prefix:
             sg, groups, mx, mp = pa_shared_plan(tables, lens, self.bs, self.partition_tokens,
                                                 self.hq // self.hkv)
-            self.shared_groups += len(groups)
-            if len(groups):
+            # block reads the plan saves: (members - 1) x shared blocks per group
+            saved = int(((groups[:, 1:] >= 0).sum(axis=1) - 1) @ groups[:, 0]) if len(groups) else 0
+            total = int((-(-lens.astype(np.int64) // self.bs)).sum())
+            if len(groups) and saved >= self.shared_min_saving * total:
+                self.shared_groups += len(groups)
                 splan = (torch.from_numpy(sg).to(self.dev),
                          torch.from_numpy(groups).to(self.dev), mx, mp)
         self.host_seconds += time.perf_counter() - h0
         max_len = int(lens.max())
         d_tab = torch.from_numpy(tables).to(self.dev)
         d_len = torch.from_numpy(lens).to(self.dev)
-        need = pa_decode_workspace_bytes(B, self.hq, self.d, max_len, self.partition_tokens)
+        need = (pa_decode_shared_workspace_bytes if splan is not None else pa_decode_workspace_bytes)(
+            B, self.hq, self.d, max_len, self.partition_tokens)
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.empty(2 * need, dtype=torch.uint8, device=self.dev)
         for layer in range(self.L):

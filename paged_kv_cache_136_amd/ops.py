@@ -151,13 +151,21 @@ def pa_swap_in(k_caches, v_caches, blocks, host, host_slots=None, stream=None):
     _swap(lib().pa_swap_in, list(k_caches), list(v_caches), blocks, host, host_slots, stream)
 
 
+def pa_decode_shared_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partition_tokens):
+    """Workspace bytes of pa_decode_shared with a plan (one partition slot
+    per (sequence, head) more than pa_decode's)."""
+    return lib().pa_decode_shared_workspace_bytes(B, num_q_heads, head_dim, max_context_len,
+                                                  partition_tokens)
+
+
 def pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len, partition_tokens):
     return lib().pa_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len,
                                            partition_tokens)
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 partition_tokens, out, workspace, stream, with_workspace=True):
+                 partition_tokens, out, workspace, stream, with_workspace=True,
+                 need_fn=pa_decode_workspace_bytes):
     _dev(q, k_cache, v_cache, block_tables, context_lens)
     B, hq, d = q.shape
     nb, bs, hkv, d2 = k_cache.shape
@@ -177,8 +185,7 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_le
             raise ValueError("out must be contiguous float32 [B, Hq, D] on the GPU")
     if workspace is not None:
         _check_workspace(workspace)
-    need = (pa_decode_workspace_bytes(B, hq, d, int(max_context_len), int(partition_tokens))
-            if with_workspace else 0)
+    need = need_fn(B, hq, d, int(max_context_len), int(partition_tokens)) if with_workspace else 0
     with _on(stream):
         if out is None:
             out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
@@ -248,12 +255,17 @@ def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, max_contex
                      groups, max_shared_parts, max_private_parts=0, scale=None,
                      partition_tokens=512, out=None, workspace=None, stream=None):
     """pa_decode with a shared-prefix plan: seq_group int32 [B] and groups
-    int32 [n, 17] on the GPU (from pa_shared_plan); max_shared_parts and
-    max_private_parts are the plan's host-side grid bounds (0 for the
-    latter: no bound)."""
-    out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
-                                 max_context_len, scale, partition_tokens, out, workspace, stream)
+    int32 [n, 17] on the GPU (from pa_shared_plan; row = shared blocks, then
+    the members); max_shared_parts and max_private_parts are the plan's
+    host-side grid bounds (0 for the latter: no bound).  A given workspace
+    must hold pa_decode_shared_workspace_bytes(...) bytes when the plan has
+    groups."""
     n = 0 if groups is None else groups.shape[0]
+    need_fn = (pa_decode_shared_workspace_bytes if n and int(max_shared_parts) > 0
+               else pa_decode_workspace_bytes)
+    out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                 max_context_len, scale, partition_tokens, out, workspace, stream,
+                                 need_fn=need_fn)
     if n:
         _dev(seq_group, groups)
         if (seq_group.dtype != torch.int32 or seq_group.shape != (q.shape[0],)

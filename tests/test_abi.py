@@ -66,6 +66,13 @@ def test_device_calls_validate_before_touching_the_gpu():
         ((4 * 8 * 8 * 128 * 4 + 255) // 256 * 256) + 2 * ((4 * 8 * 8 * 4 + 255) // 256 * 256))
     assert L.pa_decode_workspace_bytes(4, 8, 128, 512, 512) == 0
     assert L.pa_decode_workspace_bytes(4, 8, 128, 4096, 0) == 0
+    # with a shared-prefix plan: one slot per (sequence, head) more, also
+    # when the context fits one partition
+    assert L.pa_decode_shared_workspace_bytes(4, 8, 128, 4096, 512) == (
+        ((4 * 8 * 9 * 128 * 4 + 255) // 256 * 256) + 2 * ((4 * 8 * 9 * 4 + 255) // 256 * 256))
+    assert L.pa_decode_shared_workspace_bytes(4, 8, 128, 512, 512) == (
+        ((4 * 8 * 2 * 128 * 4 + 255) // 256 * 256) + 2 * ((4 * 8 * 2 * 4 + 255) // 256 * 256))
+    assert L.pa_decode_shared_workspace_bytes(4, 8, 128, 4096, 0) == 0
 
 
 def _aligned_host_ptr(keep, nbytes=256):

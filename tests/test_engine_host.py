@@ -81,6 +81,7 @@ def host_engine(monkeypatch):
                      ("pa_prefill", _prefill)):
         monkeypatch.setattr(engine_mod, name, fn)
     monkeypatch.setattr(engine_mod, "pa_decode_workspace_bytes", lambda *a: 0)
+    monkeypatch.setattr(engine_mod, "pa_decode_shared_workspace_bytes", lambda *a: 0)
     return engine_mod.DecodeEngine
 
 
@@ -97,7 +98,7 @@ def test_engine_device_order_on_cpu(host_engine, host, shared):
     kb, vb = [_bits(k) for k in ks], [_bits(v) for v in vs]
     eng = host_engine(L, nb, bs, hkv, hq, d, torch.float16, batch, host, True,
                       partition_tokens=16 if shared else 64, device="cpu", caches=(ks, vs),
-                      shared_prefix=shared)
+                      shared_prefix=shared, shared_min_saving=0.0)
     rbm = oracle.RefBlockManager(nb, bs, True)
     rsc = oracle.RefScheduler(rbm, batch, host)
     hrec = np.zeros((max(host, 1), L, 2, bs, hkv, d), dtype=np.int16)

@@ -97,7 +97,7 @@ def test_shared_fork_families(dtype, d, group):
     say("shared forks", dtype, d, group)
     c = Case(tables, lens, hkv * group, hkv, d, dtype, seed=31 + d + group)
     plan = c.plan(128)
-    assert len(plan[1]) == len(prompts) - 1      # the 95-token family shares no partition
+    assert len(plan[1]) == len(prompts)          # the 95-token family shares its 6 full blocks
     got, want = c.shared(plan, 128), c.want()
     assert np.isfinite(got).all()
     err = np.abs(got - want).max()
@@ -114,6 +114,22 @@ def test_shared_partition_sizes(pt):
     assert len(plan[1]) == 2
     err = np.abs(c.shared(plan, pt) - c.want()).max()
     assert err <= TOL["f16"], err
+
+
+def test_shared_inside_one_partition():
+    """Families whose whole contexts fit one 512-token partition: the plain
+    split has a single partition (pa_decode needs no workspace and no
+    reduce), but a member's shared blocks and its private block are two
+    slots, merged by the reduce."""
+    tables, lens = fork_family([100, 300, 47], 4, _extra(12, 21, 40), singles=[200, 9], seed=21)
+    assert int(lens.max()) <= 512
+    say("shared inside one partition")
+    c = Case(tables, lens, 8, 8, 128, "bf16", seed=21)
+    plan = c.plan(512)
+    assert len(plan[1]) == 3 and plan[2] == 1
+    got = c.shared(plan, 512)
+    assert np.isfinite(got).all()
+    assert np.abs(got - c.want()).max() <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype,hq,hkv", [("f16", 4, 4), ("bf16", 16, 4)])
@@ -185,12 +201,13 @@ def test_shared_source_out_of_range_gives_nan():
 
 def test_shared_plan_mistakes_fall_back_to_private():
     """Members that the rule excludes are computed privately: not pointing
-    at their group, listed twice, too few blocks, P beyond
-    max_shared_parts, P = 0, a group index past n_groups."""
+    at their group, listed twice, too few blocks, shared partitions beyond
+    max_shared_parts, S = 0, a group index past n_groups."""
     c = _family_case()
     sg, groups, mx, _ = c.plan(128)
     want = c.want()
     B = len(c.lens)
+    pb = 128 // BS
     cases = {}
     s1 = sg.copy(); s1[_members(groups, 0)[1]] = -1
     cases["not pointing at its group"] = (s1, groups, mx)
@@ -198,22 +215,24 @@ def test_shared_plan_mistakes_fall_back_to_private():
     cases["pointing at another group"] = (s2, groups, mx)
     g3 = groups.copy(); g3[0, 4] = g3[0, 2]
     cases["listed twice"] = (sg, g3, mx)
-    cases["P beyond max_shared_parts"] = (sg, groups, int(groups[:, 0].min()) - 1)
+    cases["shared partitions beyond max_shared_parts"] = (
+        sg, groups, min(-(-int(x) // pb) for x in groups[:, 0]) - 1)
     g5 = groups.copy(); g5[1, 0] = 0
-    cases["P = 0"] = (sg, g5, mx)
+    cases["S = 0"] = (sg, g5, mx)
     s6 = sg.copy(); s6[B - 1] = len(groups) + 4
     cases["group past n_groups"] = (s6, groups, mx)
-    g7 = groups.copy(); g7[0, 0] = 50
-    cases["P past every member's blocks"] = (sg, g7, 64)
+    g7 = groups.copy()
+    g7[0, 0] = max(-(-int(c.lens[m]) // BS) for m in _members(groups, 0))
+    cases["S past every member's blocks"] = (sg, g7, 64)
     for name, plan in cases.items():
         say("shared fallback", name)
         got = c.shared(plan, 128)
         assert np.isfinite(got).all(), name
         assert np.abs(got - want).max() <= TOL["f16"], name
-    # a member whose length leaves no private block past P partitions
+    # a member whose length leaves no private block past the S shared ones
     lens = c.lens.copy()
     m = _members(groups, 0)[3]
-    lens[m] = int(groups[0, 0]) * 128
+    lens[m] = int(groups[0, 0]) * BS
     say("shared fallback short member")
     got = c.shared((sg, groups, mx), 128, lens=lens)
     assert np.abs(got - c.want(lens=lens)).max() <= TOL["f16"]
@@ -227,8 +246,9 @@ def test_shared_private_grid_bound():
     pb = 128 // BS
     priv = []
     for b, n in enumerate(c.lens):
-        nparts = -(-(-(-int(n) // BS)) // pb)
-        priv.append(nparts - (int(groups[sg[b], 0]) if sg[b] >= 0 else 0))
+        nblk = -(-int(n) // BS)
+        shared = int(groups[sg[b], 0]) if sg[b] >= 0 else 0
+        priv.append(-(-(nblk - shared) // pb))
     assert mp == max(priv) and mp > 1
     want = c.want()
     say("shared private bound", mp)
