@@ -472,16 +472,19 @@ def run_fork_cow(args, torch, pkv, workloads):
         if not shared:
             return None
         h0 = time.perf_counter()
-        sg, groups, mx, mp = pkv.pa_shared_plan(tab_h.numpy(), len_h.numpy(), bs, 512, 1)
+        splan = pkv.pa_shared_plan(tab_h.numpy(), len_h.numpy(), bs, 512, 1)
+        sg, groups, mx, mp = splan
         plan_s.append(time.perf_counter() - h0)
-        return torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev), mx, mp
+        return (torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev), mx, mp,
+                splan.max_private_blocks)
 
     def decode(max_len, plan, ev=None):
         if ev is not None:
             ev[0].record()
         if plan is not None:
-            pkv.pa_decode_shared(q, k, v, d_tab, d_len, max_len, *plan,
-                                 partition_tokens=512, out=out, workspace=ws)
+            pkv.pa_decode_shared(q, k, v, d_tab, d_len, max_len, *plan[:4],
+                                 max_private_blocks=plan[4], partition_tokens=512, out=out,
+                                 workspace=ws)
         else:
             pkv.pa_decode(q, k, v, d_tab, d_len, max_len, partition_tokens=512, out=out,
                           workspace=ws)
@@ -861,7 +864,8 @@ def run_beam(args, torch, pkv, workloads):
         flat = np.array([s for g in beams for s in g], dtype=np.int64)
         slots, pairs = bm.append_slots(flat, np.arange(B, dtype=np.int32))
         tables, lens = bm.export_batch(flat, width, pad_block=0)
-        sg, groups, mx, mp = pkv.pa_shared_plan(tables, lens, bs, 512, cfg["hq"] // H)
+        splan = pkv.pa_shared_plan(tables, lens, bs, 512, cfg["hq"] // H)
+        sg, groups, mx, mp = splan
         host = time.perf_counter() - h0
         d_slot = torch.from_numpy(slots).to(dev)
         d_pairs = torch.from_numpy(pairs).to(dev) if len(pairs) else None
@@ -878,7 +882,8 @@ def run_beam(args, torch, pkv, workloads):
         if ev is not None:
             ev[2].record()
         pkv.pa_decode_shared(q, k, v, d_tab, d_len, int(lens.max()), d_sg, d_gr, mx, mp,
-                             partition_tokens=512, out=out, workspace=ws)
+                             max_private_blocks=splan.max_private_blocks, partition_tokens=512,
+                             out=out, workspace=ws)
         if ev is not None:
             ev[3].record()
         uniq = len(np.unique(np.concatenate([tables[i, :-(-int(n) // bs)] for i, n in enumerate(lens)])))
@@ -917,13 +922,15 @@ def run_beam(args, torch, pkv, workloads):
     cmp = {"plain_pa_decode_ms": timed(lambda: pkv.pa_decode(
         q, k, v, d_tab, d_len, mlen, partition_tokens=512, out=out, workspace=ws))}
     for pt in (512, 128):
-        sg, groups, mx, mp = pkv.pa_shared_plan(tables, lens, bs, pt, cfg["hq"] // H)
+        splan = pkv.pa_shared_plan(tables, lens, bs, pt, cfg["hq"] // H)
+        sg, groups, mx, mp = splan
         d_sg, d_gr = torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev)
         ws2 = torch.empty(max(pkv.pa_decode_shared_workspace_bytes(B, cfg["hq"], D, mlen, pt), 1),
                           dtype=torch.uint8, device=dev)
         cmp[f"shared_pt{pt}"] = {"groups": len(groups), "shared_blocks": int(groups[:, 0].sum()),
                                  "ms": timed(lambda: pkv.pa_decode_shared(
                                      q, k, v, d_tab, d_len, mlen, d_sg, d_gr, mx, mp,
+                                     max_private_blocks=splan.max_private_blocks,
                                      partition_tokens=pt, out=out, workspace=ws2))}
     npairs = np.array([x[0] for x in info])
     toks = np.array([x[1] for x in info], dtype=np.float64)

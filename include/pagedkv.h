@@ -526,13 +526,16 @@ int pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void
  *   *n_groups_out: groups written; *max_parts_out: the most shared
  *     partitions of any group (0 if none);
  *   *max_private_parts_out: the most partitions any sequence has after its
- *     group's shared blocks (a sequence in no group: all of its partitions).
+ *     group's shared blocks (a sequence in no group: all of its partitions);
+ *   *max_private_blocks_out: likewise in blocks (0 for an empty or invalid
+ *     length), the hint pa_decode_shared takes as max_private_blocks.
  * Every group it writes satisfies the membership rule above for all its
  * members. */
 int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const int32_t* lens, int32_t B,
                    int32_t block_size, int32_t partition_tokens, int32_t query_group,
                    int32_t* seq_group_out, int32_t* groups_out, int32_t* n_groups_out,
-                   int32_t* max_parts_out, int32_t* max_private_parts_out);
+                   int32_t* max_parts_out, int32_t* max_private_parts_out,
+                   int32_t* max_private_blocks_out);
 
 /* pa_decode with a shared-prefix plan (above).  Arguments as pa_decode,
  * plus:
@@ -545,6 +548,11 @@ int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const int32_t* len
  *     after its group's shared blocks (sizes the private grid; 0 = no
  *     bound, the grid then covers max_context_len).  A sequence with more
  *     gets NaN output rows.
+ *   max_private_blocks: host-side hint, the most blocks any sequence reads
+ *     outside the shared pass (0 = unknown).  It only picks how the private
+ *     pass maps waves (up to 8 blocks: four KV heads per workgroup, one per
+ *     wave; otherwise one head per workgroup, its blocks split over the
+ *     waves); the results are the same either way, whatever its value.
  * With n_groups > 0: dtype F16 or BF16 (the shared partitions run on the
  * matrix cores with up to 16 query columns: members x query group),
  * partition_tokens > 0, and, when max_shared_parts > 0, a workspace of
@@ -560,8 +568,8 @@ int pa_decode_shared(float* out, const void* q, const void* k_cache, const void*
                      int32_t block_size, int32_t num_blocks, float scale,
                      int32_t partition_tokens, int32_t dtype, const int32_t* seq_group,
                      const int32_t* groups, int32_t n_groups, int32_t max_shared_parts,
-                     int32_t max_private_parts, void* workspace, size_t workspace_bytes,
-                     void* stream);
+                     int32_t max_private_parts, int32_t max_private_blocks, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* ==== measurement helper (gfx950) ========================================
  * Streaming read of `bytes` bytes of device memory at `buf` (both multiples

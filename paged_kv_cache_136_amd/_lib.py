@@ -74,7 +74,7 @@ SIGNATURES = {
     "pa_prefill": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                   c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp]),
     "pa_shared_plan": (ctypes.c_int, [P_i32, c_i32, P_i32, c_i32, c_i32, c_i32, c_i32, P_i32,
-                                      P_i32, P_i32, P_i32, P_i32]),
+                                      P_i32, P_i32, P_i32, P_i32, P_i32]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_shared_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
@@ -86,7 +86,8 @@ SIGNATURES = {
                                          c_vp]),
     "pa_decode_shared": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
                                         c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32,
-                                        c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp]),
+                                        c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_sz,
+                                        c_vp]),
 }
 
 

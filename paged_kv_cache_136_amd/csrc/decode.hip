@@ -91,6 +91,8 @@ struct DecodeArgs {
   int32_t batch;             // B
   int32_t qgroup;            // query heads per KV head
   int32_t grid_parts;        // z extent of the private grid (<= the split of max_len)
+  int32_t private_blocks;    // host hint: most blocks a sequence reads outside the shared
+                             // pass (0: unknown); picks the private pass's wave mapping
 };
 
 __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
@@ -275,7 +277,12 @@ __device__ __forceinline__ void consume_block(RowState<DT, D, G>& st, const uint
   }
 }
 
-template <int DT, int D, int G, int NBUF>
+// HEADS: the waves of a workgroup take four adjacent KV heads of one
+// (sequence, partition) instead of splitting one head's blocks, and each
+// writes its own result (no merge through LDS).  Used for the private pass
+// of a shared-prefix plan, whose partitions are often a block or two long:
+// one head per workgroup would leave three of its four waves idle there.
+template <int DT, int D, int G, int NBUF, bool HEADS = false>
 __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   constexpr int ELEM = ElemTraits<DT>::bytes;
   constexpr int EPL = 16 / ELEM;          // elements per lane per load
@@ -300,8 +307,12 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
   const int wv = __builtin_amdgcn_readfirstlane(w);
-  const Prologue<NBUF> pro = prologue<NBUF>(a, b, wc.z, wv, wc.z);
-  const int g = rotate_head(wc.g, a.hkv, pro.rot);
+  // The wave's first block and block stride within the partition.
+  constexpr int kStep = HEADS ? 1 : kWaves;
+  const int w0 = HEADS ? 0 : wv;
+  const Prologue<NBUF> pro = HEADS ? prologue<NBUF, 1>(a, b, wc.z, 0, wc.z)
+                                   : prologue<NBUF>(a, b, wc.z, wv, wc.z);
+  const int g = HEADS ? wc.g * kWaves + wv : rotate_head(wc.g, a.hkv, pro.rot);
   const int32_t* trow = pro.trow;
   const int n = pro.n;
   const bool valid = len_valid(n, a);
@@ -315,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
   // Degenerate rows: empty sequence -> 0, invalid length -> NaN.
   if (!valid || n == 0) {
     const float fill = valid ? 0.f : __builtin_nanf("");
-    for (int i = tid; i < G * D; i += kThreads)
+    for (int i = HEADS ? lane : tid; i < G * D; i += HEADS ? 64 : kThreads)
       a.out[(static_cast<size_t>(b) * a.hq + h0 + i / D) * D + i % D] = fill;
     return;
   }
@@ -384,22 +395,22 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       consume_block<DT, D, G, LPB, RPI, true>(st, q, kw, vw, a.scale_log2, r, vr);
   };
 
-  // This wave's blocks are first+wv, first+wv+4, ...; NBUF of them are in
-  // flight in a register ring (the loop is unrolled by NBUF so each ring
-  // slot is a fixed set of registers).
+  // This wave's blocks are first+wv, first+wv+4, ... (HEADS: every block
+  // of the partition); NBUF of them are in flight in a register ring (the
+  // loop is unrolled by NBUF so each ring slot is a fixed set of registers).
   uint4 kr[NBUF][LPB], vr[NBUF][LPB];
 #pragma unroll
   for (int sl = 0; sl < NBUF; ++sl) {
-    const int jj = first + wv + sl * kWaves;
+    const int jj = first + w0 + sl * kStep;
     if (jj < last) load_block(check_id(a.seq_group == nullptr ? pro.spec[sl] : trow[jj]), kr[sl], vr[sl]);
   }
-  for (int j = first + wv; j < last; j += NBUF * kWaves) {
+  for (int j = first + w0; j < last; j += NBUF * kStep) {
 #pragma unroll
     for (int sl = 0; sl < NBUF; ++sl) {
-      const int jj = j + sl * kWaves;
+      const int jj = j + sl * kStep;
       if (jj < last) {
         consume(kr[sl], vr[sl], jj);
-        const int jn = jj + NBUF * kWaves;
+        const int jn = jj + NBUF * kStep;
         if (jn < last) load_block(block_id(jn), kr[sl], vr[sl]);
       }
     }
@@ -414,6 +425,26 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) st.o[hh][e] = group_sum<LPR, 64>(st.o[hh][e] * f);
     st.m[hh] = M;
+  }
+  if constexpr (HEADS) {
+    // The wave's result is final: row group 0 writes it.
+    if (r == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float inv = 1.f / st.l[hh];
+        const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
+        const size_t bhp = nparts == 1 ? 0 : ws_row(a, b, h0 + hh, slot);
+        float* dst = nparts == 1 ? a.out + bh * D : a.ws_o + bhp * D;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          dst[c * EPL + e] = bad_ids ? __builtin_nanf("") : st.o[hh][e] * inv;
+        if (nparts > 1 && c == 0) {
+          a.ws_m[bhp] = bad_ids ? 0.f : st.m[hh];
+          a.ws_l[bhp] = bad_ids ? __builtin_nanf("") : st.l[hh];
+        }
+      }
+    }
+    return;
   }
   if (r == 0) {
 #pragma unroll
@@ -974,9 +1005,25 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
   dim3 grid(a.hkv, B, a.grid_parts);
   // The matrix-core kernel gives each wave a whole partition.
   dim3 grid_w(a.hkv, B, (a.grid_parts + kWaves - 1) / kWaves);
+  // The private pass of a shared-prefix plan whose sequences read at most
+  // kHeadsMaxBlocks blocks outside the shared pass (16-bit K/V only): four
+  // KV heads per workgroup.  Longer private runs keep the head-per-workgroup
+  // mapping, whose shorter workgroups leave a shorter tail (the fork
+  // batch's 17-block runs measured 2-4% slower the other way).
+  constexpr bool kHeadsOk = DT != PA_DTYPE_F32;
+  constexpr int kHeadsMaxBlocks = 8;
+  const bool heads = kHeadsOk && a.n_groups > 0 && a.hkv % kWaves == 0 &&
+                     a.private_blocks > 0 && a.private_blocks <= kHeadsMaxBlocks;
+  dim3 grid_h(a.hkv / kWaves, B, a.grid_parts);
   switch (group) {
-    case 1: decode_phase1<DT, D, 1, kNbuf><<<grid, kThreads, 0, st>>>(a); break;
-    case 2: decode_phase1<DT, D, 2, kNbuf><<<grid, kThreads, 0, st>>>(a); break;
+    case 1:
+      if (heads) decode_phase1<DT, D, 1, kNbuf, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      else decode_phase1<DT, D, 1, kNbuf><<<grid, kThreads, 0, st>>>(a);
+      break;
+    case 2:
+      if (heads) decode_phase1<DT, D, 2, kNbuf, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      else decode_phase1<DT, D, 2, kNbuf><<<grid, kThreads, 0, st>>>(a);
+      break;
     case 4:
       if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, kNbufMfma, false><<<grid_w, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 4, kNbufG4><<<grid, kThreads, 0, st>>>(a);
@@ -1097,14 +1144,15 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                 int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
                 const int32_t* seq_group, const int32_t* groups, int32_t n_groups,
-                int32_t max_shared_parts, int32_t max_private_parts, void* workspace,
-                size_t workspace_bytes, void* stream, bool use_scratch = false) {
+                int32_t max_shared_parts, int32_t max_private_parts, int32_t max_private_blocks,
+                void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false) {
   const std::string name(fn);
   auto err_ = [&](int code, const std::string& msg) { return fail(code, name + ": " + msg); };
   if (B < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
     return err_(PA_ERR_INVALID, "negative size or empty pool");
-  if (n_groups < 0 || max_shared_parts < 0 || max_private_parts < 0)
-    return err_(PA_ERR_INVALID, "negative n_groups, max_shared_parts or max_private_parts");
+  if (n_groups < 0 || max_shared_parts < 0 || max_private_parts < 0 || max_private_blocks < 0)
+    return err_(PA_ERR_INVALID,
+                "negative n_groups, max_shared_parts, max_private_parts or max_private_blocks");
   if (B == 0) { clear_error(); return PA_OK; }
   // A table of width 0 has no entries and may be NULL.
   if (!out || !q || !k_cache || !v_cache || (!block_tables && max_blocks_per_seq > 0) || !context_lens)
@@ -1194,6 +1242,7 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
     a.n_groups = n_groups;
     a.max_shared_parts = max_shared_parts;
     if (max_private_parts > 0) a.grid_parts = std::min(P, max_private_parts);
+    a.private_blocks = max_private_blocks;
   }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1221,7 +1270,7 @@ extern "C" int pa_decode(float* out, const void* q, const void* k_cache, const v
   return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, max_context_len, B, num_q_heads, num_kv_heads, head_dim,
                      block_size, num_blocks, scale, partition_tokens, dtype, nullptr, nullptr, 0,
-                     0, 0, workspace, workspace_bytes, stream);
+                     0, 0, 0, workspace, workspace_bytes, stream);
 }
 
 extern "C" int pa_decode_shared(float* out, const void* q, const void* k_cache,
@@ -1232,13 +1281,13 @@ extern "C" int pa_decode_shared(float* out, const void* q, const void* k_cache,
                                 int32_t num_blocks, float scale, int32_t partition_tokens,
                                 int32_t dtype, const int32_t* seq_group, const int32_t* groups,
                                 int32_t n_groups, int32_t max_shared_parts,
-                                int32_t max_private_parts, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                int32_t max_private_parts, int32_t max_private_blocks,
+                                void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl("pa_decode_shared", out, q, k_cache, v_cache, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, B, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
                      dtype, seq_group, groups, n_groups, max_shared_parts, max_private_parts,
-                     workspace, workspace_bytes, stream);
+                     max_private_blocks, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }
@@ -1253,5 +1302,5 @@ extern "C" int pa_decode_noalloc(float* out, const void* q, const void* k_cache,
   return decode_impl("pa_decode_noalloc", out, q, k_cache, v_cache, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, B, num_q_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
-                     dtype, nullptr, nullptr, 0, 0, 0, nullptr, 0, stream, true);
+                     dtype, nullptr, nullptr, 0, 0, 0, 0, nullptr, 0, stream, true);
 }

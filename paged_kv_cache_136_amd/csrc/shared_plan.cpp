@@ -46,7 +46,7 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
                               int32_t B, int32_t block_size, int32_t partition_tokens,
                               int32_t query_group, int32_t* seq_group_out, int32_t* groups_out,
                               int32_t* n_groups_out, int32_t* max_parts_out,
-                              int32_t* max_private_parts_out) {
+                              int32_t* max_private_parts_out, int32_t* max_private_blocks_out) {
   if (B < 0 || max_blocks < 0 || block_size <= 0)
     return fail(PA_ERR_INVALID, "pa_shared_plan: negative size or block_size <= 0");
   if (partition_tokens <= 0 || partition_tokens % block_size != 0)
@@ -54,7 +54,7 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
                 "pa_shared_plan: partition_tokens must be a positive multiple of block_size");
   if (query_group != 1 && query_group != 2 && query_group != 4 && query_group != 8)
     return fail(PA_ERR_INVALID, "pa_shared_plan: query_group must be 1, 2, 4 or 8");
-  if (!n_groups_out || !max_parts_out || !max_private_parts_out ||
+  if (!n_groups_out || !max_parts_out || !max_private_parts_out || !max_private_blocks_out ||
       (B > 0 && (!tables || !lens || !seq_group_out)) || (B > 1 && !groups_out))
     return fail(PA_ERR_INVALID, "pa_shared_plan: null pointer");
   const int32_t pb = partition_tokens / block_size;
@@ -63,6 +63,7 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
   *n_groups_out = 0;
   *max_parts_out = 0;
   *max_private_parts_out = 0;
+  *max_private_blocks_out = 0;
 
   auto row = [&](int32_t b) { return tables + static_cast<size_t>(b) * max_blocks; };
   // Length in blocks of the common prefix of two rows, within both caps.
@@ -128,10 +129,10 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
       lo = hi;
     }
   }
-  // Private partitions left to each sequence: those of the blocks after its
-  // group's shared ones (every partition when it is in no group; one for an
-  // empty or invalid length, as in decode).
-  int32_t max_private = 0;
+  // Private partitions and blocks left to each sequence: those after its
+  // group's shared blocks (all of them when it is in no group; one
+  // partition and no block for an empty or invalid length, as in decode).
+  int32_t max_private = 0, max_private_blocks = 0;
   for (int32_t b = 0; b < B; ++b) {
     const int32_t n = lens[b];
     const bool ok = n > 0 && n <= static_cast<int64_t>(max_blocks) * block_size;
@@ -140,10 +141,12 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
     const int32_t shared = gi >= 0 ? groups_out[static_cast<size_t>(gi) * PA_SHARED_ROW] : 0;
     const int32_t priv = nblk == 0 ? 1 : (nblk - shared + pb - 1) / pb;
     max_private = std::max(max_private, priv);
+    max_private_blocks = std::max(max_private_blocks, nblk - shared);
   }
   *n_groups_out = ng;
   *max_parts_out = max_parts;
   *max_private_parts_out = max_private;
+  *max_private_blocks_out = max_private_blocks;
   pkv::clear_error();
   return PA_OK;
 }

@@ -202,15 +202,16 @@ class DecodeEngine:
         tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
         splan = None
         if self.shared_prefix:
-            sg, groups, mx, mp = pa_shared_plan(tables, lens, self.bs, self.partition_tokens,
-                                                self.hq // self.hkv)
+            plan = pa_shared_plan(tables, lens, self.bs, self.partition_tokens,
+                                  self.hq // self.hkv)
+            sg, groups, mx, mp = plan
             # block reads the plan saves: (members - 1) x shared blocks per group
             saved = int(((groups[:, 1:] >= 0).sum(axis=1) - 1) @ groups[:, 0]) if len(groups) else 0
             total = int((-(-lens.astype(np.int64) // self.bs)).sum())
             if len(groups) and saved >= self.shared_min_saving * total:
                 self.shared_groups += len(groups)
                 splan = (torch.from_numpy(sg).to(self.dev),
-                         torch.from_numpy(groups).to(self.dev), mx, mp)
+                         torch.from_numpy(groups).to(self.dev), mx, mp, plan.max_private_blocks)
         self.host_seconds += time.perf_counter() - h0
         max_len = int(lens.max())
         d_tab = torch.from_numpy(tables).to(self.dev)
@@ -226,7 +227,8 @@ class DecodeEngine:
                                       partition_tokens=self.partition_tokens, workspace=self.ws))
             else:
                 outs.append(pa_decode_shared(q, self.k[layer], self.v[layer], d_tab, d_len, max_len,
-                                             *splan, partition_tokens=self.partition_tokens,
+                                             *splan[:4], max_private_blocks=splan[4],
+                                             partition_tokens=self.partition_tokens,
                                              workspace=self.ws))
         return outs
 

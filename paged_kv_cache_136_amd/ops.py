@@ -231,10 +231,17 @@ def pa_decode_noalloc_max_bytes():
     return lib().pa_decode_noalloc_max_bytes()
 
 
+class SharedPlan(tuple):
+    """(seq_group, groups, max_shared_parts, max_private_parts), with the
+    planner's private-pass hint in ``max_private_blocks``."""
+    max_private_blocks = 0
+
+
 def pa_shared_plan(block_tables, context_lens, block_size, partition_tokens, query_group):
     """Shared-prefix plan from host int32 arrays tables [B, max_blocks] and
-    lens [B].  Returns (seq_group int32 [B], groups int32 [n, 17],
-    max_shared_parts, max_private_parts)."""
+    lens [B].  Returns a SharedPlan: (seq_group int32 [B], groups int32
+    [n, 17], max_shared_parts, max_private_parts), plus the hint
+    ``.max_private_blocks`` for pa_decode_shared."""
     tab = np.ascontiguousarray(block_tables, dtype=np.int32)
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
     if tab.ndim != 2 or lens.shape != (tab.shape[0],):
@@ -242,24 +249,28 @@ def pa_shared_plan(block_tables, context_lens, block_size, partition_tokens, que
     B = tab.shape[0]
     seq_group = np.empty(B, dtype=np.int32)
     groups = np.empty((max(B // 2, 1), SHARED_ROW), dtype=np.int32)
-    n, mx, mp = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    n, mx, mp, mb = (ctypes.c_int32(0) for _ in range(4))
     p = ctypes.POINTER(ctypes.c_int32)
     check(lib().pa_shared_plan(tab.ctypes.data_as(p), tab.shape[1], lens.ctypes.data_as(p), B,
                                int(block_size), int(partition_tokens), int(query_group),
                                seq_group.ctypes.data_as(p), groups.ctypes.data_as(p),
-                               ctypes.byref(n), ctypes.byref(mx), ctypes.byref(mp)))
-    return seq_group, groups[:n.value].copy(), mx.value, mp.value
+                               ctypes.byref(n), ctypes.byref(mx), ctypes.byref(mp),
+                               ctypes.byref(mb)))
+    plan = SharedPlan((seq_group, groups[:n.value].copy(), mx.value, mp.value))
+    plan.max_private_blocks = mb.value
+    return plan
 
 
 def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, max_context_len, seq_group,
                      groups, max_shared_parts, max_private_parts=0, scale=None,
-                     partition_tokens=512, out=None, workspace=None, stream=None):
+                     partition_tokens=512, out=None, workspace=None, stream=None,
+                     max_private_blocks=0):
     """pa_decode with a shared-prefix plan: seq_group int32 [B] and groups
     int32 [n, 17] on the GPU (from pa_shared_plan; row = shared blocks, then
     the members); max_shared_parts and max_private_parts are the plan's
-    host-side grid bounds (0 for the latter: no bound).  A given workspace
-    must hold pa_decode_shared_workspace_bytes(...) bytes when the plan has
-    groups."""
+    host-side grid bounds (0 for the latter: no bound), max_private_blocks
+    its private-pass hint (0: unknown).  A given workspace must hold
+    pa_decode_shared_workspace_bytes(...) bytes when the plan has groups."""
     n = 0 if groups is None else groups.shape[0]
     need_fn = (pa_decode_shared_workspace_bytes if n and int(max_shared_parts) > 0
                else pa_decode_workspace_bytes)
@@ -274,7 +285,8 @@ def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, max_contex
             raise ValueError("seq_group must be int32 [B] and groups int32 [n, 17]")
     check(lib().pa_decode_shared(*head, seq_group.data_ptr() if n else None,
                                  groups.data_ptr() if n else None, n, int(max_shared_parts),
-                                 int(max_private_parts), *ws, _stream(stream)))
+                                 int(max_private_parts), int(max_private_blocks), *ws,
+                                 _stream(stream)))
     return out
 
 

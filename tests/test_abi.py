@@ -209,7 +209,7 @@ def test_shared_decode_plan_rejections():
         # pa_decode's arguments (64-token context, one partition: no workspace), then
         # (seq_group, groups, n_groups, max_shared_parts, max_private_parts, ws, ws_bytes, stream)
         return L.pa_decode_shared(p, p, p, p, p, 8, p, 64, 2, 8, 2, 128, 16, 64, 0.088, pt,
-                                  dtype, seq_group, groups, n_groups, max_shared, 1, None, 0,
+                                  dtype, seq_group, groups, n_groups, max_shared, 1, 0, None, 0,
                                   None)
 
     for kw, status, msg in [

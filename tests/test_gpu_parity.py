@@ -550,14 +550,16 @@ def test_fork_cow_shared_decode_all_forks(fork_flow):
     cfg = f["cfg"]
     P, F, bs = cfg["prompts"], cfg["forks"], 16
     n = cfg["prompt_len"] + 1 + cfg["extra"]
-    sg, groups, mx, mp = pkv.pa_shared_plan(f["tables"], f["clens"], bs, cfg["partition_tokens"], 1)
-    assert len(groups) == P and mx == 4 and mp == 1
+    splan = pkv.pa_shared_plan(f["tables"], f["clens"], bs, cfg["partition_tokens"], 1)
+    sg, groups, mx, mp = splan
+    assert len(groups) == P and mx == 4 and mp == 1 and splan.max_private_blocks == 17
     assert sorted(int(m) for m in groups[:, 1:].ravel() if m >= 0) == list(range(P * F))
     say("fork_cow: shared-prefix decode 512 forks")
     out_s = pkv.pa_decode_shared(f["q"], f["k"], f["v"], torch.from_numpy(f["tables"]).cuda(),
                                  torch.from_numpy(f["clens"]).cuda(), n,
                                  torch.from_numpy(sg).cuda(), torch.from_numpy(groups).cuda(), mx,
-                                 mp, partition_tokens=cfg["partition_tokens"])
+                                 mp, partition_tokens=cfg["partition_tokens"],
+                                 max_private_blocks=splan.max_private_blocks)
     torch.cuda.synchronize()
     got = out_s.cpu().numpy()
     err = float(np.abs(got - _fork_oracle(f)).max())

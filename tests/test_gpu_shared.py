@@ -55,15 +55,18 @@ class Case:
     def plan(self, pt):
         return pkv.pa_shared_plan(self.tables, self.lens, BS, pt, self.hq // self.hkv)
 
-    def shared(self, plan, pt, tables=None, lens=None):
-        """plan: (seq_group, groups, max_shared_parts[, max_private_parts])."""
+    def shared(self, plan, pt, tables=None, lens=None, heads=False):
+        """plan: (seq_group, groups, max_shared_parts[, max_private_parts]).
+        heads: a private-block hint of 1, which selects the private pass's
+        four-heads-per-workgroup mapping whatever the plan (the hint never
+        changes results); else 0, the one-head mapping."""
         sg, groups, mx = plan[:3]
         mp = plan[3] if len(plan) > 3 else 0
         t = self.tables if tables is None else tables
         n = self.lens if lens is None else lens
         out = pkv.pa_decode_shared(self.q, self.k, self.v, self.dev(t), self.dev(n),
                                    self.max_len, self.dev(sg), self.dev(groups.reshape(-1, 17)),
-                                   mx, mp, partition_tokens=pt)
+                                   mx, mp, partition_tokens=pt, max_private_blocks=int(heads))
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64)
 
@@ -83,22 +86,23 @@ def _extra(n, seed, hi=60):
     return np.random.default_rng(seed).integers(1, hi, size=n)
 
 
+@pytest.mark.parametrize("heads", [False, True])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-def test_shared_fork_families(dtype, d, group):
+def test_shared_fork_families(dtype, d, group, heads):
     """Four fork families (prompts 700, 1100, 530 and 95 tokens; 16/group
     members, at most 4), ragged appends, two unforked sequences; 128-token
-    partitions."""
-    hkv, forks = 2, min(4, 16 // group)
+    partitions; the private pass in either wave mapping."""
+    hkv, forks = 4, min(4, 16 // group)      # 4 KV heads: either private mapping
     prompts = [700, 1100, 530, 95]
     tables, lens = fork_family(prompts, forks, _extra(len(prompts) * forks, d + group),
                                singles=[300, 17], seed=group)
-    say("shared forks", dtype, d, group)
+    say("shared forks", dtype, d, group, "heads", heads)
     c = Case(tables, lens, hkv * group, hkv, d, dtype, seed=31 + d + group)
     plan = c.plan(128)
     assert len(plan[1]) == len(prompts)          # the 95-token family shares its 6 full blocks
-    got, want = c.shared(plan, 128), c.want()
+    got, want = c.shared(plan, 128, heads=heads), c.want()
     assert np.isfinite(got).all()
     err = np.abs(got - want).max()
     assert err <= TOL[dtype], err
@@ -127,9 +131,10 @@ def test_shared_inside_one_partition():
     c = Case(tables, lens, 8, 8, 128, "bf16", seed=21)
     plan = c.plan(512)
     assert len(plan[1]) == 3 and plan[2] == 1
-    got = c.shared(plan, 512)
-    assert np.isfinite(got).all()
-    assert np.abs(got - c.want()).max() <= TOL["bf16"]
+    for heads in (False, True):
+        got = c.shared(plan, 512, heads=heads)
+        assert np.isfinite(got).all()
+        assert np.abs(got - c.want()).max() <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype,hq,hkv", [("f16", 4, 4), ("bf16", 16, 4)])
@@ -141,8 +146,9 @@ def test_shared_beam_tree(dtype, hq, hkv):
     c = Case(tables, lens, hq, hkv, 128, dtype, seed=77)
     plan = c.plan(64)
     assert len(plan[1]) > 0
-    err = np.abs(c.shared(plan, 64) - c.want()).max()
-    assert err <= TOL[dtype], err
+    for heads in (False, True):
+        err = np.abs(c.shared(plan, 64, heads=heads) - c.want()).max()
+        assert err <= TOL[dtype], (heads, err)
 
 
 def _family_case(seed=3):
@@ -168,7 +174,8 @@ def test_shared_large_scores():
     assert np.abs(got - c.want()).max() <= TOL["bf16"]
 
 
-def test_shared_table_mismatch_gives_nan():
+@pytest.mark.parametrize("heads", [False, True])
+def test_shared_table_mismatch_gives_nan(heads):
     """A member whose own table differs from the group's source row inside
     the shared partitions gets NaN rows; everyone else stays exact."""
     c = _family_case()
@@ -178,28 +185,30 @@ def test_shared_table_mismatch_gives_nan():
     bad = c.tables.copy()
     bad[victim, 3] = bad[mem[0], 40]                # another block that row also holds
     say("shared mismatch")
-    got = c.shared((sg, groups, mx), 128, tables=bad)
+    got = c.shared((sg, groups, mx), 128, tables=bad, heads=heads)
     want = c.want(tables=bad)
     assert np.isnan(got[victim]).all()
     others = [b for b in range(len(c.lens)) if b != victim]
     assert np.abs(got[others] - want[others]).max() <= TOL["f16"]
 
 
-def test_shared_source_out_of_range_gives_nan():
+@pytest.mark.parametrize("heads", [False, True])
+def test_shared_source_out_of_range_gives_nan(heads):
     c = _family_case()
     sg, groups, mx, _ = c.plan(128)
     g = groups.copy()
     mem = _members(g, 1)
     g[1, 1] = len(c.lens) + 3                          # source slot outside the batch
     say("shared bad source")
-    got = c.shared((sg, g, mx), 128)
+    got = c.shared((sg, g, mx), 128, heads=heads)
     want = c.want()
     assert np.isnan(got[mem[1:]]).all()
     rest = [b for b in range(len(c.lens)) if b not in mem[1:]]
     assert np.abs(got[rest] - want[rest]).max() <= TOL["f16"]
 
 
-def test_shared_plan_mistakes_fall_back_to_private():
+@pytest.mark.parametrize("heads", [False, True])
+def test_shared_plan_mistakes_fall_back_to_private(heads):
     """Members that the rule excludes are computed privately: not pointing
     at their group, listed twice, too few blocks, shared partitions beyond
     max_shared_parts, S = 0, a group index past n_groups."""
@@ -226,7 +235,7 @@ def test_shared_plan_mistakes_fall_back_to_private():
     cases["S past every member's blocks"] = (sg, g7, 64)
     for name, plan in cases.items():
         say("shared fallback", name)
-        got = c.shared(plan, 128)
+        got = c.shared(plan, 128, heads=heads)
         assert np.isfinite(got).all(), name
         assert np.abs(got - want).max() <= TOL["f16"], name
     # a member whose length leaves no private block past the S shared ones
@@ -234,11 +243,12 @@ def test_shared_plan_mistakes_fall_back_to_private():
     m = _members(groups, 0)[3]
     lens[m] = int(groups[0, 0]) * BS
     say("shared fallback short member")
-    got = c.shared((sg, groups, mx), 128, lens=lens)
+    got = c.shared((sg, groups, mx), 128, lens=lens, heads=heads)
     assert np.abs(got - c.want(lens=lens)).max() <= TOL["f16"]
 
 
-def test_shared_private_grid_bound():
+@pytest.mark.parametrize("heads", [False, True])
+def test_shared_private_grid_bound(heads):
     """The planner's private bound runs every sequence; one below it turns
     exactly the sequences with more private partitions into NaN rows."""
     c = _family_case()
@@ -252,10 +262,10 @@ def test_shared_private_grid_bound():
     assert mp == max(priv) and mp > 1
     want = c.want()
     say("shared private bound", mp)
-    got = c.shared((sg, groups, mx, mp), 128)
+    got = c.shared((sg, groups, mx, mp), 128, heads=heads)
     assert np.abs(got - want).max() <= TOL["f16"]
     say("shared private bound short", mp - 1)
-    got = c.shared((sg, groups, mx, mp - 1), 128)
+    got = c.shared((sg, groups, mx, mp - 1), 128, heads=heads)
     over = [b for b in range(len(priv)) if priv[b] > mp - 1]
     ok = [b for b in range(len(priv)) if priv[b] <= mp - 1]
     assert over and ok

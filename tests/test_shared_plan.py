@@ -63,7 +63,19 @@ def check_plan(tables, lens, bs, pt, qg, seq_group, groups, max_parts, max_priva
 
 
 def plan(tables, lens, bs, pt, qg):
-    return pkv.pa_shared_plan(tables, lens, bs, pt, qg)
+    """The planner's plan, with its private-block hint checked: the most
+    blocks any sequence has after its group's shared ones (0 for an empty
+    or invalid length)."""
+    p = pkv.pa_shared_plan(tables, lens, bs, pt, qg)
+    seq_group, groups = p[0], p[1]
+    want = 0
+    for b, n in enumerate(lens):
+        n = int(n)
+        nblk = -(-n // bs) if 0 < n <= tables.shape[1] * bs else 0
+        shared = int(groups[seq_group[b], 0]) if seq_group[b] >= 0 else 0
+        want = max(want, nblk - shared)
+    assert p.max_private_blocks == want
+    return p
 
 
 @pytest.mark.parametrize("qg", [1, 2, 4, 8])
