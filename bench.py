@@ -953,6 +953,7 @@ def run_beam(args, torch, pkv, workloads):
                    "decode": "pa_decode_shared with a per-step host plan"},
         "beams_per_s": round(B * args.steps / (step_ms.sum() * 1e-3), 1),
         "unique_kv_gbs": round(float(uniq.sum() * bs * per_tok / (dec_ms.sum() * 1e-3) / 1e9), 2),
+        "unique_kv_bytes_per_step": [int(u) * bs * per_tok for u in uniq],
         "cow_pairs_per_step": round(float(npairs.mean()), 1),
         "copy_ms_per_step": round(float(copy_ms.mean()), 4),
         "copy_gbs": round(float(copied[with_pairs].sum() / (copy_ms[with_pairs].sum() * 1e-3) / 1e9), 2)
@@ -967,7 +968,7 @@ def run_beam(args, torch, pkv, workloads):
              "peak": PEAK_HBM_GBS,
              "frac": round(float(uniq.mean() * bs * per_tok / (dec_ms.mean() * 1e-3) / 1e9)
                            / PEAK_HBM_GBS, 4),
-             "traffic": None, "avg_launch_ms": round(float(dec_ms.mean()), 5),
+             "traffic": load_traffic("pa_decode_shared_beam"), "avg_launch_ms": round(float(dec_ms.mean()), 5),
              "algorithmic_bytes_per_launch": int(uniq.mean() * bs * per_tok)},
             stream_read_ceiling(torch, pkv, args.read_gib)),
         "cpu_baseline": None, "wall_s": round(wall, 3),
