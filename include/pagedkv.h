@@ -429,7 +429,9 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t num_q_heads, int32_t head_di
  *   s_t = scale * <q[b][h], K[slot(b,t)][g]>,  t < n
  *   out[b][h] = sum_t softmax(s)_t * V[slot(b,t)][g]
  * computed with float32 accumulation as an online softmax over split-KV
- * partitions of `partition_tokens` tokens, combined by a reduce kernel.
+ * partitions of `partition_tokens` tokens, combined by a reduce kernel
+ * (or, when one workgroup holds all of a sequence's partitions, by that
+ * workgroup).
  *   out:  device float32 [B][num_q_heads][head_dim] (written, never read).
  *   q:    device [B][num_q_heads][head_dim] in `dtype`.
  *   k_cache, v_cache: device, one layer, layout above, in `dtype`.

@@ -35,6 +35,10 @@
 // Phase 2 merges the partitions: one workgroup of 4 waves per (query head,
 //   sequence), or, with at most 16 partitions and at least 1024 such pairs,
 //   one wave per pair and four pairs per workgroup (decode_reduce_wave).
+//   It is skipped when one workgroup of the private grid holds every
+//   private partition of a sequence (one partition on the vector path, four
+//   on the matrix cores): phase 1 then merges the shared slots, if any, and
+//   writes out[] itself.
 //
 // Memory traffic is dominated by K and V: 2*len*Hkv*head_dim*elem bytes per
 // sequence and layer; every byte is read once.  Q, tables and partials are
@@ -93,6 +97,9 @@ struct DecodeArgs {
   int32_t grid_parts;        // z extent of the private grid (<= the split of max_len)
   int32_t private_blocks;    // host hint: most blocks a sequence reads outside the shared
                              // pass (0: unknown); picks the private pass's wave mapping
+  int32_t finish;            // 1: one workgroup of the private grid holds all of a
+                             // sequence's private partitions, so phase 1 merges them with
+                             // the shared slots and writes out[]; no reduce runs
 };
 
 __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
@@ -213,6 +220,56 @@ __device__ __forceinline__ SeqParts seq_parts(const DecodeArgs& a, int b, int gi
   const int Ps = shared_parts_of(S, a.part_blocks);
   const int Pp = nblk == 0 ? 1 : (nblk - S + a.part_blocks - 1) / a.part_blocks;
   return {S, Ps, Ps + Pp};
+}
+
+// Final output of a sequence from phase 1 (DecodeArgs::finish): its Ps
+// shared partitions sit complete in workspace slots 0 .. Ps-1 (the shared
+// kernel ran earlier on the stream) and this workgroup holds the merge of
+// all its private blocks, with max M, sum L and unnormalized output O.
+// The merge is the reduce's, done in place: out = (O 2^(M - Mx) +
+// sum_s l_s o_s 2^(m_s - Mx)) / (L 2^(M - Mx) + sum_s l_s 2^(m_s - Mx)).
+// A shared slot of weight exactly 0 (an empty marker) adds nothing and is
+// not read; a NaN weight (a bad shared slot) is read and keeps its NaN.
+// With Ps = 0 this is O / L.
+struct SharedTail {
+  size_t row0;           // workspace row of slot 0
+  int Ps;
+  float Mx, f, inv;      // overall max, private factor 2^(M - Mx), 1 / total sum
+};
+__device__ __forceinline__ SharedTail shared_tail(const DecodeArgs& a, int b, int h, int Ps,
+                                                  float M, float L) {
+  SharedTail t;
+  t.row0 = Ps > 0 ? ws_row(a, b, h, 0) : 0;
+  t.Ps = Ps;
+  float Mx = M;
+  for (int s = 0; s < Ps; ++s) Mx = fmaxf(Mx, a.ws_m[t.row0 + static_cast<size_t>(s) * a.qgroup]);
+  t.f = fast_exp2(M - Mx);
+  float Lt = L * t.f;
+  for (int s = 0; s < Ps; ++s) {
+    const size_t r = t.row0 + static_cast<size_t>(s) * a.qgroup;
+    Lt = fmaf(a.ws_l[r], fast_exp2(a.ws_m[r] - Mx), Lt);
+  }
+  t.Mx = Mx;
+  t.inv = 1.f / Lt;
+  return t;
+}
+// o[e], the unnormalized private output at dim d0 + e, becomes the output.
+template <int D, int N>
+__device__ __forceinline__ void shared_tail_apply(const DecodeArgs& a, const SharedTail& t, int d0,
+                                                  float (&o)[N]) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] *= t.f;
+  for (int s = 0; s < t.Ps; ++s) {
+    const size_t r = t.row0 + static_cast<size_t>(s) * a.qgroup;
+    const float w = a.ws_l[r] * fast_exp2(a.ws_m[r] - t.Mx);
+    if (w != 0.f) {
+      const float* src = a.ws_o + r * D + d0;
+#pragma unroll
+      for (int e = 0; e < N; ++e) o[e] = fmaf(w, src[e], o[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] *= t.inv;
 }
 
 // Running softmax state of one lane: every lane of a row group (the LPR
@@ -431,8 +488,18 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     if (r == 0) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float inv = 1.f / st.l[hh];
         const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
+        if (a.finish) {
+          const SharedTail tl = shared_tail(a, b, h0 + hh, sp.Ps, st.m[hh], st.l[hh]);
+          float o[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = st.o[hh][e];
+          shared_tail_apply<D>(a, tl, c * EPL, o);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) a.out[bh * D + c * EPL + e] = bad_ids ? __builtin_nanf("") : o[e];
+          continue;
+        }
+        const float inv = 1.f / st.l[hh];
         const size_t bhp = nparts == 1 ? 0 : ws_row(a, b, h0 + hh, slot);
         float* dst = nparts == 1 ? a.out + bh * D : a.ws_o + bhp * D;
 #pragma unroll
@@ -476,6 +543,12 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       O = fmaf(s_o[ww][hh][d], f, O);
     }
     const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
+    if (a.finish) {
+      float o[1] = {O};
+      shared_tail_apply<D>(a, shared_tail(a, b, h0 + hh, sp.Ps, M, L), d, o);
+      a.out[bh * D + d] = bad ? __builtin_nanf("") : o[0];
+      continue;
+    }
     const float res = bad ? __builtin_nanf("") : O / L;
     if (nparts == 1) {
       a.out[bh * D + d] = res;
@@ -561,6 +634,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   // b: sequence (private) or plan group (shared).  n: tokens the blocks
   // [first, last) are cut from; trow: the table row they are read from.
   int b = wc.y, part, n, nblk, nparts, first, last;
+  int ps = 0;                             // private: the sequence's shared slots
   bool short_grid = false;
   const int32_t* trow;
   // SHARED: column t's member (-1 if none); the member slot this lane
@@ -612,6 +686,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     nblk = valid ? (n + kBlock - 1) / kBlock : 0;
     const SeqParts sp = seq_parts(a, b, pro.gi, nblk);
     nparts = sp.total;
+    ps = sp.Ps;
     // wave w streams private partition zp (slot Ps + zp); the workgroup's
     // merged result goes to its first slot p0
     part = sp.Ps + zp;
@@ -821,6 +896,12 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       L = fmaf(sw[16 * OROW + 16 + c], f, L);
       O = fmaf(sw[c * OROW + d], f, O);
     }
+    if (!SHARED && a.finish) {
+      float o[1] = {O};
+      shared_tail_apply<D>(a, shared_tail(a, oseq, oh, ps, Mx, L), d, o);
+      a.out[(static_cast<size_t>(oseq) * a.hq + oh) * D + d] = badc ? __builtin_nanf("") : o[0];
+      continue;
+    }
     const float res = badc ? __builtin_nanf("") : O / L;
     if (!SHARED && nparts == 1) {
       a.out[(static_cast<size_t>(oseq) * a.hq + oh) * D + d] = res;
@@ -994,9 +1075,19 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_wave(DecodeArgs a) {
 }
 
 template <int DT, int D>
-hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
+hipError_t launch_dt_d(const DecodeArgs& args, int B, int group, hipStream_t st) {
   // Shared partitions first (they fill workspace rows the private pass
   // skips), then every sequence's private partitions, then the reduce.
+  // When one workgroup of the private grid holds every private partition
+  // of a sequence (grid z extent 1), phase 1 finishes the sequence itself:
+  // it merges the shared slots, which are complete by then, and writes
+  // out[]; the reduce, its launch and the private partials' workspace round
+  // trip go away.
+  constexpr bool kMfmaOk = DT != PA_DTYPE_F32;
+  const bool mfma = kMfmaOk && (group == 4 || group == 8);
+  const int zext = mfma ? (args.grid_parts + kWaves - 1) / kWaves : args.grid_parts;
+  DecodeArgs a = args;
+  a.finish = zext == 1;
   if constexpr (DT != PA_DTYPE_F32) {
     if (a.n_groups > 0)
       decode_phase1_mfma<DT, D, 16, kNbufMfma, true>
@@ -1038,9 +1129,10 @@ hipError_t launch_dt_d(const DecodeArgs& a, int B, int group, hipStream_t st) {
   // 13B layer's 400 pairs do not: there four waves per pair win).
   const bool wave_reduce = a.num_parts <= kReduceWaveParts &&
                            static_cast<int64_t>(B) * a.hq >= kReduceWaveMinPairs;
-  if (a.num_parts > 1 && !wave_reduce)
+  if (a.finish || a.num_parts <= 1) return hipGetLastError();
+  if (!wave_reduce)
     decode_reduce<D><<<dim3(a.hq, B), kThreads, 0, st>>>(a);
-  else if (a.num_parts > 1)
+  else
     decode_reduce_wave<D><<<dim3((a.hq + kWaves - 1) / kWaves, B), kThreads, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -172,6 +172,26 @@ def test_decode_mfma_partition_groups(partition, dtype, group):
     assert np.abs(got - want).max() <= TOL[dtype]
 
 
+@pytest.mark.parametrize("partition", [64, 512])
+@pytest.mark.parametrize("dtype,group", [("bf16", 4), ("f16", 8)])
+def test_decode_mfma_one_workgroup_finishes(partition, dtype, group):
+    """At most four partitions per sequence on the matrix-core path: one
+    workgroup holds all of a sequence's partitions, merges them and writes
+    the output itself, with no reduce.  Lengths of 1 to 4 partitions (and
+    ragged tails) against the oracle, with a NaN-filled workspace, which
+    this path must not read."""
+    bs = 16
+    pb = partition // bs
+    lens = [1, 17, pb * bs, pb * bs + 1, 2 * pb * bs + 5, 3 * pb * bs, 4 * pb * bs - 3, 4 * pb * bs]
+    hq = 2 * group
+    say("decode_mfma_finish", partition, dtype, group)
+    need = pkv.pa_decode_workspace_bytes(len(lens), hq, 128, max(lens), partition)
+    ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
+    got, want = _run_decode(lens, hq, 2, 128, dtype, partition, seed=13 + partition, workspace=ws)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]
+
+
 def test_decode_tiny_workload():
     """Lengths [7,16,31,48,63], 4 heads x 64, fp32, scale 1/8, 64-block pool;
     tables built by the library's block manager with the prefix cache on

@@ -109,6 +109,31 @@ def test_shared_fork_families(dtype, d, group, heads):
     assert np.abs(got - c.private(128)).max() <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_shared_finish_in_phase1(group, dtype):
+    """512-token partitions leave every sequence one private partition (the
+    planner's bound is 1): phase 1 merges each member's shared slots into
+    its private result and writes the output, with no reduce; in either
+    private mapping, against the oracle and against the same plan with no
+    bound (the reduce merges, on the vector path)."""
+    hkv, forks = 4, min(4, 16 // group)
+    prompts = [700, 1100, 530, 95]
+    tables, lens = fork_family(prompts, forks, _extra(len(prompts) * forks, 5 + group),
+                               singles=[300, 17], seed=40 + group)
+    say("shared finish", group, dtype)
+    c = Case(tables, lens, hkv * group, hkv, 128, dtype, seed=90 + group)
+    plan = c.plan(512)
+    assert plan[3] == 1 and len(plan[1]) == len(prompts)
+    want = c.want()
+    for heads in (False, True):
+        got = c.shared(plan, 512, heads=heads)
+        assert np.isfinite(got).all()
+        assert np.abs(got - want).max() <= TOL[dtype], heads
+        unbounded = c.shared(tuple(plan[:3]) + (0,), 512, heads=heads)
+        assert np.abs(unbounded - want).max() <= TOL[dtype], heads
+
+
 @pytest.mark.parametrize("pt", [16, 64, 512])
 def test_shared_partition_sizes(pt):
     tables, lens = fork_family([1500, 640], 8, _extra(16, pt, 200), seed=5)
@@ -153,13 +178,47 @@ def test_shared_beam_tree(dtype, hq, hkv):
 
 def _family_case(seed=3):
     """Two families of 4 forks (1000 and 700 tokens) and one single; f16,
-    4 heads x 128; 128-token partitions."""
+    4 heads x 128."""
     tables, lens = fork_family([1000, 700], 4, _extra(8, seed, 40), singles=[333], seed=seed)
     return Case(tables, lens, 4, 4, 128, "f16", seed=seed)
 
 
+def _mode(c, finish):
+    """Partition size and private bound of a run: finish -> 512-token
+    partitions with the planner's bound of one private partition, so
+    phase 1 merges the shared slots and writes the output (no reduce);
+    else 128-token partitions with no bound (the reduce merges)."""
+    if not finish:
+        return 128, 0
+    mp = c.plan(512)[3]
+    assert mp == 1
+    return 512, mp
+
+
 def _members(groups, gi):
     return [int(m) for m in groups[gi, 1:] if m >= 0]
+
+
+def _over_bound(lens, plan, pt, mp):
+    """Sequences with more private partitions than the bound mp (0: none):
+    those after the shared blocks the membership rule grants (every block
+    when the rule excludes the sequence).  Their rows are NaN."""
+    if not mp:
+        return []
+    sg, groups, mx = plan[:3]
+    pb = pt // BS
+    over = []
+    for b, n in enumerate(lens):
+        nblk = -(-int(n) // BS)
+        gi = int(sg[b])
+        S = 0
+        if 0 <= gi < len(groups) and b in _members(groups, gi):
+            S0 = int(groups[gi, 0])
+            if 1 <= S0 < nblk and -(-S0 // pb) <= mx:
+                S = S0
+        if -(-(nblk - S) // pb) > mp:
+            over.append(b)
+    return over
 
 
 def test_shared_large_scores():
@@ -174,77 +233,106 @@ def test_shared_large_scores():
     assert np.abs(got - c.want()).max() <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("finish", [False, True])
 @pytest.mark.parametrize("heads", [False, True])
-def test_shared_table_mismatch_gives_nan(heads):
+def test_shared_table_mismatch_gives_nan(heads, finish):
     """A member whose own table differs from the group's source row inside
     the shared partitions gets NaN rows; everyone else stays exact."""
     c = _family_case()
-    sg, groups, mx, _ = c.plan(128)
+    pt, mp = _mode(c, finish)
+    sg, groups, mx, _ = c.plan(pt)
     mem = _members(groups, 0)
     victim = mem[2]
     bad = c.tables.copy()
     bad[victim, 3] = bad[mem[0], 40]                # another block that row also holds
-    say("shared mismatch")
-    got = c.shared((sg, groups, mx), 128, tables=bad, heads=heads)
+    say("shared mismatch", heads, finish)
+    got = c.shared((sg, groups, mx, mp), pt, tables=bad, heads=heads)
     want = c.want(tables=bad)
     assert np.isnan(got[victim]).all()
+    assert not _over_bound(c.lens, (sg, groups, mx), pt, mp)
     others = [b for b in range(len(c.lens)) if b != victim]
     assert np.abs(got[others] - want[others]).max() <= TOL["f16"]
 
 
+@pytest.mark.parametrize("finish", [False, True])
 @pytest.mark.parametrize("heads", [False, True])
-def test_shared_source_out_of_range_gives_nan(heads):
+def test_shared_source_out_of_range_gives_nan(heads, finish):
     c = _family_case()
-    sg, groups, mx, _ = c.plan(128)
+    pt, mp = _mode(c, finish)
+    sg, groups, mx, _ = c.plan(pt)
     g = groups.copy()
     mem = _members(g, 1)
     g[1, 1] = len(c.lens) + 3                          # source slot outside the batch
-    say("shared bad source")
-    got = c.shared((sg, g, mx), 128, heads=heads)
+    say("shared bad source", heads, finish)
+    got = c.shared((sg, g, mx, mp), pt, heads=heads)
     want = c.want()
     assert np.isnan(got[mem[1:]]).all()
-    rest = [b for b in range(len(c.lens)) if b not in mem[1:]]
+    # the member whose slot now holds the bad source reads all its blocks
+    # privately: past a bound of one partition it is NaN too
+    over = _over_bound(c.lens, (sg, g, mx), pt, mp)
+    assert over == ([mem[0]] if mp else [])
+    assert np.isnan(got[over]).all()
+    rest = [b for b in range(len(c.lens)) if b not in mem[1:] + over]
     assert np.abs(got[rest] - want[rest]).max() <= TOL["f16"]
 
 
+@pytest.mark.parametrize("finish", [False, True])
 @pytest.mark.parametrize("heads", [False, True])
-def test_shared_plan_mistakes_fall_back_to_private(heads):
+def test_shared_plan_mistakes_fall_back_to_private(heads, finish):
     """Members that the rule excludes are computed privately: not pointing
     at their group, listed twice, too few blocks, shared partitions beyond
-    max_shared_parts, S = 0, a group index past n_groups."""
+    max_shared_parts, S = 0, a group index past n_groups.  With a bound of
+    one private partition (finish) the fallbacks that leave a sequence
+    more than one are NaN instead, like any sequence past the bound."""
     c = _family_case()
-    sg, groups, mx, _ = c.plan(128)
+    pt, mp = _mode(c, finish)
+    sg, groups, mx, _ = c.plan(pt)
     want = c.want()
     B = len(c.lens)
-    pb = 128 // BS
+    pb = pt // BS
     cases = {}
     s1 = sg.copy(); s1[_members(groups, 0)[1]] = -1
-    cases["not pointing at its group"] = (s1, groups, mx)
+    cases["not pointing at its group"] = (s1, groups, mx, mp)
     s2 = sg.copy(); s2[_members(groups, 0)[2]] = 1
-    cases["pointing at another group"] = (s2, groups, mx)
+    cases["pointing at another group"] = (s2, groups, mx, mp)
     g3 = groups.copy(); g3[0, 4] = g3[0, 2]
-    cases["listed twice"] = (sg, g3, mx)
-    cases["shared partitions beyond max_shared_parts"] = (
-        sg, groups, min(-(-int(x) // pb) for x in groups[:, 0]) - 1)
+    cases["listed twice"] = (sg, g3, mx, mp)
+    if mx > 1:
+        cases["shared partitions beyond max_shared_parts"] = (
+            sg, groups, min(-(-int(x) // pb) for x in groups[:, 0]) - 1, mp)
     g5 = groups.copy(); g5[1, 0] = 0
-    cases["S = 0"] = (sg, g5, mx)
+    cases["S = 0"] = (sg, g5, mx, mp)
     s6 = sg.copy(); s6[B - 1] = len(groups) + 4
-    cases["group past n_groups"] = (s6, groups, mx)
+    cases["group past n_groups"] = (s6, groups, mx, mp)
     g7 = groups.copy()
     g7[0, 0] = max(-(-int(c.lens[m]) // BS) for m in _members(groups, 0))
-    cases["S past every member's blocks"] = (sg, g7, 64)
+    cases["S past every member's blocks"] = (sg, g7, 64, mp)
     for name, plan in cases.items():
-        say("shared fallback", name)
-        got = c.shared(plan, 128, heads=heads)
+        say("shared fallback", name, heads, finish)
+        got = c.shared(plan, pt, heads=heads)
+        if mp:
+            over = _over_bound(c.lens, plan, pt, mp)
+            ok = [b for b in range(B) if b not in over]
+            assert np.isnan(got[over]).all(), name
+            assert np.abs(got[ok] - want[ok]).max() <= TOL["f16"], name
+            continue
         assert np.isfinite(got).all(), name
         assert np.abs(got - want).max() <= TOL["f16"], name
     # a member whose length leaves no private block past the S shared ones
     lens = c.lens.copy()
     m = _members(groups, 0)[3]
     lens[m] = int(groups[0, 0]) * BS
-    say("shared fallback short member")
-    got = c.shared((sg, groups, mx), 128, lens=lens, heads=heads)
-    assert np.abs(got - c.want(lens=lens)).max() <= TOL["f16"]
+    say("shared fallback short member", heads, finish)
+    got = c.shared((sg, groups, mx, mp), pt, lens=lens, heads=heads)
+    want = c.want(lens=lens)
+    if mp:
+        # its S blocks, all private now, are two partitions: past the bound
+        assert -(-int(lens[m]) // BS) > pb
+        assert np.isnan(got[m]).all()
+        rest = [b for b in range(B) if b != m]
+        assert np.abs(got[rest] - want[rest]).max() <= TOL["f16"]
+    else:
+        assert np.abs(got - want).max() <= TOL["f16"]
 
 
 @pytest.mark.parametrize("heads", [False, True])
