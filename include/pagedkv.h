@@ -519,7 +519,9 @@ int pa_decode_noalloc(float* out, const void* q, const void* k_cache, const void
  * by table row; a bucket is cut greedily into groups of at most
  * PA_SHARED_MAX_MEMBERS / query_group sequences, a sequence joining the
  * open group while (members - 1) x shared blocks does not drop; a group's
- * S is the common leading run of its rows (at least 2 blocks).
+ * S is the common leading run of its rows (at least 2 blocks).  Groups are
+ * written by S, largest first (the decode's shared pass starts its
+ * workgroups in group order, so the longest start first).
  *   tables: host int32 [B][max_blocks]; lens: host int32 [B].
  *   partition_tokens: the value pa_decode_shared will get (> 0, multiple of
  *     block_size); query_group: num_q_heads / num_kv_heads (1, 2, 4, 8).

@@ -69,6 +69,7 @@ constexpr int kLoadAux = 2;        // cache policy of K/V loads: nontemporal (re
 constexpr int kNbuf = 3;           // K/V blocks in flight per wave, vector path (groups of 1, 2)
 constexpr int kNbufG4 = 1;         // same, fp32 query group of 4 (VGPR-limited)
 constexpr int kNbufMfma = 1;       // same, matrix-core path (groups of 4 and 8)
+constexpr int kNbufShared = 2;     // same, shared-prefix pass (a few long streams per group)
 
 struct DecodeArgs {
   float* out;            // [B][Hq][D]
@@ -228,45 +229,65 @@ __device__ __forceinline__ SeqParts seq_parts(const DecodeArgs& a, int b, int gi
 // all its private blocks, with max M, sum L and unnormalized output O.
 // The merge is the reduce's, done in place: out = (O 2^(M - Mx) +
 // sum_s l_s o_s 2^(m_s - Mx)) / (L 2^(M - Mx) + sum_s l_s 2^(m_s - Mx)).
-// A shared slot of weight exactly 0 (an empty marker) adds nothing and is
-// not read; a NaN weight (a bad shared slot) is read and keeps its NaN.
+// A shared slot of weight exactly 0 (an empty marker) adds nothing, even
+// where its row holds NaN; a NaN weight (a bad shared slot) keeps its NaN.
 // With Ps = 0 this is O / L.
+//
+// Wave-cooperative: all 64 lanes call shared_tail with the same sequence,
+// head, M and L.  Lane s reads slot s's (m, l), so the first 64 slots cost
+// one round trip, and the rows are then read four at a time.
 struct SharedTail {
   size_t row0;           // workspace row of slot 0
   int Ps;
   float Mx, f, inv;      // overall max, private factor 2^(M - Mx), 1 / total sum
+  float wl;              // weight of slot `lane` (lane < Ps), unnormalized
 };
 __device__ __forceinline__ SharedTail shared_tail(const DecodeArgs& a, int b, int h, int Ps,
-                                                  float M, float L) {
+                                                  float M, float L, int lane) {
   SharedTail t;
   t.row0 = Ps > 0 ? ws_row(a, b, h, 0) : 0;
   t.Ps = Ps;
-  float Mx = M;
-  for (int s = 0; s < Ps; ++s) Mx = fmaxf(Mx, a.ws_m[t.row0 + static_cast<size_t>(s) * a.qgroup]);
-  t.f = fast_exp2(M - Mx);
-  float Lt = L * t.f;
-  for (int s = 0; s < Ps; ++s) {
-    const size_t r = t.row0 + static_cast<size_t>(s) * a.qgroup;
-    Lt = fmaf(a.ws_l[r], fast_exp2(a.ws_m[r] - Mx), Lt);
-  }
+  const size_t G = static_cast<size_t>(a.qgroup);
+  const bool in0 = lane < Ps;
+  const float m0 = in0 ? a.ws_m[t.row0 + lane * G] : -INFINITY;
+  const float l0 = in0 ? a.ws_l[t.row0 + lane * G] : 0.f;
+  float Mx = fmaxf(M, m0);
+  for (int s = lane + 64; s < Ps; s += 64) Mx = fmaxf(Mx, a.ws_m[t.row0 + s * G]);
+  Mx = group_max<1, 64>(Mx);
+  t.wl = in0 ? l0 * fast_exp2(m0 - Mx) : 0.f;
+  float Ls = t.wl;
+  for (int s = lane + 64; s < Ps; s += 64)
+    Ls = fmaf(a.ws_l[t.row0 + s * G], fast_exp2(a.ws_m[t.row0 + s * G] - Mx), Ls);
+  Ls = group_sum<1, 64>(Ls);
   t.Mx = Mx;
-  t.inv = 1.f / Lt;
+  t.f = fast_exp2(M - Mx);
+  t.inv = 1.f / fmaf(L, t.f, Ls);
   return t;
 }
 // o[e], the unnormalized private output at dim d0 + e, becomes the output.
 template <int D, int N>
 __device__ __forceinline__ void shared_tail_apply(const DecodeArgs& a, const SharedTail& t, int d0,
                                                   float (&o)[N]) {
+  const size_t G = static_cast<size_t>(a.qgroup);
 #pragma unroll
   for (int e = 0; e < N; ++e) o[e] *= t.f;
-  for (int s = 0; s < t.Ps; ++s) {
-    const size_t r = t.row0 + static_cast<size_t>(s) * a.qgroup;
-    const float w = a.ws_l[r] * fast_exp2(a.ws_m[r] - t.Mx);
-    if (w != 0.f) {
-      const float* src = a.ws_o + r * D + d0;
+  for (int s0 = 0; s0 < t.Ps; s0 += 4) {
+    float w[4], v[4][N];
 #pragma unroll
-      for (int e = 0; e < N; ++e) o[e] = fmaf(w, src[e], o[e]);
+    for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u;
+      // rows past Ps are not read: their loads repeat the last valid row
+      const float* src = a.ws_o + (t.row0 + min(s, t.Ps - 1) * G) * D + d0;
+#pragma unroll
+      for (int e = 0; e < N; ++e) v[u][e] = src[e];
+      float ws = s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t.wl), min(s, 63)))
+                        : a.ws_l[t.row0 + s * G] * fast_exp2(a.ws_m[t.row0 + s * G] - t.Mx);
+      w[u] = s < t.Ps ? ws : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < N; ++e) o[e] = fmaf(w[u], w[u] != 0.f ? v[u][e] : 0.f, o[e]);
   }
 #pragma unroll
   for (int e = 0; e < N; ++e) o[e] *= t.inv;
@@ -484,21 +505,28 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     st.m[hh] = M;
   }
   if constexpr (HEADS) {
-    // The wave's result is final: row group 0 writes it.
-    if (r == 0) {
+    // The wave's result is final: row group 0 writes it (m and l are the
+    // same in every lane after the merge above).
+    if (a.finish) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
-        if (a.finish) {
-          const SharedTail tl = shared_tail(a, b, h0 + hh, sp.Ps, st.m[hh], st.l[hh]);
+        const SharedTail tl = shared_tail(a, b, h0 + hh, sp.Ps, st.m[hh], st.l[hh], lane);
+        if (r == 0) {
+          const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
           float o[EPL];
 #pragma unroll
           for (int e = 0; e < EPL; ++e) o[e] = st.o[hh][e];
           shared_tail_apply<D>(a, tl, c * EPL, o);
 #pragma unroll
           for (int e = 0; e < EPL; ++e) a.out[bh * D + c * EPL + e] = bad_ids ? __builtin_nanf("") : o[e];
-          continue;
         }
+      }
+      return;
+    }
+    if (r == 0) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
         const float inv = 1.f / st.l[hh];
         const size_t bhp = nparts == 1 ? 0 : ws_row(a, b, h0 + hh, slot);
         float* dst = nparts == 1 ? a.out + bh * D : a.ws_o + bhp * D;
@@ -544,8 +572,10 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     }
     const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
     if (a.finish) {
+      // every lane of the wave is here (G * D is a multiple of 64), with
+      // the same head
       float o[1] = {O};
-      shared_tail_apply<D>(a, shared_tail(a, b, h0 + hh, sp.Ps, M, L), d, o);
+      shared_tail_apply<D>(a, shared_tail(a, b, h0 + hh, sp.Ps, M, L, lane), d, o);
       a.out[bh * D + d] = bad ? __builtin_nanf("") : o[0];
       continue;
     }
@@ -897,8 +927,9 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       O = fmaf(sw[c * OROW + d], f, O);
     }
     if (!SHARED && a.finish) {
+      // the wave covers 64 dims of one column here, whole
       float o[1] = {O};
-      shared_tail_apply<D>(a, shared_tail(a, oseq, oh, ps, Mx, L), d, o);
+      shared_tail_apply<D>(a, shared_tail(a, oseq, oh, ps, Mx, L, lane), d, o);
       a.out[(static_cast<size_t>(oseq) * a.hq + oh) * D + d] = badc ? __builtin_nanf("") : o[0];
       continue;
     }
@@ -1090,7 +1121,7 @@ hipError_t launch_dt_d(const DecodeArgs& args, int B, int group, hipStream_t st)
   a.finish = zext == 1;
   if constexpr (DT != PA_DTYPE_F32) {
     if (a.n_groups > 0)
-      decode_phase1_mfma<DT, D, 16, kNbufMfma, true>
+      decode_phase1_mfma<DT, D, 16, kNbufShared, true>
           <<<dim3(a.hkv, a.n_groups, (a.max_shared_parts + kWaves - 1) / kWaves), kThreads, 0, st>>>(a);
   }
   dim3 grid(a.hkv, B, a.grid_parts);

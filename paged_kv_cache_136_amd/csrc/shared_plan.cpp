@@ -18,7 +18,10 @@
 //   * runs are cut greedily: a row joins the open group while the group's
 //     saving, (members - 1) x shared blocks, does not drop, up to
 //     16 / query_group members; a group needs at least two members and
-//     kMinShared shared blocks.
+//     kMinShared shared blocks;
+//   * groups are listed by shared blocks, most first: the shared pass
+//     dispatches its workgroups in group order, so the longest start first
+//     and the short ones fill in behind them instead of trailing alone.
 #include <algorithm>
 #include <numeric>
 #include <unordered_map>
@@ -128,6 +131,23 @@ extern "C" int pa_shared_plan(const int32_t* tables, int32_t max_blocks, const i
       if (hi - lo >= 2) emit(c, lo, hi, shared);
       lo = hi;
     }
+  }
+  // Longest groups first (stable, so equal groups keep their order).
+  if (ng > 1) {
+    std::vector<int32_t> idx(ng), rank(ng);
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+      return groups_out[static_cast<size_t>(x) * PA_SHARED_ROW] >
+             groups_out[static_cast<size_t>(y) * PA_SHARED_ROW];
+    });
+    std::vector<int32_t> rows(groups_out, groups_out + static_cast<size_t>(ng) * PA_SHARED_ROW);
+    for (int32_t i = 0; i < ng; ++i) {
+      std::copy_n(rows.data() + static_cast<size_t>(idx[i]) * PA_SHARED_ROW, PA_SHARED_ROW,
+                  groups_out + static_cast<size_t>(i) * PA_SHARED_ROW);
+      rank[idx[i]] = i;
+    }
+    for (int32_t b = 0; b < B; ++b)
+      if (seq_group_out[b] >= 0) seq_group_out[b] = rank[seq_group_out[b]];
   }
   // Private partitions and blocks left to each sequence: those after its
   // group's shared blocks (all of them when it is in no group; one

@@ -25,8 +25,9 @@ def check_plan(tables, lens, bs, pt, qg, seq_group, groups, max_parts, max_priva
     """Every rule a plan must satisfy (independent of how it was made), its
     bounds (the most shared partitions of a group, and the most partitions
     of any sequence after its group's shared blocks, one for an empty or
-    invalid length), and the planner's own floor of MIN_SHARED blocks.
-    Returns the block reads the plan saves."""
+    invalid length), and the planner's own floor of MIN_SHARED blocks and
+    group order (most shared blocks first).  Returns the block reads the
+    plan saves."""
     B = len(lens)
     pb = pt // bs
     assert seq_group.shape == (B,) and groups.shape[1:] == (ROW,)
@@ -49,6 +50,8 @@ def check_plan(tables, lens, bs, pt, qg, seq_group, groups, max_parts, max_priva
             assert S < nblk, "the last block must stay private"
             assert np.array_equal(tables[m, :S], tables[mem[0], :S])
     assert mx == max_parts
+    # this planner lists its groups longest first
+    assert all(int(groups[i, 0]) >= int(groups[i + 1, 0]) for i in range(len(groups) - 1))
     for b in range(B):
         if b not in seen:
             assert seq_group[b] == -1
