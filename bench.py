@@ -620,7 +620,7 @@ def run_fork_cow(args, torch, pkv, workloads):
                           "plain_pa_decode_ms": round(float(plain_ms.mean()), 5),
                           "plain_unique_gbs": round(float(unique[-1] / (plain_ms.mean() * 1e-3) / 1e9), 2)},
         "roofline": with_ceiling(
-            {"kernel": "pa_decode_shared (shared phase + private phase + reduce), unique bytes",
+            {"kernel": "pa_decode_shared (shared pass + private pass, which finishes each sequence), unique bytes",
              "bound": "hbm", "achieved": round(achieved_u, 2), "peak": PEAK_HBM_GBS,
              "unit": "GB/s", "frac": round(achieved_u / PEAK_HBM_GBS, 4),
              "traffic": load_traffic("pa_decode_shared_fork_cow"),
@@ -872,20 +872,19 @@ def run_beam(args, torch, pkv, workloads):
         d_tab = torch.from_numpy(tables).to(dev)
         d_len = torch.from_numpy(lens).to(dev)
         d_sg, d_gr = torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev)
-        if ev is not None:
-            ev[0].record()
+        def mark(i):
+            if ev is not None and ev[i] is not None:
+                ev[i].record()
+        mark(0)
         if d_pairs is not None:
             pkv.pa_copy_blocks([k], [v], d_pairs)
-        if ev is not None:
-            ev[1].record()
+        mark(1)
         pkv.pa_write_kv(k, v, kn, vn, d_slot)
-        if ev is not None:
-            ev[2].record()
+        mark(2)
         pkv.pa_decode_shared(q, k, v, d_tab, d_len, int(lens.max()), d_sg, d_gr, mx, mp,
                              max_private_blocks=splan.max_private_blocks, partition_tokens=512,
                              out=out, workspace=ws)
-        if ev is not None:
-            ev[3].record()
+        mark(3)
         uniq = len(np.unique(np.concatenate([tables[i, :-(-int(n) // bs)] for i, n in enumerate(lens)])))
         last[:] = [d_tab, d_len, tables, lens]
         return len(pairs), int(lens.sum()), uniq, host
@@ -895,15 +894,22 @@ def run_beam(args, torch, pkv, workloads):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[T(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Even steps record events around each phase (copy, write, decode);
+    # odd steps only at their start and end, since every event record
+    # leaves the GPU idle for a few microseconds: the step rate comes from
+    # the odd steps (all steps if there is one), the phases from the even.
+    evs = [[T(enable_timing=True) if i % 2 == 0 or j in (0, 3) else None for j in range(4)]
+           for i in range(args.steps)]
     info = []
     t0 = time.perf_counter()
     for e in evs:
         info.append(step(e))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    copy_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    phase = np.arange(args.steps) % 2 == 0
+    whole = ~phase if args.steps > 1 else phase
+    copy_ms = np.array([e[0].elapsed_time(e[1]) for e in evs if e[1] is not None])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs if e[1] is not None])
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     # The final batch again: plain pa_decode against pa_decode_shared with a
     # host plan (beams of a group share their prefix up to the last fork).
@@ -934,26 +940,28 @@ def run_beam(args, torch, pkv, workloads):
                                      partition_tokens=pt, out=out, workspace=ws2))}
     npairs = np.array([x[0] for x in info])
     toks = np.array([x[1] for x in info], dtype=np.float64)
-    uniq = np.array([x[2] for x in info], dtype=np.float64)
+    uniq_all = np.array([x[2] for x in info], dtype=np.float64)
+    uniq = uniq_all[phase]
     per_tok = 2 * H * D * 2
     block_kv = 2 * k[0].numel() * 2
-    copied = npairs * block_kv * 2              # read + write
-    with_pairs = npairs > 0
+    copied = npairs[phase] * block_kv * 2       # read + write
+    with_pairs = npairs[phase] > 0
     return {
         "metric": "beam search over the paged cache: decode KV GB/s and beams/s",
-        "value": round(float(toks.sum() * per_tok / (step_ms.sum() * 1e-3) / 1e9), 2), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(float(step_ms.mean()), 4), "higher_is_better": True, "scaling": "weak",
+        "value": round(float(toks[whole].sum() * per_tok / (step_ms[whole].sum() * 1e-3) / 1e9), 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(float(step_ms[whole].mean()), 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "beam", "groups": G, "beams": W, "prompt_lengths": "log-uniform [50, 2048], seed 7",
                    "kv_heads": H, "q_heads": cfg["hq"], "head_dim": D, "block_size": bs, "num_blocks": NB,
                    "partition_tokens": 512,
-                   "timing": "GPU events per step (COW copies + write + decode); value counts every "
-                             "beam's tokens (shared blocks once per beam)",
+                   "timing": "GPU events per step (COW copies + write + decode): odd steps at start and "
+                             "end only (value, ms_per_step, beams/s), even steps around each phase (copy, "
+                             "decode, roofline); value counts every beam's tokens (shared blocks once per beam)",
                    "decode": "pa_decode_shared with a per-step host plan"},
-        "beams_per_s": round(B * args.steps / (step_ms.sum() * 1e-3), 1),
+        "beams_per_s": round(B * int(whole.sum()) / (step_ms[whole].sum() * 1e-3), 1),
         "unique_kv_gbs": round(float(uniq.sum() * bs * per_tok / (dec_ms.sum() * 1e-3) / 1e9), 2),
-        "unique_kv_bytes_per_step": [int(u) * bs * per_tok for u in uniq],
+        "unique_kv_bytes_per_step": [int(u) * bs * per_tok for u in uniq_all],
         "cow_pairs_per_step": round(float(npairs.mean()), 1),
         "copy_ms_per_step": round(float(copy_ms.mean()), 4),
         "copy_gbs": round(float(copied[with_pairs].sum() / (copy_ms[with_pairs].sum() * 1e-3) / 1e9), 2)
@@ -962,7 +970,7 @@ def run_beam(args, torch, pkv, workloads):
         "host_ms_per_step": round(float(np.mean([x[3] for x in info]) * 1e3), 4),
         "final_batch_decode": cmp,
         "roofline": with_ceiling(
-            {"kernel": "pa_decode_shared (shared phase + private phase + reduce), unique bytes",
+            {"kernel": "pa_decode_shared (shared pass + private pass, which finishes each sequence), unique bytes",
              "bound": "hbm", "unit": "GB/s",
              "achieved": round(float(uniq.mean() * bs * per_tok / (dec_ms.mean() * 1e-3) / 1e9), 2),
              "peak": PEAK_HBM_GBS,

@@ -37,9 +37,18 @@ def _dev(*ts):
             raise ValueError("tensor must be contiguous")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    """Handle of the HIP stream to launch on: ``stream``, else torch's
+    current stream on the current device, read as a raw handle (building a
+    Stream object costs a few microseconds per call)."""
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(torch.cuda.current_device()))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _on(stream):

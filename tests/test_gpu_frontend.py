@@ -79,6 +79,19 @@ def test_prefill_rejects_host_out():
     torch.cuda.synchronize()
 
 
+def test_launch_stream_is_torchs_current_stream():
+    """Without a stream argument the calls launch on torch's current stream
+    (read as a raw handle): the default one, or a side stream made current."""
+    from paged_kv_cache_136_amd.ops import _stream
+    say("frontend current stream")
+    assert (_stream(None).value or 0) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert _stream(None).value == side.cuda_stream != 0
+    assert (_stream(None).value or 0) == torch.cuda.current_stream().cuda_stream
+    assert _stream(side).value == side.cuda_stream
+
+
 def test_decode_on_a_side_stream():
     """Defaulted out and workspace on a non-current stream; the current
     stream allocates and writes over freed memory meanwhile."""
