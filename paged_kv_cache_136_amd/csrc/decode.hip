@@ -70,6 +70,8 @@ constexpr int kNbuf = 3;           // K/V blocks in flight per wave, vector path
 constexpr int kNbufG4 = 1;         // same, fp32 query group of 4 (VGPR-limited)
 constexpr int kNbufMfma = 1;       // same, matrix-core path (groups of 4 and 8)
 constexpr int kNbufShared = 2;     // same, shared-prefix pass (a few long streams per group)
+constexpr int kNbufHeads = 1;      // same, four-heads private pass (runs of at most 8 blocks):
+                                   // 88 VGPRs, so five waves per SIMD hide its round trips
 
 struct DecodeArgs {
   float* out;            // [B][Hq][D]
@@ -1139,11 +1141,11 @@ hipError_t launch_dt_d(const DecodeArgs& args, int B, int group, hipStream_t st)
   dim3 grid_h(a.hkv / kWaves, B, a.grid_parts);
   switch (group) {
     case 1:
-      if (heads) decode_phase1<DT, D, 1, kNbuf, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      if (heads) decode_phase1<DT, D, 1, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 1, kNbuf><<<grid, kThreads, 0, st>>>(a);
       break;
     case 2:
-      if (heads) decode_phase1<DT, D, 2, kNbuf, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      if (heads) decode_phase1<DT, D, 2, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 2, kNbuf><<<grid, kThreads, 0, st>>>(a);
       break;
     case 4:
