@@ -611,17 +611,18 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 //       (2^-9 for bf16) does not reach the output (2^-18 after the split).
 //       C: lane (qa, t), reg r holds O[head t][dim 16n + 4qa + r], so the
 //       rescale by alpha is lane-local.
-// Work split: wave-owned partitions, merged per workgroup.  A workgroup of
-//       4 waves takes 4 consecutive partitions (grid z = partitions / 4);
-//       wave w streams every block of partition 4z + w, with no barrier
-//       until its partition is done.  The four results are then merged
+// Work split: four partitions per workgroup, merged once.  A workgroup of
+//       4 waves takes 4 consecutive partitions (grid z = partitions / 4),
+//       and wave w streams blocks w, w+4, w+8, ... of their range, with no
+//       barrier until its blocks are done.  The four results are then merged
 //       through LDS (each wave's staging space is free by then) and written
 //       once, at the group's first partition; the other three partitions
 //       get only m = -big, l = 0, which the reduce skips.  Writing every
 //       partition's G output rows instead cost the long GQA batch ~12% of
 //       its read bandwidth for 0.8% more bytes; with four waves splitting
 //       each partition the cost is per workgroup as well, and this form has
-//       a quarter as many.
+//       a quarter as many.  (Giving each wave one whole partition instead
+//       of every fourth block measured ~1% slower.)
 // SHARED: the workgroups run over (KV head, plan group, shared partitions).
 //       The 16 query columns are (member slot t / qgroup, query head
 //       t % qgroup) of the group's members, the blocks come from the table
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   // rotation is the workgroup's: its four waves take the same head, which
   // the merge below relies on.
   Prologue<NBUF> pro{};
-  if constexpr (!SHARED) pro = prologue<NBUF, 1>(a, wc.y, zp, 0, wc.z);
+  if constexpr (!SHARED) pro = prologue<NBUF, kWaves>(a, wc.y, wc.z * kWaves, w, wc.z);
   const int g = rotate_head(wc.g, a.hkv, SHARED ? wc.y + wc.z : pro.rot);
   const int h0 = g * (SHARED ? a.qgroup : G);
   // b: sequence (private) or plan group (shared).  n: tokens the blocks
@@ -719,13 +720,13 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     const SeqParts sp = seq_parts(a, b, pro.gi, nblk);
     nparts = sp.total;
     ps = sp.Ps;
-    // wave w streams private partition zp (slot Ps + zp); the workgroup's
-    // merged result goes to its first slot p0
+    // the workgroup streams private partitions p0 .. pend-1 (slots Ps +
+    // ...); its merged result goes to its first slot p0
     part = sp.Ps + zp;
     p0 = sp.Ps + wc.z * kWaves;
     if (p0 >= nparts) return;             // uniform over the workgroup
     pend = min(nparts, p0 + kWaves);
-    active = part < nparts;
+    active = true;
     short_grid = nparts - sp.Ps > static_cast<int>(gridDim.z) * kWaves;
     if (!valid || n == 0) {               // uniform: nparts == 1, p0 == 0
       const float fill = valid ? 0.f : __builtin_nanf("");
@@ -734,8 +735,10 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
       return;
     }
     trow = pro.trow;
-    first = sp.S + zp * a.part_blocks;
-    last = active ? min(nblk, first + a.part_blocks) : first;
+    // the workgroup's partitions [p0, pend), their blocks dealt to the
+    // waves in turn
+    first = sp.S + (p0 - sp.Ps) * a.part_blocks;
+    last = min(nblk, sp.S + (pend - sp.Ps) * a.part_blocks);
   }
 
   // Q^T as the QK B operand: column t, dims 32j + 8qa .. +8 (zero for a
@@ -849,22 +852,25 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     }
   };
 
-  // The partition's blocks in order, NBUF of them in flight.
+  // The wave's blocks in order, NBUF of them in flight: every block of its
+  // partition (shared), or blocks w, w+4, ... of the workgroup's (private).
+  constexpr int kStep = SHARED ? 1 : kWaves;
+  const int w0 = SHARED ? 0 : w;
   uint4 kr[NBUF][KSTEPS], vrg[NBUF][VLOADS];
 #pragma unroll
   for (int sl = 0; sl < NBUF; ++sl) {
-    const int jj = first + sl;
+    const int jj = first + w0 + sl * kStep;
     if (jj < last)
       load_block(check_id(!SHARED && a.seq_group == nullptr ? pro.spec[sl] : trow[jj]), kr[sl],
                  vrg[sl]);
   }
-  for (int j = first; j < last; j += NBUF) {
+  for (int j = first + w0; j < last; j += NBUF * kStep) {
 #pragma unroll
     for (int sl = 0; sl < NBUF; ++sl) {
-      const int jj = j + sl;
+      const int jj = j + sl * kStep;
       if (jj < last) {
         consume(kr[sl], vrg[sl], jj);
-        const int jn = jj + NBUF;
+        const int jn = jj + NBUF * kStep;
         if (jn < last) load_block(block_id(jn), kr[sl], vrg[sl]);
       }
     }
