@@ -42,6 +42,54 @@ from .ops import (pa_copy_blocks, pa_decode, pa_decode_shared, pa_decode_shared_
 from .scheduler import Scheduler
 
 
+_TORCH_INT = {np.dtype(np.int32): torch.int32, np.dtype(np.int64): torch.int64}
+
+
+class _Uploads:
+    """A step's small host arrays (slots, tables, lengths, plans) uploaded
+    through one pinned buffer: each upload fills the next piece of it and
+    starts an asynchronous copy on the current stream, so the host keeps
+    queueing work instead of waiting for each pageable copy to drain the
+    GPU.  reset() makes the whole buffer free again once every copy of the
+    previous step is done; a step that needs more grows it there.  A CPU
+    device (host-only tests) uploads directly."""
+
+    def __init__(self, dev, nbytes=1 << 20):
+        self.dev = dev
+        self.cuda = dev.type == "cuda"
+        self.want = nbytes
+        self.pin = None
+        self.off = 0
+        self.used = False
+        self.done = torch.cuda.Event() if self.cuda else None
+
+    def reset(self):
+        if self.used:
+            self.done.record()                # after everything queued so far
+            self.done.synchronize()
+            self.used = False
+        if self.cuda and (self.pin is None or self.pin.numel() < self.want):
+            self.pin = torch.empty(self.want, dtype=torch.uint8, pin_memory=True)
+            self.pin_np = self.pin.numpy()
+        self.off = 0
+
+    def __call__(self, a, dtype):
+        a = np.ascontiguousarray(a, dtype=dtype)
+        if not self.cuda:
+            return torch.from_numpy(a.copy())
+        n = (a.nbytes + 255) & ~255
+        if self.pin is None or self.off + n > self.pin.numel():
+            self.want = max(self.want, 2 * (self.off + n))
+            return torch.from_numpy(a.copy()).to(self.dev)     # this step only
+        self.pin_np[self.off:self.off + a.nbytes].view(a.dtype)[:] = a.reshape(-1)
+        src = self.pin[self.off:self.off + a.nbytes].view(_TORCH_INT[a.dtype]).view(a.shape)
+        dst = torch.empty(a.shape, dtype=src.dtype, device=self.dev)
+        dst.copy_(src, non_blocking=True)
+        self.off += n
+        self.used = True
+        return dst
+
+
 class DecodeEngine:
     """Paged KV caches (one K and one V tensor per layer, [num_blocks, bs,
     Hkv, D]), a block manager, a scheduler and a pinned host swap pool of
@@ -76,6 +124,7 @@ class DecodeEngine:
         self.host = torch.empty(max(host_slots, 1) * self.record_bytes, dtype=torch.uint8,
                                 pin_memory=self.dev.type == "cuda")
         self.ws = None                   # decode workspace, grown on demand
+        self.up = _Uploads(self.dev)
         self.step_no = 0
         self.host_seconds = 0.0          # time in scheduler / block-manager calls
         # With ``timing``, HIP events on the launch stream bracket the prompt
@@ -88,7 +137,7 @@ class DecodeEngine:
         self.sched.add_request(rid, prompt, max_new_tokens)
 
     def _i32(self, a):
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev)
+        return self.up(a, np.int32)
 
     def _event(self):
         if not self.timing or self.dev.type != "cuda":
@@ -114,6 +163,7 @@ class DecodeEngine:
         request yields its first token).
         Returns (plan, outs, prompt_outs, prompt_ids)."""
         self.step_no += 1
+        self.up.reset()
         h0 = time.perf_counter()
         plan = self.sched.step_arrays()
         self.host_seconds += time.perf_counter() - h0
@@ -125,11 +175,16 @@ class DecodeEngine:
         e_p0 = self._event()
         prompt_outs, prompt_ids = self._prompts(plan, kv_rows, q_rows)
         e_p1 = self._event()
+        # The decode's host work (tables, plan, uploads) needs only the
+        # block manager's state after this step's appends, so it runs here,
+        # while the GPU works through the prompts, rather than after the
+        # short writes below, where the GPU would wait for it.
+        dec = self._decode_prep(plan)
         # 3. copy-on-write copies, the appended tokens' K/V and swap-outs,
         #    epoch by epoch
         writes = plan["writes"]
         rows = [kv_rows(layer, "append", plan) for layer in range(self.L)] if len(writes) else None
-        slots = torch.from_numpy(plan["slots"].copy()).to(self.dev) if len(writes) else None
+        slots = self.up(plan["slots"], np.int64) if len(writes) else None
         w = c = so = 0
         for nw, nc, ns in plan["cuts"].tolist():
             self._cow_and_writes(plan, rows, slots, c, nc, w, nw)
@@ -141,7 +196,7 @@ class DecodeEngine:
         self._cow_and_writes(plan, rows, slots, c, len(plan["cow"]), w, len(writes))
         # 4. decode every layer
         e_d0 = self._event()
-        outs = self._decode(plan, q_rows)
+        outs = self._decode(dec, q_rows)
         e_d1 = self._event()
         if self.dev.type == "cuda":
             torch.cuda.current_stream().synchronize()
@@ -158,7 +213,7 @@ class DecodeEngine:
     def _prompts(self, plan, kv_rows, q_rows):
         if not len(plan["prefill_slots"]):
             return [], []
-        slots = torch.from_numpy(plan["prefill_slots"].copy()).to(self.dev)
+        slots = self.up(plan["prefill_slots"], np.int64)
         for layer in range(self.L):
             k, v = kv_rows(layer, "prompt", plan)
             pa_write_kv(self.k[layer], self.v[layer], k, v, slots)
@@ -175,9 +230,7 @@ class DecodeEngine:
         self.host_seconds += time.perf_counter() - h0
         qstart = np.zeros(len(ids) + 1, dtype=np.int32)
         qstart[1:] = np.cumsum(counts)
-        d_tab = torch.from_numpy(tables).to(self.dev)
-        d_len = torch.from_numpy(lens).to(self.dev)
-        d_qs = torch.from_numpy(qstart).to(self.dev)
+        d_tab, d_len, d_qs = self._i32(tables), self._i32(lens), self._i32(qstart)
         outs = []
         for layer in range(self.L):
             outs.append(pa_prefill(q_rows(layer, "prompt", int(qstart[-1])), self.k[layer],
@@ -192,11 +245,12 @@ class DecodeEngine:
                 k, v = rows[layer]
                 pa_write_kv(self.k[layer], self.v[layer], k[w0:w1], v[w0:w1], slots[w0:w1])
 
-    def _decode(self, plan, q_rows):
+    def _decode_prep(self, plan):
+        """Host side of the decode: the batch's tables and lengths, the
+        shared-prefix plan if one pays, their uploads and the workspace."""
         ids = plan["batch"]
-        outs = []
         if not len(ids):
-            return outs
+            return None
         B = len(ids)
         h0 = time.perf_counter()
         tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
@@ -210,16 +264,21 @@ class DecodeEngine:
             total = int((-(-lens.astype(np.int64) // self.bs)).sum())
             if len(groups) and saved >= self.shared_min_saving * total:
                 self.shared_groups += len(groups)
-                splan = (torch.from_numpy(sg).to(self.dev),
-                         torch.from_numpy(groups).to(self.dev), mx, mp, plan.max_private_blocks)
+                splan = (self._i32(sg), self._i32(groups), mx, mp, plan.max_private_blocks)
         self.host_seconds += time.perf_counter() - h0
         max_len = int(lens.max())
-        d_tab = torch.from_numpy(tables).to(self.dev)
-        d_len = torch.from_numpy(lens).to(self.dev)
+        d_tab, d_len = self._i32(tables), self._i32(lens)
         need = (pa_decode_shared_workspace_bytes if splan is not None else pa_decode_workspace_bytes)(
             B, self.hq, self.d, max_len, self.partition_tokens)
         if need and (self.ws is None or self.ws.numel() < need):
             self.ws = torch.empty(2 * need, dtype=torch.uint8, device=self.dev)
+        return B, d_tab, d_len, max_len, splan
+
+    def _decode(self, dec, q_rows):
+        outs = []
+        if dec is None:
+            return outs
+        B, d_tab, d_len, max_len, splan = dec
         for layer in range(self.L):
             q = q_rows(layer, "decode", B)
             if splan is None:
