@@ -244,27 +244,47 @@ struct SharedTail {
   float Mx, f, inv;      // overall max, private factor 2^(M - Mx), 1 / total sum
   float wl;              // weight of slot `lane` (lane < Ps), unnormalized
 };
-__device__ __forceinline__ SharedTail shared_tail(const DecodeArgs& a, int b, int h, int Ps,
-                                                  float M, float L, int lane) {
-  SharedTail t;
-  t.row0 = Ps > 0 ? ws_row(a, b, h, 0) : 0;
-  t.Ps = Ps;
-  const size_t G = static_cast<size_t>(a.qgroup);
+// The (m, l) of the first 64 shared slots, slot `lane` in each lane: the
+// finish's only reads that do not depend on the private result, so a caller
+// can issue them early and let them travel with its K/V loads.
+struct SlotPair {
+  size_t row0;
+  int Ps;
+  float m0, l0;
+};
+__device__ __forceinline__ SlotPair shared_slots(const DecodeArgs& a, int b, int h, int Ps,
+                                                 int lane) {
+  SlotPair p;
+  p.row0 = Ps > 0 ? ws_row(a, b, h, 0) : 0;
+  p.Ps = Ps;
   const bool in0 = lane < Ps;
-  const float m0 = in0 ? a.ws_m[t.row0 + lane * G] : -INFINITY;
-  const float l0 = in0 ? a.ws_l[t.row0 + lane * G] : 0.f;
-  float Mx = fmaxf(M, m0);
-  for (int s = lane + 64; s < Ps; s += 64) Mx = fmaxf(Mx, a.ws_m[t.row0 + s * G]);
+  const size_t G = static_cast<size_t>(a.qgroup);
+  p.m0 = in0 ? a.ws_m[p.row0 + lane * G] : -INFINITY;
+  p.l0 = in0 ? a.ws_l[p.row0 + lane * G] : 0.f;
+  return p;
+}
+__device__ __forceinline__ SharedTail shared_tail(const DecodeArgs& a, const SlotPair& p, float M,
+                                                  float L, int lane) {
+  SharedTail t;
+  t.row0 = p.row0;
+  t.Ps = p.Ps;
+  const size_t G = static_cast<size_t>(a.qgroup);
+  float Mx = fmaxf(M, p.m0);
+  for (int s = lane + 64; s < p.Ps; s += 64) Mx = fmaxf(Mx, a.ws_m[t.row0 + s * G]);
   Mx = group_max<1, 64>(Mx);
-  t.wl = in0 ? l0 * fast_exp2(m0 - Mx) : 0.f;
+  t.wl = lane < p.Ps ? p.l0 * fast_exp2(p.m0 - Mx) : 0.f;
   float Ls = t.wl;
-  for (int s = lane + 64; s < Ps; s += 64)
+  for (int s = lane + 64; s < p.Ps; s += 64)
     Ls = fmaf(a.ws_l[t.row0 + s * G], fast_exp2(a.ws_m[t.row0 + s * G] - Mx), Ls);
   Ls = group_sum<1, 64>(Ls);
   t.Mx = Mx;
   t.f = fast_exp2(M - Mx);
   t.inv = 1.f / fmaf(L, t.f, Ls);
   return t;
+}
+__device__ __forceinline__ SharedTail shared_tail(const DecodeArgs& a, int b, int h, int Ps,
+                                                  float M, float L, int lane) {
+  return shared_tail(a, shared_slots(a, b, h, Ps, lane), M, L, lane);
 }
 // o[e], the unnormalized private output at dim d0 + e, becomes the output.
 template <int D, int N>
@@ -475,6 +495,14 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       consume_block<DT, D, G, LPB, RPI, true>(st, q, kw, vw, a.scale_log2, r, vr);
   };
 
+  // HEADS with the finish: the shared slots' (m, l) go out with the first
+  // K/V loads (the finish would otherwise start with that round trip).
+  SlotPair pre[HEADS ? G : 1];
+  if constexpr (HEADS) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) pre[hh] = shared_slots(a, b, h0 + hh, a.finish ? sp.Ps : 0, lane);
+  }
+
   // This wave's blocks are first+wv, first+wv+4, ... (HEADS: every block
   // of the partition); NBUF of them are in flight in a register ring (the
   // loop is unrolled by NBUF so each ring slot is a fixed set of registers).
@@ -512,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     if (a.finish) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const SharedTail tl = shared_tail(a, b, h0 + hh, sp.Ps, st.m[hh], st.l[hh], lane);
+        const SharedTail tl = shared_tail(a, pre[hh], st.m[hh], st.l[hh], lane);
         if (r == 0) {
           const size_t bh = static_cast<size_t>(b) * a.hq + h0 + hh;
           float o[EPL];
