@@ -10,8 +10,10 @@ permutation).  One step is one pass of the whole hot path:
          pa_bm_export_batch into a pinned staging buffer, one async upload
          (the block tables only when they changed)
   device pa_copy_blocks when appends report copy-on-write pairs (none in
-         this workload), then for each layer pa_write_kv (the new token's
-         K/V) and pa_decode (split-KV phase 1 + reduce)
+         this workload), then for each layer pa_write_decode: the new
+         token's K/V written to its slot and the split-KV decode over it
+         (phase 1 + reduce) in one call; --separate-write times pa_write_kv
+         then pa_decode instead
 
 Sequences grow by one token per step, as in real decoding; the KV bytes of
 every step are counted exactly.  The metric is achieved KV GB/s (valid
@@ -61,6 +63,9 @@ def parse_args():
                         "FETCH_SIZE / WRITE_SIZE readings")
     p.add_argument("--read-gib", type=int, default=8,
                    help="size of the streaming-read ceiling measurement (0 = skip)")
+    p.add_argument("--separate-write", action="store_true",
+                   help="decode lines: pa_write_kv then pa_decode per layer instead of "
+                        "pa_write_decode")
     return p.parse_args()
 
 
@@ -318,13 +323,22 @@ class DecodeBench:
             pkv.pa_copy_blocks(self.k_layers, self.v_layers, self.d_pairs[:len(pairs)])
         max_len = int(self.lens0.max()) + s
         for layer in range(self.L):
-            pkv.pa_write_kv(self.k_layers[layer], self.v_layers[layer], self.k_new[layer],
-                            self.v_new[layer], self.d_slot)
+            if self.args.separate_write:
+                pkv.pa_write_kv(self.k_layers[layer], self.v_layers[layer], self.k_new[layer],
+                                self.v_new[layer], self.d_slot)
             if ev_pairs is not None:
                 ev_pairs[layer][0].record()
-            pkv.pa_decode(self.q[layer], self.k_layers[layer], self.v_layers[layer], self.d_tab,
-                          self.d_len, max_len, partition_tokens=self.partition,
-                          out=self.out[layer], workspace=self.ws)
+            if self.args.separate_write:
+                pkv.pa_decode(self.q[layer], self.k_layers[layer], self.v_layers[layer], self.d_tab,
+                              self.d_len, max_len, partition_tokens=self.partition,
+                              out=self.out[layer], workspace=self.ws)
+            else:
+                # the new token's slot is table[(len - 1) // 16] * 16 + (len - 1) % 16,
+                # the one append_slots returned
+                pkv.pa_write_decode(self.q[layer], self.k_layers[layer], self.v_layers[layer],
+                                    self.k_new[layer], self.v_new[layer], self.d_tab, self.d_len,
+                                    max_len, partition_tokens=self.partition,
+                                    out=self.out[layer], workspace=self.ws)
             if ev_pairs is not None and not (layer == self.L - 1 and ev_end is not None):
                 ev_pairs[layer][1].record()
         if ev_end is not None:
@@ -397,6 +411,8 @@ class DecodeBench:
                        "lengths": LENGTH_NOTES[self.name],
                        "mean_context": round(float(np.mean(step_tokens)) / self.B, 1),
                        "partition_tokens": self.partition,
+                       "kv_write": "pa_write_kv, then pa_decode" if self.args.separate_write
+                       else "in the decode call (pa_write_decode)",
                        "timing": "GPU events per step, 1 GiB cache flush between steps"
                                  if small else "wall clock over all steps"},
             "seqs_per_s": round(self.B * args.steps / timed_s, 1),
@@ -406,10 +422,11 @@ class DecodeBench:
             "gpu_step_ms_p10_p50_p90": [round(float(x), 4) for x in
                                         np.percentile(step_gpu_ms, [10, 50, 90])],
             "roofline": with_ceiling(
-                {"kernel": "pa_decode (split-KV phase 1 + reduce), one layer",
+                {"kernel": "pa_decode (split-KV phase 1 + reduce), one layer" if self.args.separate_write
+                 else "pa_write_decode (the new token's K/V write, split-KV phase 1 + reduce), one layer",
                  "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                  "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                 "traffic": load_traffic("pa_decode_" + self.name),
+                 "traffic": None if self.args.separate_write else load_traffic("pa_decode_" + self.name),
                  "avg_launch_ms": round(float(dec_ms.mean()), 5),
                  "algorithmic_bytes_per_launch": int(launch_bytes.mean())},
                 stream_read_ceiling(torch, self.pkv, args.read_gib)),

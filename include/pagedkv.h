@@ -461,6 +461,33 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
               int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_write_kv of each sequence's new token, then pa_decode, in one call
+ * ("qaqbuyan.com article 130", no-cache decode loop: the step computes the
+ * new token's K and V, appends them to the cache, then attends over every
+ * cached token including it; "P06 · BlockManager" spec overview: the slot
+ * of position pos is table[pos / bs] * bs + pos % bs).  For every sequence b
+ * with a valid context_lens[b] = n >= 1, the row of position n - 1 (the new
+ * token, whose slot was appended before this call) is written from
+ * k_new / v_new to that slot of k_cache / v_cache, and the attention is
+ * computed as pa_decode computes it after that write: the same output, bit
+ * for bit, and the same cache bytes as pa_write_kv followed by pa_decode.
+ * The decode reads the new row from k_new / v_new rather than back from
+ * memory.
+ *   k_new, v_new: device [B][num_kv_heads][head_dim] in `dtype`, 16-byte
+ *     aligned, read only.
+ *   k_cache, v_cache: written at the new tokens' slots only.
+ * Other arguments, supported shapes, workspace and errors as pa_decode.  A
+ * sequence with n == 0 or an invalid length writes nothing; one whose block
+ * for position n - 1 is outside [0, num_blocks) writes nothing (and, as in
+ * pa_decode, gets NaN rows).  Precondition, as for pa_write_kv: no two
+ * sequences' new tokens share a slot (copy-on-write has been done). */
+int pa_write_decode(float* out, const void* q, void* k_cache, void* v_cache, const void* k_new,
+                    const void* v_new, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, float scale, int32_t partition_tokens,
+                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* pa_decode without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments, semantics, supported shapes and

@@ -66,6 +66,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // DATA_FORMAT = 32-bit, everything else 0.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kLoadAux = 2;        // cache policy of K/V loads: nontemporal (read once)
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their
+// maxima (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8): wait for every vector memory operation of the wave, stores included.
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kNbuf = 3;           // K/V blocks in flight per wave, vector path (groups of 1, 2)
 constexpr int kNbufG4 = 1;         // same, fp32 query group of 4 (VGPR-limited)
 constexpr int kNbufMfma = 1;       // same, matrix-core path (groups of 4 and 8)
@@ -81,6 +85,8 @@ struct DecodeArgs {
   const char* q;         // [B][Hq][D]
   const char* k;         // [num_blocks][16][Hkv][D]
   const char* v;
+  char* k_w;             // the same caches, written by pa_write_decode only
+  char* v_w;
   const int32_t* tables; // [B][max_blocks]
   const int32_t* lens;   // [B]
   int32_t max_blocks;
@@ -103,6 +109,11 @@ struct DecodeArgs {
   int32_t finish;            // 1: one workgroup of the private grid holds all of a
                              // sequence's private partitions, so phase 1 merges them with
                              // the shared slots and writes out[]; no reduce runs
+  // pa_write_decode: each valid, non-empty sequence's new token (position
+  // len - 1) has its K/V row here instead of in the cache; phase 1 writes
+  // it to its slot and uses it (null otherwise).
+  const char* k_new;         // [B][Hkv][D]
+  const char* v_new;
 };
 
 __device__ __forceinline__ bool len_valid(int n, const DecodeArgs& a) {
@@ -382,8 +393,12 @@ __device__ __forceinline__ void consume_block(RowState<DT, D, G>& st, const uint
 // writes its own result (no merge through LDS).  Used for the private pass
 // of a shared-prefix plan, whose partitions are often a block or two long:
 // one head per workgroup would leave three of its four waves idle there.
-template <int DT, int D, int G, int NBUF, bool HEADS = false>
+// APPEND (pa_write_decode, no plan): the wave that reads a sequence's last
+// block takes the new token's row from k_new / v_new instead of the cache
+// and stores it there, once per (sequence, KV head).
+template <int DT, int D, int G, int NBUF, bool HEADS = false, bool APPEND = false>
 __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
+  static_assert(!(HEADS && APPEND), "the four-heads mapping serves plans only");
   constexpr int ELEM = ElemTraits<DT>::bytes;
   constexpr int EPL = 16 / ELEM;          // elements per lane per load
   constexpr int LPR = D * ELEM / 16;      // lanes per token row
@@ -487,6 +502,17 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       vw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             vd, lane_off, i * RPI * row_bytes, kLoadAux));
   };
+  // APPEND: the wave that reads the sequence's last block takes the new
+  // token's row (len - 1) of head g from k_new / v_new in place of the
+  // loaded one, and stores it to the cache when the block id is valid (an
+  // invalid one flags the sequence and writes nothing).  Nothing reads that
+  // row back in this launch.
+  uint4 knew{}, vnew{};
+  if constexpr (APPEND) {
+    const size_t src = ((static_cast<size_t>(b) * a.hkv + g) * D + c * EPL) * ELEM;
+    knew = *reinterpret_cast<const uint4*>(a.k_new + src);
+    vnew = *reinterpret_cast<const uint4*>(a.v_new + src);
+  }
   auto consume = [&](const uint4 (&kw)[LPB], const uint4 (&vw)[LPB], int gblk) {
     const int vr = n - gblk * kBlock;
     if (vr >= kBlock)
@@ -517,6 +543,25 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     for (int sl = 0; sl < NBUF; ++sl) {
       const int jj = j + sl * kStep;
       if (jj < last) {
+        if constexpr (APPEND) {
+          if (jj == nblk - 1) {
+            const int nr = n - 1 - jj * kBlock;
+#pragma unroll
+            for (int i = 0; i < LPB; ++i) {
+              const bool mine = i * RPI + r == nr;
+              kr[sl][i] = select4(mine, knew, kr[sl][i]);
+              vr[sl][i] = select4(mine, vnew, vr[sl][i]);
+            }
+            const int32_t id = trow[jj];
+            if (r == nr % RPI && id >= 0 && id < a.num_blocks) {
+              const size_t off = static_cast<size_t>(id) * block_bytes +
+                                 static_cast<size_t>(nr) * row_bytes +
+                                 static_cast<size_t>(g * D + c * EPL) * ELEM;
+              *reinterpret_cast<uint4*>(a.k_w + off) = knew;
+              *reinterpret_cast<uint4*>(a.v_w + off) = vnew;
+            }
+          }
+        }
         consume(kr[sl], vr[sl], jj);
         const int jn = jj + NBUF * kStep;
         if (jn < last) load_block(block_id(jn), kr[sl], vr[sl]);
@@ -657,8 +702,9 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 //       row of the group's first slot, and each column's (m, l, o) goes to
 //       its member's workspace row.  Every member checks that its own table
 //       holds the same ids over the partition (NaN output otherwise).
-template <int DT, int D, int G, int NBUF, bool SHARED>
+template <int DT, int D, int G, int NBUF, bool SHARED, bool APPEND = false>
 __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
+  static_assert(!(SHARED && APPEND), "pa_write_decode takes no plan");
   static_assert(DT != PA_DTYPE_F32 && (D == 64 || D == 128), "shape");
   static_assert(SHARED ? G == 16 : (G == 4 || G == 8), "query columns");
   using M = MfmaOps<DT>;
@@ -884,6 +930,28 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   // partition (shared), or blocks w, w+4, ... of the workgroup's (private).
   constexpr int kStep = SHARED ? 1 : kWaves;
   const int w0 = SHARED ? 0 : w;
+  // APPEND: the wave that reads the sequence's last block first stores the
+  // new token's row of head g there (the lanes of row len - 1, each its
+  // 16-byte chunk, dims 8vc .. +8, when the block id is valid: an invalid
+  // one flags the sequence and writes nothing), waits for the stores, and
+  // then reads the row back with its other loads; no other wave reads that
+  // row in this launch.  (Taking the row into the loaded registers instead,
+  // as the vector kernel does, costs this kernel a wave per SIMD.)
+  if constexpr (APPEND) {
+    const int lb = nblk - 1;
+    if (lb >= first + w0 && lb < last && (lb - first - w0) % kStep == 0) {
+      const int nr = n - 1 - lb * kBlock;
+      const int32_t id = trow[lb];
+      if (vr == nr % RPI && id >= 0 && id < a.num_blocks) {
+        const size_t src = ((static_cast<size_t>(b) * a.hkv + g) * D + 8 * vc) * ELEM;
+        const size_t off = static_cast<size_t>(id) * block_bytes + static_cast<size_t>(nr) * row_bytes +
+                           static_cast<size_t>(g * D + 8 * vc) * ELEM;
+        *reinterpret_cast<uint4*>(a.k_w + off) = *reinterpret_cast<const uint4*>(a.k_new + src);
+        *reinterpret_cast<uint4*>(a.v_w + off) = *reinterpret_cast<const uint4*>(a.v_new + src);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+  }
   uint4 kr[NBUF][KSTEPS], vrg[NBUF][VLOADS];
 #pragma unroll
   for (int sl = 0; sl < NBUF; ++sl) {
@@ -1173,22 +1241,35 @@ hipError_t launch_dt_d(const DecodeArgs& args, int B, int group, hipStream_t st)
   const bool heads = kHeadsOk && a.n_groups > 0 && a.hkv % kWaves == 0 &&
                      a.private_blocks > 0 && a.private_blocks <= kHeadsMaxBlocks;
   dim3 grid_h(a.hkv / kWaves, B, a.grid_parts);
+  const bool append = a.k_new != nullptr;
   switch (group) {
     case 1:
       if (heads) decode_phase1<DT, D, 1, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      else if (append) decode_phase1<DT, D, 1, kNbuf, false, true><<<grid, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 1, kNbuf><<<grid, kThreads, 0, st>>>(a);
       break;
     case 2:
       if (heads) decode_phase1<DT, D, 2, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      else if (append) decode_phase1<DT, D, 2, kNbuf, false, true><<<grid, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 2, kNbuf><<<grid, kThreads, 0, st>>>(a);
       break;
     case 4:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 4, kNbufMfma, false><<<grid_w, kThreads, 0, st>>>(a);
-      else decode_phase1<DT, D, 4, kNbufG4><<<grid, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) {
+        if (append) decode_phase1_mfma<DT, D, 4, kNbufMfma, false, true><<<grid_w, kThreads, 0, st>>>(a);
+        else decode_phase1_mfma<DT, D, 4, kNbufMfma, false><<<grid_w, kThreads, 0, st>>>(a);
+      } else {
+        if (append) decode_phase1<DT, D, 4, kNbufG4, false, true><<<grid, kThreads, 0, st>>>(a);
+        else decode_phase1<DT, D, 4, kNbufG4><<<grid, kThreads, 0, st>>>(a);
+      }
       break;
     case 8:
-      if constexpr (DT != PA_DTYPE_F32) decode_phase1_mfma<DT, D, 8, kNbufMfma, false><<<grid_w, kThreads, 0, st>>>(a);
-      else decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a);
+      if constexpr (DT != PA_DTYPE_F32) {
+        if (append) decode_phase1_mfma<DT, D, 8, kNbufMfma, false, true><<<grid_w, kThreads, 0, st>>>(a);
+        else decode_phase1_mfma<DT, D, 8, kNbufMfma, false><<<grid_w, kThreads, 0, st>>>(a);
+      } else {
+        if (append) decode_phase1<DT, D, 8, 2, false, true><<<grid, kThreads, 0, st>>>(a);
+        else decode_phase1<DT, D, 8, 2><<<grid, kThreads, 0, st>>>(a);
+      }
       break;
     default: return hipErrorInvalidValue;
   }
@@ -1304,7 +1385,8 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
                 int32_t num_blocks, float scale, int32_t partition_tokens, int32_t dtype,
                 const int32_t* seq_group, const int32_t* groups, int32_t n_groups,
                 int32_t max_shared_parts, int32_t max_private_parts, int32_t max_private_blocks,
-                void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false) {
+                void* workspace, size_t workspace_bytes, void* stream, bool use_scratch = false,
+                const void* k_new = nullptr, const void* v_new = nullptr) {
   const std::string name(fn);
   auto err_ = [&](int code, const std::string& msg) { return fail(code, name + ": " + msg); };
   if (B < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_blocks <= 0)
@@ -1332,6 +1414,10 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache)) & 15)
     return err_(PA_ERR_INVALID, "q and caches must be 16-byte aligned");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return err_(PA_ERR_INVALID, "k_new and v_new must both be given");
+  if (k_new && ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15))
+    return err_(PA_ERR_INVALID, "k_new and v_new must be 16-byte aligned");
   const size_t block_bytes = static_cast<size_t>(num_kv_heads) * head_dim * kBlock *
                              (dtype == PA_DTYPE_F32 ? 4 : 2);
   if (block_bytes >= (static_cast<size_t>(1) << 31))
@@ -1384,6 +1470,14 @@ int decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
   a.q = static_cast<const char*>(q);
   a.k = static_cast<const char*>(k_cache);
   a.v = static_cast<const char*>(v_cache);
+  if (k_new) {
+    // the caches are the caller's writable device memory (pa_write_decode
+    // takes them as non-const pointers)
+    a.k_w = static_cast<char*>(const_cast<void*>(k_cache));
+    a.v_w = static_cast<char*>(const_cast<void*>(v_cache));
+    a.k_new = static_cast<const char*>(k_new);
+    a.v_new = static_cast<const char*>(v_new);
+  }
   a.tables = block_tables;
   a.lens = context_lens;
   a.max_blocks = max_blocks_per_seq;
@@ -1447,6 +1541,22 @@ extern "C" int pa_decode_shared(float* out, const void* q, const void* k_cache,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
                      dtype, seq_group, groups, n_groups, max_shared_parts, max_private_parts,
                      max_private_blocks, workspace, workspace_bytes, stream);
+}
+
+extern "C" int pa_write_decode(float* out, const void* q, void* k_cache, void* v_cache,
+                               const void* k_new, const void* v_new,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, float scale,
+                               int32_t partition_tokens, int32_t dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID, "pa_write_decode: null pointer");
+  return decode_impl("pa_write_decode", out, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, B, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
+                     dtype, nullptr, nullptr, 0, 0, 0, 0, workspace, workspace_bytes, stream, false,
+                     k_new, v_new);
 }
 
 extern "C" size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }

@@ -222,6 +222,27 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
     return out
 
 
+def pa_write_decode(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens, max_context_len,
+                    scale=None, partition_tokens=512, out=None, workspace=None, stream=None):
+    """pa_write_kv of each sequence's new token followed by pa_decode, in
+    one call: k_new / v_new [B, Hkv, D] (the caches' dtype) are the K/V rows
+    of the token at position context_lens[b] - 1, written to its slot
+    through the block table while the decode reads it.  Returns float32
+    out [B, Hq, D]."""
+    out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                 max_context_len, scale, partition_tokens, out, workspace, stream)
+    _dev(k_new, v_new)
+    B, hkv, d = q.shape[0], k_cache.shape[2], k_cache.shape[3]
+    if k_new.shape != (B, hkv, d) or v_new.shape != (B, hkv, d):
+        raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    if not (k_new.dtype == v_new.dtype == k_cache.dtype):
+        raise ValueError("k_new and v_new must share the caches' dtype")
+    # head = (out, q, k, v, tables, max_blocks, lens, max_len, B, hq, hkv, d, bs, nb, scale, pt, dtype)
+    check(lib().pa_write_decode(*head[:4], k_new.data_ptr(), v_new.data_ptr(), *head[4:], *ws,
+                                _stream(stream)))
+    return out
+
+
 def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
                       scale=None, partition_tokens=512, stream=None):
     """pa_decode whose split-KV partials live in the library's per-device

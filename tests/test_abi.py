@@ -242,3 +242,22 @@ def test_noalloc_decode_rejects_oversize_before_touching_the_gpu():
     assert st == 2 and b"scratch" in L.pa_last_error()
     st = L.pa_decode_noalloc(p, p, p, p, p, 8, p, 64, 2, 8, 2, 96, 16, 64, 0.088, 0, 1, None)
     assert st == 3 and b"head_dim" in L.pa_last_error()
+
+
+def test_write_decode_validates_before_touching_the_gpu():
+    """pa_write_decode rejects missing or misaligned new rows, and every
+    argument pa_decode rejects, before its first HIP call."""
+    from paged_kv_cache_136_amd import lib
+    L = lib()
+    keep = []
+    p = _aligned_host_ptr(keep)
+
+    def call(k_new=p, v_new=p, head_dim=128, B=2):
+        # out, q, k, v, k_new, v_new, tables, max_blocks, lens, max_len, B, Hq, Hkv, D,
+        # bs, num_blocks, scale, partition_tokens, dtype, workspace, bytes, stream
+        return L.pa_write_decode(p, p, p, p, k_new, v_new, p, 8, p, 64, B, 8, 2, head_dim, 16,
+                                 64, 0.088, 512, 1, p, 1 << 20, None)
+    assert call(k_new=None) == 2 and b"null" in L.pa_last_error()
+    assert call(v_new=p + 4) == 2 and b"16-byte aligned" in L.pa_last_error()
+    assert call(head_dim=96) == 3 and b"head_dim" in L.pa_last_error()
+    assert call(k_new=None, v_new=None, B=0) == 0          # B == 0 launches nothing
