@@ -763,7 +763,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     const int P = shared_parts_of(S, a.part_blocks);
     if (p0 >= P) return;
     pend = min(P, p0 + kWaves);
-    active = part < P;
+    active = true;
     const int slots = PA_SHARED_MAX_MEMBERS / a.qgroup;
     // Membership as the private kernels decide it.
     auto member = [&](int sl) -> int {
@@ -780,9 +780,11 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     const int lead = row[1];
     src_ok = lead >= 0 && lead < a.batch;
     trow = a.tables + static_cast<size_t>(src_ok ? lead : 0) * a.max_blocks;
-    first = part * a.part_blocks;
-    // within max_blocks: a member exists
-    last = src_ok && active ? min(first + a.part_blocks, S) : first;
+    // The workgroup's partitions [p0, pend), their blocks dealt to the
+    // waves in turn, so a group with fewer than four partitions still
+    // keeps every wave streaming (within max_blocks: a member exists).
+    first = p0 * a.part_blocks;
+    last = src_ok ? min(pend * a.part_blocks, S) : first;
     n = last * kBlock;                               // shared blocks are full
     nblk = last;
     nparts = 0;
@@ -926,10 +928,10 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
     }
   };
 
-  // The wave's blocks in order, NBUF of them in flight: every block of its
-  // partition (shared), or blocks w, w+4, ... of the workgroup's (private).
-  constexpr int kStep = SHARED ? 1 : kWaves;
-  const int w0 = SHARED ? 0 : w;
+  // The wave's blocks in order, NBUF of them in flight: blocks w, w+4, ...
+  // of the workgroup's range (its four partitions, or fewer).
+  constexpr int kStep = kWaves;
+  const int w0 = w;
   // APPEND: the wave that reads the sequence's last block first stores the
   // new token's row of head g there (the lanes of row len - 1, each its
   // 16-byte chunk, dims 8vc .. +8, when the block id is valid: an invalid
@@ -977,12 +979,13 @@ __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
   lsum = group_sum<16, 64>(lsum);
   bool bad = bad_ids || !src_ok;
   if constexpr (SHARED) {
-    // Member slot t's own table must hold the source row's ids over
-    // [first, last): lane qa of slot t compares blocks first + qa, +4, ...
+    // Member slot t's own table must hold the source row's ids over the
+    // wave's blocks: lane qa of slot t compares blocks w + 4qa, +16, ...
+    // (the four waves together cover [first, last)).
     bool mismatch = false;
     if (chk_seq >= 0 && src_ok) {
       const int32_t* mrow = a.tables + static_cast<size_t>(chk_seq) * a.max_blocks;
-      for (int j = first + qa; j < last; j += 4) mismatch |= mrow[j] != trow[j];
+      for (int j = first + w0 + kStep * qa; j < last; j += 4 * kStep) mismatch |= mrow[j] != trow[j];
     }
     const float mis = group_max<16, 64>(mismatch ? 1.f : 0.f);   // slot t's flag, every qa lane
     bad |= __shfl(mis, t / a.qgroup) != 0.f;                      // the flag of column t's slot
