@@ -727,7 +727,8 @@ def run_serve(args, torch, pkv, workloads):
     scheduler's decisions, then swap copies, the admitted prompts' K/V
     writes and their attention over the uncached suffix (pa_prefill, 32
     layers), copy-on-write copies, the batch's K/V writes and 32 decode
-    launches, and a stream sync.  Reported: sustained generated tokens/s,
+    launches (the writes inside them, pa_write_decode, on steps without a
+    preemption), and a stream sync.  Reported: sustained generated tokens/s,
     decode KV GB/s over the timed steps, and the GPU time of the prompt
     phase and of the decode phase (HIP events on the launch stream)."""
     from paged_kv_cache_136_amd.engine import DecodeEngine
@@ -767,17 +768,19 @@ def run_serve(args, torch, pkv, workloads):
     torch.cuda.synchronize()
     tokens = kv_bytes = prompt_rows = prompt_flops = 0
     counts = {"admitted": 0, "finished": 0, "preempted": 0, "resumed": 0, "recomputed": 0}
-    host0, pms0, dms0 = eng.host_seconds, eng.prompt_ms, eng.decode_ms
+    host0, pms0, dms0, fold0 = eng.host_seconds, eng.prompt_ms, eng.decode_ms, eng.folded_steps
     t0 = time.perf_counter()
     for _ in range(args.steps):
         plan, outs, prompt_outs, prompt_ids = eng.step(kv_rows, q_rows, sample)
         n_batch = len(plan["batch"])
         tokens += n_batch + len(prompt_ids)
-        if n_batch:
-            kv_bytes += sum(eng.bm.seq_len(int(i)) for i in plan["batch"]) * per_tok
+        # the lengths the engine exported for its launches (no host calls
+        # of the bench's own inside the timed steps)
+        kv_bytes += int(eng.last_decode_lens.astype(np.int64).sum()) * per_tok
+        plens = dict(zip(prompt_ids, eng.last_prompt_lens.tolist()))
         for rid, n in zip(plan["admitted"].tolist(), plan["prefill_counts"].tolist()):
-            if rid in prompt_ids:
-                total = eng.bm.seq_len(rid)
+            if rid in plens:
+                total = plens[rid]
                 prompt_rows += n
                 # causal: row i of the suffix attends to total - n + i + 1 keys
                 prompt_flops += 4 * D * H * L * (n * (total - n) + n * (n + 1) // 2)
@@ -798,10 +801,13 @@ def run_serve(args, torch, pkv, workloads):
                    "requests": n_req, "prompts": "log-uniform [50, 2048], half after a shared "
                    "256-token system prompt", "budgets": "log-uniform [16, 512]",
                    "timing": "wall clock over whole engine steps (host scheduling, copies, "
-                             "prompt writes and attention, writes, 32 decode launches, one sync "
-                             "per step)",
+                             "prompt writes and attention, the batch's writes, 32 decode "
+                             "launches, one sync per step)",
+                   "kv_write": "inside the decode launches (pa_write_decode) on steps without "
+                               "a preemption, else pa_write_kv",
                    "partition_tokens": pt, "shared_prefix_decode": shared},
         "shared_groups_per_step": round(eng.shared_groups / max(eng.step_no, 1), 2),
+        "write_folded_steps": eng.folded_steps - fold0,
         "kv_gbs": round(kv_bytes / wall / 1e9, 2),
         "pct_hbm_peak": round(100 * kv_bytes / wall / 1e9 / PEAK_HBM_GBS, 2),
         "decode_phase_ms_per_step": round(decode_ms / args.steps, 4),

@@ -15,7 +15,13 @@ require:
      before it, then its swap-out copies (pa_swap_out) -- a victim's own
      write lands before its blocks are copied out, and blocks it frees are
      written again only afterwards; then the remaining copies and writes;
-  4. decode (pa_decode) of the batch, every layer; with ``shared_prefix``
+  4. decode (pa_decode) of the batch, every layer.  When no preemption
+     split the step's writes and the batch is exactly the requests that
+     appended, in the same order (the usual step), each layer's writes of
+     the batch's new tokens happen inside its decode instead (pa_write_decode:
+     the token at position len - 1 is the one each of them appended), and
+     step 3 is only the copies; a step decoded through a shared-prefix plan
+     keeps its writes in step 3.  With ``shared_prefix``
      the host plans shared-prefix groups once per step (pa_shared_plan) and
      every layer decodes with pa_decode_shared, reading blocks that several
      sequences share (a common system prompt, forks) once per group -- when
@@ -38,7 +44,7 @@ import torch
 from .block_manager import BlockManager
 from .ops import (pa_copy_blocks, pa_decode, pa_decode_shared, pa_decode_shared_workspace_bytes,
                   pa_decode_workspace_bytes, pa_prefill, pa_shared_plan, pa_swap_in, pa_swap_out,
-                  pa_write_kv, swap_record_bytes)
+                  pa_write_decode, pa_write_kv, swap_record_bytes)
 from .scheduler import Scheduler
 
 
@@ -124,6 +130,12 @@ class DecodeEngine:
         self.host = torch.empty(max(host_slots, 1) * self.record_bytes, dtype=torch.uint8,
                                 pin_memory=self.dev.type == "cuda")
         self.ws = None                   # decode workspace, grown on demand
+        self.folded_steps = 0            # steps whose batch writes ran inside the decode
+        # The last step's context lengths of the decode batch (after its
+        # appends, plan["batch"] order) and of the prompt-attention requests
+        # (prompt_ids order); empty when there were none.
+        self.last_decode_lens = np.zeros(0, np.int32)
+        self.last_prompt_lens = np.zeros(0, np.int32)
         self.up = _Uploads(self.dev)
         self.step_no = 0
         self.host_seconds = 0.0          # time in scheduler / block-manager calls
@@ -184,7 +196,11 @@ class DecodeEngine:
         #    epoch by epoch
         writes = plan["writes"]
         rows = [kv_rows(layer, "append", plan) for layer in range(self.L)] if len(writes) else None
-        slots = self.up(plan["slots"], np.int64) if len(writes) else None
+        # The batch's writes fold into its decode when nothing orders them
+        # against a swap-out and every decoded request appended exactly once.
+        fold = (dec is not None and dec[4] is None and len(writes) > 0 and not len(plan["cuts"])
+                and np.array_equal(writes, plan["batch"]))
+        slots = self.up(plan["slots"], np.int64) if len(writes) and not fold else None
         w = c = so = 0
         for nw, nc, ns in plan["cuts"].tolist():
             self._cow_and_writes(plan, rows, slots, c, nc, w, nw)
@@ -193,10 +209,12 @@ class DecodeEngine:
                 pa_swap_out(self.k, self.v, self._i32(sw[:, 0]), self.host,
                             host_slots=self._i32(sw[:, 1]))
             w, c, so = nw, nc, ns
-        self._cow_and_writes(plan, rows, slots, c, len(plan["cow"]), w, len(writes))
+        self._cow_and_writes(plan, rows, slots, c, len(plan["cow"]), w,
+                             w if fold else len(writes))
         # 4. decode every layer
         e_d0 = self._event()
-        outs = self._decode(dec, q_rows)
+        self.folded_steps += fold
+        outs = self._decode(dec, q_rows, rows if fold else None)
         e_d1 = self._event()
         if self.dev.type == "cuda":
             torch.cuda.current_stream().synchronize()
@@ -211,6 +229,7 @@ class DecodeEngine:
         return plan, outs, prompt_outs, prompt_ids
 
     def _prompts(self, plan, kv_rows, q_rows):
+        self.last_prompt_lens = np.zeros(0, np.int32)
         if not len(plan["prefill_slots"]):
             return [], []
         slots = self.up(plan["prefill_slots"], np.int64)
@@ -228,6 +247,7 @@ class DecodeEngine:
         h0 = time.perf_counter()
         tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
         self.host_seconds += time.perf_counter() - h0
+        self.last_prompt_lens = lens
         qstart = np.zeros(len(ids) + 1, dtype=np.int32)
         qstart[1:] = np.cumsum(counts)
         d_tab, d_len, d_qs = self._i32(tables), self._i32(lens), self._i32(qstart)
@@ -249,11 +269,13 @@ class DecodeEngine:
         """Host side of the decode: the batch's tables and lengths, the
         shared-prefix plan if one pays, their uploads and the workspace."""
         ids = plan["batch"]
+        self.last_decode_lens = np.zeros(0, np.int32)
         if not len(ids):
             return None
         B = len(ids)
         h0 = time.perf_counter()
         tables, lens = self.bm.export_batch(ids, self._table_width(ids), pad_block=0)
+        self.last_decode_lens = lens
         splan = None
         if self.shared_prefix:
             plan = pa_shared_plan(tables, lens, self.bs, self.partition_tokens,
@@ -274,14 +296,21 @@ class DecodeEngine:
             self.ws = torch.empty(2 * need, dtype=torch.uint8, device=self.dev)
         return B, d_tab, d_len, max_len, splan
 
-    def _decode(self, dec, q_rows):
+    def _decode(self, dec, q_rows, rows=None):
+        """Every layer's decode; ``rows`` (per layer, the batch's new K/V
+        rows in batch order) makes it write them first."""
         outs = []
         if dec is None:
             return outs
         B, d_tab, d_len, max_len, splan = dec
         for layer in range(self.L):
             q = q_rows(layer, "decode", B)
-            if splan is None:
+            if rows is not None:
+                k, v = rows[layer]
+                outs.append(pa_write_decode(q, self.k[layer], self.v[layer], k, v, d_tab, d_len,
+                                            max_len, partition_tokens=self.partition_tokens,
+                                            workspace=self.ws))
+            elif splan is None:
                 outs.append(pa_decode(q, self.k[layer], self.v[layer], d_tab, d_len, max_len,
                                       partition_tokens=self.partition_tokens, workspace=self.ws))
             else:

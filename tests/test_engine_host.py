@@ -66,6 +66,16 @@ def _decode(q, k, v, tables, lens, max_len, *plan, partition_tokens=512, workspa
     return torch.from_numpy(out).float()
 
 
+def _write_decode(q, k, v, kn, vn, tables, lens, max_len, **kw):
+    # each sequence's new rows at the slot of its position len - 1, then the
+    # decode over the caches that now hold them
+    bs = k.shape[1]
+    n = lens.long()
+    slots = tables.long()[torch.arange(len(n)), (n - 1) // bs] * bs + (n - 1) % bs
+    _write_kv(k, v, kn, vn, slots)
+    return _decode(q, k, v, tables, lens, max_len)
+
+
 def _prefill(q, k, v, tables, qstart, lens, max_q, **kw):
     qlens = np.diff(qstart.numpy())
     out = oracle.ref_prefill(q.float().numpy(), k.float().numpy(), v.float().numpy(),
@@ -78,6 +88,7 @@ def host_engine(monkeypatch):
     for name, fn in (("pa_write_kv", _write_kv), ("pa_copy_blocks", _copy_blocks),
                      ("pa_swap_out", _swap_out), ("pa_swap_in", _swap_in),
                      ("pa_decode", _decode), ("pa_decode_shared", _decode),
+                     ("pa_write_decode", _write_decode),
                      ("pa_prefill", _prefill)):
         monkeypatch.setattr(engine_mod, name, fn)
     monkeypatch.setattr(engine_mod, "pa_decode_workspace_bytes", lambda *a: 0)
@@ -188,4 +199,8 @@ def test_engine_device_order_on_cpu(host_engine, host, shared):
     assert seen["preempted"] > 0 and seen["appended_victim"] > 0 and seen["prompts"] > 0
     if host:
         assert seen["decode_only"] > 0
+    # steps without a preemption or a shared-prefix plan write the batch's
+    # rows inside the decode (at position len - 1 through the table: the
+    # append's own slot); the others write them first
+    assert 0 < eng.folded_steps < step
     assert eng.bm.num_free_blocks == nb
