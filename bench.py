@@ -64,8 +64,9 @@ def parse_args():
     p.add_argument("--read-gib", type=int, default=8,
                    help="size of the streaming-read ceiling measurement (0 = skip)")
     p.add_argument("--separate-write", action="store_true",
-                   help="decode lines: pa_write_kv then pa_decode per layer instead of "
-                        "pa_write_decode")
+                   help="decode, fork and beam lines: pa_write_kv then pa_decode (or "
+                        "pa_decode_shared) instead of pa_write_decode "
+                        "(pa_write_decode_shared)")
     return p.parse_args()
 
 
@@ -440,9 +441,11 @@ def run_fork_cow(args, torch, pkv, workloads):
     round after the fork copies 7 shared, partly filled blocks per prompt
     (448 pa_copy_blocks pairs); rounds 2..255 are run untimed; the timed
     steps are then rounds of append + write + decode over 512 sequences of
-    2305+ tokens.  Decode is pa_decode_shared with a plan from
-    pa_shared_plan made on the host every step (the 128 prompt blocks of a
-    family are read once per family); plain pa_decode on the final batch is
+    2305+ tokens.  Decode is pa_write_decode_shared (the appended tokens'
+    K/V written in the same call; --separate-write: pa_write_kv, then
+    pa_decode_shared) with a plan from pa_shared_plan made on the host every
+    step (the 128 prompt blocks of a family are read once per family);
+    plain pa_decode on the final batch is
     timed after the steps for comparison.  Reported: logical KV GB/s (every
     sequence's tokens) and GB/s over the unique blocks read, plus the COW
     round's copy kernel."""
@@ -495,10 +498,18 @@ def run_fork_cow(args, torch, pkv, workloads):
         return (torch.from_numpy(sg).to(dev), torch.from_numpy(groups).to(dev), mx, mp,
                 splan.max_private_blocks)
 
-    def decode(max_len, plan, ev=None):
+    fold = not args.separate_write
+
+    def decode(max_len, plan, ev=None, write=False):
+        """The decode; with ``write``, the appended tokens' K/V written in
+        the same call (their slots are the sequences' positions len - 1)."""
         if ev is not None:
             ev[0].record()
-        if plan is not None:
+        if plan is not None and write:
+            pkv.pa_write_decode_shared(q, k, v, kn, vn, d_tab, d_len, max_len, *plan[:4],
+                                       max_private_blocks=plan[4], partition_tokens=512,
+                                       out=out, workspace=ws)
+        elif plan is not None:
             pkv.pa_decode_shared(q, k, v, d_tab, d_len, max_len, *plan[:4],
                                  max_private_blocks=plan[4], partition_tokens=512, out=out,
                                  workspace=ws)
@@ -534,8 +545,9 @@ def run_fork_cow(args, torch, pkv, workloads):
     cow_ev[0].record()
     pkv.pa_copy_blocks([k], [v], d_pairs)
     cow_ev[1].record()
-    pkv.pa_write_kv(k, v, kn, vn, d_slot)
-    decode(L0 + 2, plan)
+    if not fold:
+        pkv.pa_write_kv(k, v, kn, vn, d_slot)
+    decode(L0 + 2, plan, write=fold)
     round_ev[1].record()
     torch.cuda.synchronize()
     cow_ms, round_ms = cow_ev[0].elapsed_time(cow_ev[1]), round_ev[0].elapsed_time(round_ev[1])
@@ -560,8 +572,9 @@ def run_fork_cow(args, torch, pkv, workloads):
     for w in range(args.warmup):
         d_slot, _, _ = append(seqs, toks)
         plan = prepare()
-        pkv.pa_write_kv(k, v, kn, vn, d_slot)
-        decode(L0 + 1 + X + w + 1, plan)
+        if not fold:
+            pkv.pa_write_kv(k, v, kn, vn, d_slot)
+        decode(L0 + 1 + X + w + 1, plan, write=fold)
     torch.cuda.synchronize()
     evs = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
     dec = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
@@ -573,8 +586,12 @@ def run_fork_cow(args, torch, pkv, workloads):
         d_slot, _, _ = append(seqs, toks)
         plan = prepare()
         evs[i][0].record()
-        pkv.pa_write_kv(k, v, kn, vn, d_slot)
-        n_groups = decode(n, plan, dec[i])
+        if fold:
+            # one call: the step is the decode launch (no events inside)
+            n_groups = decode(n, plan, write=True)
+        else:
+            pkv.pa_write_kv(k, v, kn, vn, d_slot)
+            n_groups = decode(n, plan, dec[i])
         evs[i][1].record()
         lens.append(n)
         # unique blocks read: the shared prefix once per prompt plus every
@@ -583,7 +600,7 @@ def run_fork_cow(args, torch, pkv, workloads):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    dec_ms = np.array([a.elapsed_time(b) for a, b in dec])
+    dec_ms = step_ms if fold else np.array([a.elapsed_time(b) for a, b in dec])
     # plain pa_decode over the final batch, same tables, for comparison
     n_last = lens[-1]
     plain = [(T(enable_timing=True), T(enable_timing=True)) for _ in range(args.steps)]
@@ -615,7 +632,9 @@ def run_fork_cow(args, torch, pkv, workloads):
                    "block_size": bs, "num_blocks": NB, "partition_tokens": 512,
                    "timing": "GPU events per step (write + decode); value counts logical "
                              "KV bytes (shared prefix blocks once per sequence)",
-                   "decode": "pa_decode_shared with a per-step host plan"},
+                   "decode": "pa_decode_shared with a per-step host plan",
+                   "kv_write": "pa_write_kv, then pa_decode_shared" if not fold
+                   else "in the decode call (pa_write_decode_shared)"},
         "seqs_per_s": round(B * args.steps / (step_ms.sum() * 1e-3), 1),
         "gpu_step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(step_ms, [10, 50, 90])],
         "unique_kv_gbs": round(float(unique.sum() / (step_ms.sum() * 1e-3) / 1e9), 2),
@@ -637,10 +656,13 @@ def run_fork_cow(args, torch, pkv, workloads):
                           "plain_pa_decode_ms": round(float(plain_ms.mean()), 5),
                           "plain_unique_gbs": round(float(unique[-1] / (plain_ms.mean() * 1e-3) / 1e9), 2)},
         "roofline": with_ceiling(
-            {"kernel": "pa_decode_shared (shared pass + private pass, which finishes each sequence), unique bytes",
+            {"kernel": ("pa_write_decode_shared (the new tokens' write, shared pass + private pass, "
+                        "which finishes each sequence), unique bytes" if fold else
+                        "pa_decode_shared (shared pass + private pass, which finishes each "
+                        "sequence), unique bytes"),
              "bound": "hbm", "achieved": round(achieved_u, 2), "peak": PEAK_HBM_GBS,
              "unit": "GB/s", "frac": round(achieved_u / PEAK_HBM_GBS, 4),
-             "traffic": load_traffic("pa_decode_shared_fork_cow"),
+             "traffic": load_traffic("pa_decode_shared_fork_cow") if fold else None,
              "avg_launch_ms": round(float(dec_ms.mean()), 5),
              "algorithmic_bytes_per_launch": int(unique.mean())}, ceiling),
         "cpu_baseline": cpu,
@@ -839,8 +861,10 @@ def run_beam(args, torch, pkv, workloads):
     step each group's 8 beams are re-forked from seeded parents at their
     current (arbitrary) positions, the old beams freed, and all 512 beams
     append a token: beams sharing a partly filled last block copy it
-    (pa_copy_blocks with many small pairs), then pa_write_kv and
-    pa_decode_shared (host plan every step) over the 512 beams.  Reported:
+    (pa_copy_blocks with many small pairs), then pa_write_decode_shared
+    (the new tokens' K/V written inside the decode; --separate-write:
+    pa_write_kv, then pa_decode_shared; host plan every step) over the 512
+    beams.  Reported:
     step rate, copy pairs per step and the copy kernel's rate, decode KV
     GB/s (logical and over unique blocks), and plain pa_decode against
     pa_decode_shared on the final batch."""
@@ -890,7 +914,7 @@ def run_beam(args, torch, pkv, workloads):
         splan = pkv.pa_shared_plan(tables, lens, bs, 512, cfg["hq"] // H)
         sg, groups, mx, mp = splan
         host = time.perf_counter() - h0
-        d_slot = torch.from_numpy(slots).to(dev)
+        d_slot = torch.from_numpy(slots).to(dev) if not fold else None
         d_pairs = torch.from_numpy(pairs).to(dev) if len(pairs) else None
         d_tab = torch.from_numpy(tables).to(dev)
         d_len = torch.from_numpy(lens).to(dev)
@@ -901,18 +925,26 @@ def run_beam(args, torch, pkv, workloads):
         mark(0)
         if d_pairs is not None:
             pkv.pa_copy_blocks([k], [v], d_pairs)
-        mark(1)
-        pkv.pa_write_kv(k, v, kn, vn, d_slot)
-        mark(2)
-        pkv.pa_decode_shared(q, k, v, d_tab, d_len, int(lens.max()), d_sg, d_gr, mx, mp,
-                             max_private_blocks=splan.max_private_blocks, partition_tokens=512,
-                             out=out, workspace=ws)
+        if fold:
+            # the copies, then one call (the decode phase is that call)
+            mark(2)
+            pkv.pa_write_decode_shared(q, k, v, kn, vn, d_tab, d_len, int(lens.max()), d_sg,
+                                       d_gr, mx, mp, max_private_blocks=splan.max_private_blocks,
+                                       partition_tokens=512, out=out, workspace=ws)
+        else:
+            mark(1)
+            pkv.pa_write_kv(k, v, kn, vn, d_slot)
+            mark(2)
+            pkv.pa_decode_shared(q, k, v, d_tab, d_len, int(lens.max()), d_sg, d_gr, mx, mp,
+                                 max_private_blocks=splan.max_private_blocks,
+                                 partition_tokens=512, out=out, workspace=ws)
         mark(3)
         uniq = len(np.unique(np.concatenate([tables[i, :-(-int(n) // bs)] for i, n in enumerate(lens)])))
         last[:] = [d_tab, d_len, tables, lens]
         return len(pairs), int(lens.sum()), uniq, host
 
     last = [None] * 4
+    fold = not args.separate_write
 
     for _ in range(args.warmup):
         step()
@@ -921,7 +953,10 @@ def run_beam(args, torch, pkv, workloads):
     # odd steps only at their start and end, since every event record
     # leaves the GPU idle for a few microseconds: the step rate comes from
     # the odd steps (all steps if there is one), the phases from the even.
-    evs = [[T(enable_timing=True) if i % 2 == 0 or j in (0, 3) else None for j in range(4)]
+    # (With the write folded into the decode there is no event between
+    # write and decode: copy = events 0 -> 2, decode = 2 -> 3.)
+    evs = [[T(enable_timing=True) if (i % 2 == 0 and not (fold and j == 1)) or j in (0, 3)
+            else None for j in range(4)]
            for i in range(args.steps)]
     info = []
     t0 = time.perf_counter()
@@ -931,8 +966,9 @@ def run_beam(args, torch, pkv, workloads):
     wall = time.perf_counter() - t0
     phase = np.arange(args.steps) % 2 == 0
     whole = ~phase if args.steps > 1 else phase
-    copy_ms = np.array([e[0].elapsed_time(e[1]) for e in evs if e[1] is not None])
-    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs if e[1] is not None])
+    copy_end = 2 if fold else 1
+    copy_ms = np.array([e[0].elapsed_time(e[copy_end]) for e in evs if e[2] is not None])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs if e[2] is not None])
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     # The final batch again: plain pa_decode against pa_decode_shared with a
     # host plan (beams of a group share their prefix up to the last fork).
@@ -981,7 +1017,9 @@ def run_beam(args, torch, pkv, workloads):
                    "timing": "GPU events per step (COW copies + write + decode): odd steps at start and "
                              "end only (value, ms_per_step, beams/s), even steps around each phase (copy, "
                              "decode, roofline); value counts every beam's tokens (shared blocks once per beam)",
-                   "decode": "pa_decode_shared with a per-step host plan"},
+                   "decode": "pa_decode_shared with a per-step host plan",
+                   "kv_write": "pa_write_kv, then pa_decode_shared" if not fold
+                   else "in the decode call (pa_write_decode_shared)"},
         "beams_per_s": round(B * int(whole.sum()) / (step_ms[whole].sum() * 1e-3), 1),
         "unique_kv_gbs": round(float(uniq.sum() * bs * per_tok / (dec_ms.sum() * 1e-3) / 1e9), 2),
         "unique_kv_bytes_per_step": [int(u) * bs * per_tok for u in uniq_all],
@@ -993,13 +1031,17 @@ def run_beam(args, torch, pkv, workloads):
         "host_ms_per_step": round(float(np.mean([x[3] for x in info]) * 1e3), 4),
         "final_batch_decode": cmp,
         "roofline": with_ceiling(
-            {"kernel": "pa_decode_shared (shared pass + private pass, which finishes each sequence), unique bytes",
+            {"kernel": ("pa_write_decode_shared (the new tokens' write, shared pass + private pass, "
+                        "which finishes each sequence), unique bytes" if fold else
+                        "pa_decode_shared (shared pass + private pass, which finishes each "
+                        "sequence), unique bytes"),
              "bound": "hbm", "unit": "GB/s",
              "achieved": round(float(uniq.mean() * bs * per_tok / (dec_ms.mean() * 1e-3) / 1e9), 2),
              "peak": PEAK_HBM_GBS,
              "frac": round(float(uniq.mean() * bs * per_tok / (dec_ms.mean() * 1e-3) / 1e9)
                            / PEAK_HBM_GBS, 4),
-             "traffic": load_traffic("pa_decode_shared_beam"), "avg_launch_ms": round(float(dec_ms.mean()), 5),
+             "traffic": load_traffic("pa_decode_shared_beam") if fold else None,
+             "avg_launch_ms": round(float(dec_ms.mean()), 5),
              "algorithmic_bytes_per_launch": int(uniq.mean() * bs * per_tok)},
             stream_read_ceiling(torch, pkv, args.read_gib)),
         "cpu_baseline": None, "wall_s": round(wall, 3),

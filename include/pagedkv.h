@@ -602,6 +602,34 @@ int pa_decode_shared(float* out, const void* q, const void* k_cache, const void*
                      int32_t max_private_parts, int32_t max_private_blocks, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* pa_write_kv of each sequence's new token, then pa_decode_shared, in one
+ * call: pa_write_decode's write ("qaqbuyan.com article 130", no-cache
+ * decode loop: append the new K/V, then attend over every cached token)
+ * with a shared-prefix plan's decode ("day31", fork and copy-on-write:
+ * forked sequences share the parent's blocks).  Arguments as
+ * pa_decode_shared, plus k_new / v_new as in pa_write_decode.  A plan
+ * never shares a sequence's last block, so the private pass, which reads
+ * it, writes the row of position n - 1 there and reads the new row from
+ * k_new / v_new; the shared pass reads only blocks before it.  The result
+ * is that of pa_write_kv followed by pa_decode_shared: the same cache
+ * bytes, and the same output up to rounding in the last bit (the fused
+ * kernels are compiled apart from the others, and the compiler may fuse a
+ * multiply and an add differently in each).  One exception: a sequence
+ * that gets NaN rows because the private grid does not reach its last
+ * block (more private partitions than max_private_parts, as for a plan
+ * that does not match the tables) is not written.  Otherwise a sequence is
+ * written as pa_write_decode writes it. */
+int pa_write_decode_shared(float* out, const void* q, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, int32_t B, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, float scale, int32_t partition_tokens,
+                           int32_t dtype, const int32_t* seq_group, const int32_t* groups,
+                           int32_t n_groups, int32_t max_shared_parts, int32_t max_private_parts,
+                           int32_t max_private_blocks, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* ==== measurement helper (gfx950) ========================================
  * Streaming read of `bytes` bytes of device memory at `buf` (both multiples
  * of 16): `workgroups` workgroups each read one contiguous chunk once, with

@@ -5,8 +5,8 @@
 * :func:`pa_write_kv`, :func:`pa_copy_blocks`, :func:`pa_swap_out`,
   :func:`pa_swap_in`, :func:`pa_decode`, :func:`pa_write_decode`,
   :func:`pa_decode_workspace_bytes`,
-  :func:`pa_decode_shared`, :func:`pa_decode_shared_workspace_bytes`,
-  :func:`pa_prefill`, :func:`pa_decode_noalloc`
+  :func:`pa_decode_shared`, :func:`pa_write_decode_shared`,
+  :func:`pa_decode_shared_workspace_bytes`, :func:`pa_prefill`, :func:`pa_decode_noalloc`
   -- the device calls, on torch tensors;
 * :func:`pa_shared_plan` -- host planner of shared-prefix groups for
   :func:`pa_decode_shared`;
@@ -24,13 +24,13 @@ from .scheduler import Scheduler
 from .ops import (pa_copy_blocks, pa_decode, pa_decode_noalloc, pa_decode_noalloc_max_bytes,
                   pa_decode_shared, pa_decode_shared_workspace_bytes,
                   pa_decode_workspace_bytes, pa_prefill, pa_shared_plan,
-                  pa_stream_read, pa_swap_in, pa_swap_out, pa_write_decode, pa_write_kv,
-                  swap_record_bytes)
+                  pa_stream_read, pa_swap_in, pa_swap_out, pa_write_decode,
+                  pa_write_decode_shared, pa_write_kv, swap_record_bytes)
 
 lib()  # load now: a missing library is an import error, never a fallback
 
 __all__ = ["BlockManager", "Scheduler", "OutOfBlocks", "PagedKVError", "pa_write_kv", "pa_copy_blocks",
            "pa_swap_out", "pa_swap_in", "swap_record_bytes", "pa_decode", "pa_write_decode", "pa_prefill",
            "pa_decode_workspace_bytes", "pa_decode_shared", "pa_decode_shared_workspace_bytes",
-           "pa_shared_plan",
+           "pa_shared_plan", "pa_write_decode_shared",
            "pa_decode_noalloc", "pa_decode_noalloc_max_bytes", "pa_stream_read", "LIB_PATH"]

@@ -82,6 +82,10 @@ SIGNATURES = {
     "pa_write_decode": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32,
                                        c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32,
                                        c_i32, c_vp, c_sz, c_vp]),
+    "pa_write_decode_shared": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
+                                              c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                              c_f32, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                              c_i32, c_vp, c_sz, c_vp]),
     "pa_stream_read": (ctypes.c_int, [c_vp, ctypes.c_uint64, c_i32, c_vp, c_vp]),
     "pa_decode_noalloc_max_bytes": (c_sz, []),
     "pa_decode_noalloc": (ctypes.c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,

@@ -393,12 +393,13 @@ __device__ __forceinline__ void consume_block(RowState<DT, D, G>& st, const uint
 // writes its own result (no merge through LDS).  Used for the private pass
 // of a shared-prefix plan, whose partitions are often a block or two long:
 // one head per workgroup would leave three of its four waves idle there.
-// APPEND (pa_write_decode, no plan): the wave that reads a sequence's last
-// block takes the new token's row from k_new / v_new instead of the cache
-// and stores it there, once per (sequence, KV head).
+// APPEND (pa_write_decode, pa_write_decode_shared): the wave that reads a
+// sequence's last block takes the new token's row from k_new / v_new
+// instead of the cache and stores it there, once per (sequence, KV head).
+// With a plan the last block is always private (never in a shared pass),
+// so the private pass is the one that reads it.
 template <int DT, int D, int G, int NBUF, bool HEADS = false, bool APPEND = false>
 __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
-  static_assert(!(HEADS && APPEND), "the four-heads mapping serves plans only");
   constexpr int ELEM = ElemTraits<DT>::bytes;
   constexpr int EPL = 16 / ELEM;          // elements per lane per load
   constexpr int LPR = D * ELEM / 16;      // lanes per token row
@@ -502,13 +503,22 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
       vw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             vd, lane_off, i * RPI * row_bytes, kLoadAux));
   };
-  // APPEND: the wave that reads the sequence's last block takes the new
-  // token's row (len - 1) of head g from k_new / v_new in place of the
-  // loaded one, and stores it to the cache when the block id is valid (an
-  // invalid one flags the sequence and writes nothing).  Nothing reads that
-  // row back in this launch.
+  // APPEND: the wave that reads the sequence's last block (lb) loads the new
+  // token's row (len - 1) of head g from k_new / v_new before its first
+  // K/V loads, stores it to the cache right after issuing them (when the
+  // block id is valid: an invalid one flags the sequence and writes
+  // nothing), and takes it into the loaded registers in place of whatever
+  // its own load of that block returns.  Nothing else reads that row in
+  // this launch.  Storing early keeps the store's completion off the wave's
+  // critical path (the merge barrier waits for outstanding stores).
+  // HEADS keeps the row in LDS rather than in registers through the ring,
+  // which holds it to five waves per SIMD.
+  const int lb = nblk - 1;
+  const bool has_last = APPEND && lb >= first + w0 && lb < last && (lb - first - w0) % kStep == 0;
+  const int nr = n - 1 - lb * kBlock;      // the new row within block lb
+  __shared__ uint4 s_new[APPEND && HEADS ? kWaves : 1][2][64];
   uint4 knew{}, vnew{};
-  if constexpr (APPEND) {
+  if (has_last) {
     const size_t src = ((static_cast<size_t>(b) * a.hkv + g) * D + c * EPL) * ELEM;
     knew = *reinterpret_cast<const uint4*>(a.k_new + src);
     vnew = *reinterpret_cast<const uint4*>(a.v_new + src);
@@ -538,28 +548,33 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
     const int jj = first + w0 + sl * kStep;
     if (jj < last) load_block(check_id(a.seq_group == nullptr ? pro.spec[sl] : trow[jj]), kr[sl], vr[sl]);
   }
+  if (has_last) {
+    const int32_t id = trow[lb];
+    if (r == nr % RPI && id >= 0 && id < a.num_blocks) {
+      const size_t off = static_cast<size_t>(id) * block_bytes + static_cast<size_t>(nr) * row_bytes +
+                         static_cast<size_t>(g * D + c * EPL) * ELEM;
+      *reinterpret_cast<uint4*>(a.k_w + off) = knew;
+      *reinterpret_cast<uint4*>(a.v_w + off) = vnew;
+    }
+    if constexpr (HEADS) {
+      s_new[wv][0][lane] = knew;
+      s_new[wv][1][lane] = vnew;
+    }
+  }
   for (int j = first + w0; j < last; j += NBUF * kStep) {
 #pragma unroll
     for (int sl = 0; sl < NBUF; ++sl) {
       const int jj = j + sl * kStep;
       if (jj < last) {
         if constexpr (APPEND) {
-          if (jj == nblk - 1) {
-            const int nr = n - 1 - jj * kBlock;
+          if (jj == lb) {
+            // (HEADS: K, then V, back from LDS, one at a time)
+            const uint4 kn = HEADS ? s_new[wv][0][lane] : knew;
 #pragma unroll
-            for (int i = 0; i < LPB; ++i) {
-              const bool mine = i * RPI + r == nr;
-              kr[sl][i] = select4(mine, knew, kr[sl][i]);
-              vr[sl][i] = select4(mine, vnew, vr[sl][i]);
-            }
-            const int32_t id = trow[jj];
-            if (r == nr % RPI && id >= 0 && id < a.num_blocks) {
-              const size_t off = static_cast<size_t>(id) * block_bytes +
-                                 static_cast<size_t>(nr) * row_bytes +
-                                 static_cast<size_t>(g * D + c * EPL) * ELEM;
-              *reinterpret_cast<uint4*>(a.k_w + off) = knew;
-              *reinterpret_cast<uint4*>(a.v_w + off) = vnew;
-            }
+            for (int i = 0; i < LPB; ++i) kr[sl][i] = select4(i * RPI + r == nr, kn, kr[sl][i]);
+            const uint4 vn = HEADS ? s_new[wv][1][lane] : vnew;
+#pragma unroll
+            for (int i = 0; i < LPB; ++i) vr[sl][i] = select4(i * RPI + r == nr, vn, vr[sl][i]);
           }
         }
         consume(kr[sl], vr[sl], jj);
@@ -704,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void decode_phase1(DecodeArgs a) {
 //       holds the same ids over the partition (NaN output otherwise).
 template <int DT, int D, int G, int NBUF, bool SHARED, bool APPEND = false>
 __global__ __launch_bounds__(kThreads) void decode_phase1_mfma(DecodeArgs a) {
-  static_assert(!(SHARED && APPEND), "pa_write_decode takes no plan");
+  static_assert(!(SHARED && APPEND), "the shared pass never reads a last block");
   static_assert(DT != PA_DTYPE_F32 && (D == 64 || D == 128), "shape");
   static_assert(SHARED ? G == 16 : (G == 4 || G == 8), "query columns");
   using M = MfmaOps<DT>;
@@ -1247,12 +1262,14 @@ hipError_t launch_dt_d(const DecodeArgs& args, int B, int group, hipStream_t st)
   const bool append = a.k_new != nullptr;
   switch (group) {
     case 1:
-      if (heads) decode_phase1<DT, D, 1, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      if (heads && append) decode_phase1<DT, D, 1, kNbufHeads, kHeadsOk, true><<<grid_h, kThreads, 0, st>>>(a);
+      else if (heads) decode_phase1<DT, D, 1, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
       else if (append) decode_phase1<DT, D, 1, kNbuf, false, true><<<grid, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 1, kNbuf><<<grid, kThreads, 0, st>>>(a);
       break;
     case 2:
-      if (heads) decode_phase1<DT, D, 2, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
+      if (heads && append) decode_phase1<DT, D, 2, kNbufHeads, kHeadsOk, true><<<grid_h, kThreads, 0, st>>>(a);
+      else if (heads) decode_phase1<DT, D, 2, kNbufHeads, kHeadsOk><<<grid_h, kThreads, 0, st>>>(a);
       else if (append) decode_phase1<DT, D, 2, kNbuf, false, true><<<grid, kThreads, 0, st>>>(a);
       else decode_phase1<DT, D, 2, kNbuf><<<grid, kThreads, 0, st>>>(a);
       break;
@@ -1560,6 +1577,26 @@ extern "C" int pa_write_decode(float* out, const void* q, void* k_cache, void* v
                      num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
                      dtype, nullptr, nullptr, 0, 0, 0, 0, workspace, workspace_bytes, stream, false,
                      k_new, v_new);
+}
+
+extern "C" int pa_write_decode_shared(float* out, const void* q, void* k_cache, void* v_cache,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, int32_t max_context_len,
+                                      int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      float scale, int32_t partition_tokens, int32_t dtype,
+                                      const int32_t* seq_group, const int32_t* groups,
+                                      int32_t n_groups, int32_t max_shared_parts,
+                                      int32_t max_private_parts, int32_t max_private_blocks,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new))
+    return fail(PA_ERR_INVALID, "pa_write_decode_shared: null pointer");
+  return decode_impl("pa_write_decode_shared", out, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, B, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, partition_tokens,
+                     dtype, seq_group, groups, n_groups, max_shared_parts, max_private_parts,
+                     max_private_blocks, workspace, workspace_bytes, stream, false, k_new, v_new);
 }
 
 extern "C" size_t pa_decode_noalloc_max_bytes(void) { return kScratchBytes; }

@@ -18,10 +18,10 @@ require:
   4. decode (pa_decode) of the batch, every layer.  When no preemption
      split the step's writes and the batch is exactly the requests that
      appended, in the same order (the usual step), each layer's writes of
-     the batch's new tokens happen inside its decode instead (pa_write_decode:
-     the token at position len - 1 is the one each of them appended), and
-     step 3 is only the copies; a step decoded through a shared-prefix plan
-     keeps its writes in step 3.  With ``shared_prefix``
+     the batch's new tokens happen inside its decode instead
+     (pa_write_decode, or pa_write_decode_shared with a plan: the token at
+     position len - 1 is the one each of them appended), and step 3 is only
+     the copies.  With ``shared_prefix``
      the host plans shared-prefix groups once per step (pa_shared_plan) and
      every layer decodes with pa_decode_shared, reading blocks that several
      sequences share (a common system prompt, forks) once per group -- when
@@ -44,7 +44,7 @@ import torch
 from .block_manager import BlockManager
 from .ops import (pa_copy_blocks, pa_decode, pa_decode_shared, pa_decode_shared_workspace_bytes,
                   pa_decode_workspace_bytes, pa_prefill, pa_shared_plan, pa_swap_in, pa_swap_out,
-                  pa_write_decode, pa_write_kv, swap_record_bytes)
+                  pa_write_decode, pa_write_decode_shared, pa_write_kv, swap_record_bytes)
 from .scheduler import Scheduler
 
 
@@ -198,7 +198,7 @@ class DecodeEngine:
         rows = [kv_rows(layer, "append", plan) for layer in range(self.L)] if len(writes) else None
         # The batch's writes fold into its decode when nothing orders them
         # against a swap-out and every decoded request appended exactly once.
-        fold = (dec is not None and dec[4] is None and len(writes) > 0 and not len(plan["cuts"])
+        fold = (dec is not None and len(writes) > 0 and not len(plan["cuts"])
                 and np.array_equal(writes, plan["batch"]))
         slots = self.up(plan["slots"], np.int64) if len(writes) and not fold else None
         w = c = so = 0
@@ -305,11 +305,17 @@ class DecodeEngine:
         B, d_tab, d_len, max_len, splan = dec
         for layer in range(self.L):
             q = q_rows(layer, "decode", B)
-            if rows is not None:
+            if rows is not None and splan is None:
                 k, v = rows[layer]
                 outs.append(pa_write_decode(q, self.k[layer], self.v[layer], k, v, d_tab, d_len,
                                             max_len, partition_tokens=self.partition_tokens,
                                             workspace=self.ws))
+            elif rows is not None:
+                k, v = rows[layer]
+                outs.append(pa_write_decode_shared(
+                    q, self.k[layer], self.v[layer], k, v, d_tab, d_len, max_len, *splan[:4],
+                    max_private_blocks=splan[4], partition_tokens=self.partition_tokens,
+                    workspace=self.ws))
             elif splan is None:
                 outs.append(pa_decode(q, self.k[layer], self.v[layer], d_tab, d_len, max_len,
                                       partition_tokens=self.partition_tokens, workspace=self.ws))

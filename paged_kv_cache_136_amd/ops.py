@@ -231,16 +231,22 @@ def pa_write_decode(q, k_cache, v_cache, k_new, v_new, block_tables, context_len
     out [B, Hq, D]."""
     out, head, ws = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                  max_context_len, scale, partition_tokens, out, workspace, stream)
+    _check_new_rows(q, k_cache, k_new, v_new)
+    # head = (out, q, k, v, tables, max_blocks, lens, max_len, B, hq, hkv, d, bs, nb, scale, pt, dtype)
+    check(lib().pa_write_decode(*head[:4], k_new.data_ptr(), v_new.data_ptr(), *head[4:], *ws,
+                                _stream(stream)))
+    return out
+
+
+def _check_new_rows(q, k_cache, k_new, v_new):
     _dev(k_new, v_new)
     B, hkv, d = q.shape[0], k_cache.shape[2], k_cache.shape[3]
     if k_new.shape != (B, hkv, d) or v_new.shape != (B, hkv, d):
         raise ValueError("k_new and v_new must be [B, Hkv, D]")
     if not (k_new.dtype == v_new.dtype == k_cache.dtype):
         raise ValueError("k_new and v_new must share the caches' dtype")
-    # head = (out, q, k, v, tables, max_blocks, lens, max_len, B, hq, hkv, d, bs, nb, scale, pt, dtype)
-    check(lib().pa_write_decode(*head[:4], k_new.data_ptr(), v_new.data_ptr(), *head[4:], *ws,
-                                _stream(stream)))
-    return out
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous")
 
 
 def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
@@ -301,6 +307,34 @@ def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, max_contex
     host-side grid bounds (0 for the latter: no bound), max_private_blocks
     its private-pass hint (0: unknown).  A given workspace must hold
     pa_decode_shared_workspace_bytes(...) bytes when the plan has groups."""
+    out, head, plan, ws = _shared_args(q, k_cache, v_cache, block_tables, context_lens,
+                                       max_context_len, seq_group, groups, max_shared_parts,
+                                       max_private_parts, max_private_blocks, scale,
+                                       partition_tokens, out, workspace, stream)
+    check(lib().pa_decode_shared(*head, *plan, *ws, _stream(stream)))
+    return out
+
+
+def pa_write_decode_shared(q, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+                           max_context_len, seq_group, groups, max_shared_parts,
+                           max_private_parts=0, scale=None, partition_tokens=512, out=None,
+                           workspace=None, stream=None, max_private_blocks=0):
+    """pa_write_decode's write of each sequence's new token (k_new / v_new
+    [B, Hkv, D], at position context_lens[b] - 1) with pa_decode_shared's
+    decode, in one call; the plan arguments as pa_decode_shared's."""
+    out, head, plan, ws = _shared_args(q, k_cache, v_cache, block_tables, context_lens,
+                                       max_context_len, seq_group, groups, max_shared_parts,
+                                       max_private_parts, max_private_blocks, scale,
+                                       partition_tokens, out, workspace, stream)
+    _check_new_rows(q, k_cache, k_new, v_new)
+    check(lib().pa_write_decode_shared(*head[:4], k_new.data_ptr(), v_new.data_ptr(), *head[4:],
+                                       *plan, *ws, _stream(stream)))
+    return out
+
+
+def _shared_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, seq_group,
+                 groups, max_shared_parts, max_private_parts, max_private_blocks, scale,
+                 partition_tokens, out, workspace, stream):
     n = 0 if groups is None else groups.shape[0]
     need_fn = (pa_decode_shared_workspace_bytes if n and int(max_shared_parts) > 0
                else pa_decode_workspace_bytes)
@@ -313,11 +347,9 @@ def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, max_contex
                 or groups.dtype != torch.int32 or groups.shape != (n, SHARED_ROW)
                 or not groups.is_contiguous()):
             raise ValueError("seq_group must be int32 [B] and groups int32 [n, 17]")
-    check(lib().pa_decode_shared(*head, seq_group.data_ptr() if n else None,
-                                 groups.data_ptr() if n else None, n, int(max_shared_parts),
-                                 int(max_private_parts), int(max_private_blocks), *ws,
-                                 _stream(stream)))
-    return out
+    plan = (seq_group.data_ptr() if n else None, groups.data_ptr() if n else None, n,
+            int(max_shared_parts), int(max_private_parts), int(max_private_blocks))
+    return out, head, plan, ws
 
 
 def pa_prefill(q, k_cache, v_cache, block_tables, query_start, context_lens, max_query_len,

@@ -261,3 +261,27 @@ def test_write_decode_validates_before_touching_the_gpu():
     assert call(v_new=p + 4) == 2 and b"16-byte aligned" in L.pa_last_error()
     assert call(head_dim=96) == 3 and b"head_dim" in L.pa_last_error()
     assert call(k_new=None, v_new=None, B=0) == 0          # B == 0 launches nothing
+
+
+def test_write_decode_shared_validates_before_touching_the_gpu():
+    """pa_write_decode_shared rejects missing or misaligned new rows and
+    every plan argument pa_decode_shared rejects, before its first HIP
+    call."""
+    from paged_kv_cache_136_amd import lib
+    L = lib()
+    keep = []
+    p = _aligned_host_ptr(keep)
+
+    def call(k_new=p, v_new=p, n_groups=1, seq_group=p, dtype=1, B=2):
+        # pa_write_decode's arguments up to dtype, then (seq_group, groups,
+        # n_groups, max_shared_parts, max_private_parts, max_private_blocks,
+        # workspace, bytes, stream)
+        return L.pa_write_decode_shared(p, p, p, p, k_new, v_new, p, 8, p, 64, B, 8, 2, 128, 16,
+                                        64, 0.088, 512, dtype, seq_group, p, n_groups, 1, 1, 0,
+                                        p, 1 << 20, None)
+    assert call(k_new=None) == 2 and b"null" in L.pa_last_error()
+    assert call(v_new=p + 4) == 2 and b"16-byte aligned" in L.pa_last_error()
+    assert call(seq_group=None) == 2 and b"null plan pointer" in L.pa_last_error()
+    assert call(dtype=0) == 3 and b"F16 or BF16" in L.pa_last_error()
+    assert call(n_groups=-1) == 2 and b"negative n_groups" in L.pa_last_error()
+    assert call(k_new=None, v_new=None, B=0) == 0          # B == 0 launches nothing

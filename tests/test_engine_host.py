@@ -5,7 +5,9 @@ with the preemption and device-order readings of the scheduler).
 The library's scheduler and block manager run for real; the device calls
 the engine makes are replaced by plain torch stand-ins on CPU tensors (the
 oracle's attention for decode and prefill, element copies for writes,
-copy-on-write and swaps).  The oracle scheduler and copies run beside it in
+copy-on-write and swaps; for a decode that writes its batch's new tokens,
+with or without a shared-prefix plan, the copy to the slot of position
+len - 1 through the table, then the oracle's attention).  The oracle scheduler and copies run beside it in
 the plan's decision order, and after every step the plans, the caches (bit
 for bit), the decode outputs and the prompt-attention outputs must agree.
 A stand-in that ran the prompt attention after the step's later writes, or
@@ -66,7 +68,7 @@ def _decode(q, k, v, tables, lens, max_len, *plan, partition_tokens=512, workspa
     return torch.from_numpy(out).float()
 
 
-def _write_decode(q, k, v, kn, vn, tables, lens, max_len, **kw):
+def _write_decode(q, k, v, kn, vn, tables, lens, max_len, *plan, **kw):
     # each sequence's new rows at the slot of its position len - 1, then the
     # decode over the caches that now hold them
     bs = k.shape[1]
@@ -89,6 +91,7 @@ def host_engine(monkeypatch):
                      ("pa_swap_out", _swap_out), ("pa_swap_in", _swap_in),
                      ("pa_decode", _decode), ("pa_decode_shared", _decode),
                      ("pa_write_decode", _write_decode),
+                     ("pa_write_decode_shared", _write_decode),
                      ("pa_prefill", _prefill)):
         monkeypatch.setattr(engine_mod, name, fn)
     monkeypatch.setattr(engine_mod, "pa_decode_workspace_bytes", lambda *a: 0)
@@ -199,8 +202,8 @@ def test_engine_device_order_on_cpu(host_engine, host, shared):
     assert seen["preempted"] > 0 and seen["appended_victim"] > 0 and seen["prompts"] > 0
     if host:
         assert seen["decode_only"] > 0
-    # steps without a preemption or a shared-prefix plan write the batch's
-    # rows inside the decode (at position len - 1 through the table: the
-    # append's own slot); the others write them first
+    # steps without a preemption write the batch's rows inside the decode
+    # (at position len - 1 through the table: the append's own slot); the
+    # others write them first
     assert 0 < eng.folded_steps < step
     assert eng.bm.num_free_blocks == nb

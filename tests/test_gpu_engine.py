@@ -11,10 +11,10 @@ step's device work in the plan's decision order (epochs split at each
 preemption).  Requests share prompt prefixes (prefix hits), the pool is
 small enough to force preemption -- including victims that already
 appended in their step -- and the host swap pool is either roomy
-(swap-out/in) or absent (recompute).  On steps without a preemption or a
-shared-prefix plan the batch's own K/V writes run inside its decode
-(pa_write_decode), on the others through pa_write_kv; the byte and output
-checks cover both.
+(swap-out/in) or absent (recompute).  On steps without a preemption the
+batch's own K/V writes run inside its decode (pa_write_decode, or
+pa_write_decode_shared with a plan), on the others through pa_write_kv;
+the byte and output checks cover both.
 """
 
 import numpy as np
@@ -161,9 +161,8 @@ def test_serve_loop_matches_oracle(host, shared):
     assert seen["preempted"] > 0 and seen["hits"] > 0 and seen["appended_victim"] > 0
     assert seen["prompt_rows"] > 0
     assert (eng.shared_groups > 0) == shared
-    # the batch's writes ran inside pa_write_decode on the steps that allow
-    # it, through pa_write_kv on the others (a preemption, or a step decoded
-    # with a shared-prefix plan)
+    # the batch's writes ran inside the decode on the steps that allow it,
+    # through pa_write_kv on the others (a preemption)
     say("serve loop steps with folded writes", eng.folded_steps, "of", step)
     assert 0 < eng.folded_steps < step
     if host:
