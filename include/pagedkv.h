@@ -13,7 +13,11 @@
  *   - pa_decode: attention of one query token per sequence over K/V that
  *     live in fixed-size blocks scattered through HBM, found through the
  *     sequence's block table, with split-KV partitions and a final reduce;
- *     pa_decode_shared reads blocks shared by several sequences once.
+ *     pa_decode_shared reads blocks shared by several sequences once;
+ *   - pa_write_decode / pa_write_decode_shared: each sequence's new token
+ *     written and the decode over it, in one call;
+ *   - pa_prefill: causal attention of prompts' uncached suffixes;
+ *   - pa_sched_*: a continuous-batching scheduler over the block manager.
  *
  * Pages cited:
  *   [A130]  "qaqbuyan.com article 130" (vLLM PagedAttention walk-through):
