@@ -72,7 +72,7 @@ constexpr int kLoadAux = 2;        // cache policy of K/V loads: nontemporal (re
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kNbuf = 3;           // K/V blocks in flight per wave, vector path (groups of 1, 2)
 constexpr int kNbufG4 = 1;         // same, fp32 query group of 4 (VGPR-limited)
-constexpr int kNbufMfma = 1;       // same, matrix-core path (groups of 4 and 8)
+constexpr int kNbufMfma = 2;       // same, matrix-core path (groups of 4 and 8)
 constexpr int kNbufShared = 2;     // same, shared-prefix pass (a few long streams per group)
 constexpr int kNbufHeads = 1;      // same, four-heads private pass (runs of at most 8 blocks):
                                    // 88 VGPRs, so five waves per SIMD hide its round trips
