@@ -28,10 +28,15 @@
 //     partition writes out[] directly, otherwise (m, l, o/l) go to the
 //     workspace.
 // Phase 1, matrix cores (query groups of 4 and 8, 16-bit K/V): QK^T and PV
-//   as MFMAs; each wave streams a whole partition and a workgroup merges
-//   its four partitions before writing (decode_phase1_mfma).
+//   as MFMAs; a workgroup takes four consecutive partitions of one (KV
+//   head, sequence), its waves take their blocks in turn, two in flight
+//   each, and the four waves' results are merged before one partial row is
+//   written (decode_phase1_mfma).
 // Shared-prefix plans add a matrix-core pass over each group's shared
 //   partitions, read once for all members, before the private pass.
+// pa_write_decode and pa_write_decode_shared (APPEND): the phase-1 wave
+//   that reads a sequence's last block also writes the new token's K/V row
+//   there, and uses it in place of what it loaded.
 // Phase 2 merges the partitions: one workgroup of 4 waves per (query head,
 //   sequence), or, with at most 16 partitions and at least 1024 such pairs,
 //   one wave per pair and four pairs per workgroup (decode_reduce_wave).
