@@ -245,8 +245,6 @@ def _check_new_rows(q, k_cache, k_new, v_new):
         raise ValueError("k_new and v_new must be [B, Hkv, D]")
     if not (k_new.dtype == v_new.dtype == k_cache.dtype):
         raise ValueError("k_new and v_new must share the caches' dtype")
-    if not (k_new.is_contiguous() and v_new.is_contiguous()):
-        raise ValueError("k_new and v_new must be contiguous")
 
 
 def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
