@@ -475,8 +475,10 @@ int pa_decode(float* out, const void* q, const void* k_cache, const void* v_cach
  * k_new / v_new to that slot of k_cache / v_cache, and the attention is
  * computed as pa_decode computes it after that write: the same output, bit
  * for bit, and the same cache bytes as pa_write_kv followed by pa_decode.
- * The decode reads the new row from k_new / v_new rather than back from
- * memory.
+ * The wave that reads a sequence's last block writes the new row there:
+ * on the vector path it takes the row from k_new / v_new into its loaded
+ * registers; on the matrix-core path (query groups of 4 and 8, 16-bit K/V)
+ * it stores the row first, waits for the store, and reads it back.
  *   k_new, v_new: device [B][num_kv_heads][head_dim] in `dtype`, 16-byte
  *     aligned, read only.
  *   k_cache, v_cache: written at the new tokens' slots only.
