@@ -587,6 +587,51 @@ def test_fork_cow_shared_decode_all_forks(fork_flow):
     assert np.isfinite(got).all() and err <= TOL["f16"], err
 
 
+def test_fork_cow_write_decode_shared_next_round(fork_flow):
+    """The fork line's launch: one more append round for all 512 forks
+    (each takes a new private block: 2305 tokens fill 144 blocks), the new
+    tokens' K/V written inside pa_write_decode_shared while the prompt
+    blocks are read once per family.  The slots equal the oracle manager's,
+    the caches are bit-identical to the oracle's write at those slots, and
+    every row and head of all 512 forks is checked against the float64
+    oracle over the updated cache.  Runs after the other fork tests (it
+    moves the flow one round on)."""
+    f = fork_flow
+    cfg = f["cfg"]
+    H, d, bs, pt = cfg["hkv"], cfg["d"], 16, cfg["partition_tokens"]
+    seqs = f["seqs"]
+    toks = workloads.token_ids(len(seqs), seed=31337)
+    slots, pairs = f["bm"].append_slots(seqs, toks)
+    want = [f["rbm"].append_slot(s, t) for s, t in zip(seqs, toks)]
+    assert slots.tolist() == [w[0] for w in want] and len(pairs) == 0
+    assert all(w[1] is None for w in want)
+    n = cfg["prompt_len"] + 1 + cfg["extra"] + 1
+    tables, clens = f["bm"].export_batch(seqs, -(-n // bs), pad_block=0)
+    assert (clens == n).all()
+    splan = pkv.pa_shared_plan(tables, clens, bs, pt, 1)
+    sg, groups, mx, mp = splan
+    assert len(groups) == cfg["prompts"] and mp == 1
+    kn = workloads.normal_torch((len(seqs), H, d), 4242, torch.float16, "cuda")
+    vn = workloads.normal_torch((len(seqs), H, d), 4243, torch.float16, "cuda")
+    say("fork_cow: write + shared-prefix decode of 512 forks, one more round")
+    out = pkv.pa_write_decode_shared(f["q"], f["k"], f["v"], kn, vn, torch.from_numpy(tables).cuda(),
+                                     torch.from_numpy(clens).cuda(), n, torch.from_numpy(sg).cuda(),
+                                     torch.from_numpy(groups).cuda(), mx, mp, partition_tokens=pt,
+                                     max_private_blocks=splan.max_private_blocks)
+    torch.cuda.synchronize()
+    oracle.ref_write_kv(f["kh"], f["vh"], _bits(kn), _bits(vn), slots, inplace=True)
+    assert np.array_equal(_bits(f["k"]), f["kh"]) and np.array_equal(_bits(f["v"]), f["vh"])
+    ref_tables = np.array([f["rbm"].get_table(s) for s in seqs])
+    assert np.array_equal(tables, ref_tables)
+    say("fork_cow: oracle over all 512 forks after the round")
+    ref = _oracle_rows(host_f32(f["q"]), f["kh"].view(np.float16), f["vh"].view(np.float16),
+                       ref_tables, clens, np.arange(len(seqs)))
+    got = out.cpu().numpy()
+    err = float(np.abs(got - ref).max())
+    report("fork_cow pa_write_decode_shared, 512 x 32 rows, max abs err vs oracle", err)
+    assert np.isfinite(got).all() and err <= TOL["f16"], err
+
+
 def test_fork_cow_release():
     """Frees the fork workload's 5 GiB of caches for the tests after it."""
     _FORK.clear()
